@@ -1,0 +1,149 @@
+"""fp64 CPU oracle of the selective scan (S6) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``selective_state_space_22_amd``) and the library never imports it.
+
+Two independent implementations of the same definition live here:
+  * ``scan`` / ``step``: the C oracle ``s6_oracle.c`` (fp64, libm, OpenMP over
+    (batch, channel)), called through ctypes;
+  * ``scan_numpy``: a numpy fp64 twin vectorised over (batch, channel, state)
+    with a Python loop over tokens, used to cross-check the C code.
+Both follow "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
+section 2.1 eq. (2) (ZOH), eq. (3a)/(3b) (recurrence and readout),
+section 3.2 (selection: per-token dt through softplus, B/C shared by channels)
+and the Figure 3 caption (SiLU gate).  Readings where the page is silent:
+bias before softplus, skip term Dskip*x before the gate, gate z*sigmoid(z),
+zero initial state unless h0 is given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "s6_oracle.c")
+_LIB = os.path.join(_HERE, "libs6oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (fp64, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.s6_oracle_scan.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, ctypes.c_int]
+        lib.s6_oracle_scan.restype = ctypes.c_int
+        lib.s6_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_int]
+        lib.s6_oracle_step.restype = ctypes.c_int
+        lib.s6_oracle_max_threads.argtypes = []
+        lib.s6_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().s6_oracle_max_threads())
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=True, h0=None,
+         nthreads: int | None = None):
+    """fp64 forward scan.  Returns (out (batch,L,D), last_state (batch,D,N))."""
+    u, delta, A, B, C = (_f64(x) for x in (u, delta, A, B, C))
+    delta_bias, Dskip, z, h0 = (_f64(x) for x in (delta_bias, Dskip, z, h0))
+    batch, L, D = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (D, N)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert z is None or z.shape == u.shape
+    assert h0 is None or h0.shape == (batch, D, N)
+    out = np.empty((batch, L, D), dtype=np.float64)
+    last = np.empty((batch, D, N), dtype=np.float64)
+    nt = nthreads if nthreads else max_threads()
+    rc = _load().s6_oracle_scan(batch, L, D, N, _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                                _ptr(Dskip), _ptr(z), int(bool(softplus)), _ptr(h0), _ptr(out), _ptr(last), nt)
+    if rc != 0:
+        raise RuntimeError(f"s6_oracle_scan failed with {rc}")
+    return out, last
+
+
+def step(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=True, nthreads: int | None = None):
+    """One fp64 decode step.  state (batch,D,N) is copied, advanced and returned with out (batch,D)."""
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    u, delta, A, B, C = (_f64(x) for x in (u, delta, A, B, C))
+    delta_bias, Dskip, z = (_f64(x) for x in (delta_bias, Dskip, z))
+    batch, D = u.shape
+    N = A.shape[1]
+    assert st.shape == (batch, D, N) and B.shape == (batch, N) and C.shape == (batch, N)
+    out = np.empty((batch, D), dtype=np.float64)
+    nt = nthreads if nthreads else max_threads()
+    rc = _load().s6_oracle_step(batch, D, N, _ptr(st), _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B),
+                                _ptr(C), _ptr(Dskip), _ptr(z), int(bool(softplus)), _ptr(out), nt)
+    if rc != 0:
+        raise RuntimeError(f"s6_oracle_step failed with {rc}")
+    return out, st
+
+
+def scan_inputs(inp, h0=None, nthreads=None, softplus=None):
+    """Oracle scan of a ``workloads.ScanInputs`` (uses the exact values the GPU sees)."""
+    sp = inp.softplus if softplus is None else softplus
+    return scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.delta_bias, inp.Dskip, inp.z, sp, h0, nthreads)
+
+
+def scan_numpy(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=True, h0=None):
+    """Independent numpy fp64 twin of ``scan`` (vectorised over batch, channel, state)."""
+    u = np.asarray(u, np.float64)
+    dt = np.asarray(delta, np.float64)
+    A = np.asarray(A, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    batch, L, D = u.shape
+    N = A.shape[1]
+    if delta_bias is not None:
+        dt = dt + np.asarray(delta_bias, np.float64)[None, None, :]
+    if softplus:
+        dt = np.logaddexp(0.0, dt)  # log(e^0 + e^v)
+    h = np.zeros((batch, D, N)) if h0 is None else np.array(h0, np.float64, copy=True)
+    out = np.empty((batch, L, D))
+    for t in range(L):
+        x = dt[:, t, :, None] * A[None, :, :]                         # (batch, D, N)
+        abar = np.exp(x)
+        safe = np.where(x == 0.0, 1.0, x)
+        phi = np.where(x == 0.0, 1.0, np.expm1(x) / safe)
+        bbar = phi * dt[:, t, :, None] * B[:, t, None, :]
+        h = abar * h + bbar * u[:, t, :, None]
+        y = np.einsum("bdn,bn->bd", h, C[:, t, :])
+        if Dskip is not None:
+            y = y + np.asarray(Dskip, np.float64)[None, :] * u[:, t, :]
+        if z is not None:
+            zt = np.asarray(z, np.float64)[:, t, :]
+            y = y * (zt / (1.0 + np.exp(-zt)))
+        out[:, t, :] = y
+    return out, h

@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the selective scan (S6).
+
+This module only draws random numbers and packs them; it holds none of the
+scan's own arithmetic, so both the HIP path and the fp64 oracle can be fed
+from it.  Shapes and distributions follow the workloads the Mamba paper's
+models imply (Mamba-130M / Mamba-3B layer shapes, expand factor E = 2, state
+size N = 16) and the "S4D-real" initialisation A_n = -(n+1) from the paper's
+A-initialisation ablation (kb.agiseed.tech Mamba overview, section 6.5).
+
+Distributions (all drawn in float32 from numpy PCG64):
+  dt0    ~ exp(U(ln 1e-3, ln 1e-1))        per channel, delta_bias = softplus^-1(dt0)
+  Dskip  ~ N(0, 1)                          per channel
+  u, z   ~ N(0, 1)                          (batch, L, D)
+  delta  ~ U(-4, -2)                        (batch, L, D), raw (pre-softplus)
+  B, C   ~ N(0, 1)                          (batch, L, N)
+  reset  (million-token workload only): Bernoulli(0.01) per (batch row, token),
+         shared by all channels; at those tokens delta ~ U(30, 40).
+Draw order: dt0, Dskip, u, z, delta, B, C, [reset mask, reset deltas].
+bf16 workloads draw in float32 and round once to bf16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+SEED_BASE = 22_000
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    io: str  # "f32" or "bf16"
+    reset_frac: float = 0.0
+    decode_steps: int = 0  # >0: decode workload advanced one token at a time
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.dim * self.dstate
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny", 0, 1, 256, 64, 16, "f32"),
+        Workload("mamba130m_layer", 1, 8, 2048, 1536, 16, "bf16"),
+        Workload("mamba3b_layer", 2, 4, 4096, 5120, 16, "bf16"),
+        Workload("million_tokens", 3, 1, 1 << 20, 256, 16, "f32", reset_frac=0.01),
+        Workload("decode", 4, 256, 64, 5120, 16, "bf16", decode_steps=64),
+    )
+}
+
+
+def bf16_round(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Round float32 -> bf16 with round-to-nearest-even.
+
+    Returns (bits as uint16, the same values widened back to float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    nan = np.isnan(x)
+    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    r = ((u + bias) >> 16).astype(np.uint16)
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    widened = (r.astype(np.uint32) << 16).view(np.float32)
+    return r, widened
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def a_init(dim: int, dstate: int, kind: str = "s4d_real", rng: np.random.Generator | None = None) -> np.ndarray:
+    """Real diagonal A of shape (D, N), one of the paper's real initialisations."""
+    n = np.arange(dstate, dtype=np.float32)
+    if kind == "s4d_real":  # A_n = -(n+1)
+        row = -(n + 1.0)
+        return np.ascontiguousarray(np.broadcast_to(row, (dim, dstate)), dtype=np.float32)
+    if kind == "neg_half":  # A_n = -1/2
+        return np.full((dim, dstate), -0.5, dtype=np.float32)
+    if kind == "exp_normal":  # A_n = -exp(N(0,1)), independent per (d, n)
+        rng = rng or np.random.default_rng(SEED_BASE + 99)
+        return (-np.exp(rng.standard_normal((dim, dstate), dtype=np.float32))).astype(np.float32)
+    raise ValueError(kind)
+
+
+def softplus_inverse(y: np.ndarray) -> np.ndarray:
+    """x such that log(1 + e^x) = y (input recipe for delta_bias), in float64."""
+    y = np.asarray(y, dtype=np.float64)
+    return np.log(np.expm1(y))
+
+
+@dataclasses.dataclass
+class ScanInputs:
+    """Host copies of one scan problem.
+
+    *_f32 arrays hold the exact values the GPU sees (bf16 values widened);
+    *_bits arrays hold the bf16 bit patterns for bf16 workloads (else None)."""
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int
+    io: str
+    u: np.ndarray
+    delta: np.ndarray
+    z: np.ndarray | None
+    B: np.ndarray
+    C: np.ndarray
+    A: np.ndarray
+    delta_bias: np.ndarray | None
+    Dskip: np.ndarray | None
+    u_bits: np.ndarray | None = None
+    delta_bits: np.ndarray | None = None
+    z_bits: np.ndarray | None = None
+    B_bits: np.ndarray | None = None
+    C_bits: np.ndarray | None = None
+    softplus: bool = True
+
+    def io_array(self, name: str) -> np.ndarray:
+        """Array in the I/O dtype (uint16 bits for bf16, float32 otherwise)."""
+        if self.io == "bf16":
+            return getattr(self, name + "_bits")
+        return getattr(self, name)
+
+
+def generate(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32", seed: int = SEED_BASE,
+             reset_frac: float = 0.0, a_kind: str = "s4d_real", with_z: bool = True,
+             with_dskip: bool = True, with_bias: bool = True) -> ScanInputs:
+    """Draw one scan problem with the workload distributions above."""
+    if io not in ("f32", "bf16"):
+        raise ValueError(io)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=dim)).astype(np.float64)
+    dskip = rng.standard_normal(dim, dtype=f32)
+    u = rng.standard_normal((batch, seqlen, dim), dtype=f32)
+    z = rng.standard_normal((batch, seqlen, dim), dtype=f32)
+    delta = rng.uniform(-4.0, -2.0, size=(batch, seqlen, dim)).astype(f32)
+    Bm = rng.standard_normal((batch, seqlen, dstate), dtype=f32)
+    Cm = rng.standard_normal((batch, seqlen, dstate), dtype=f32)
+    if reset_frac > 0:
+        mask = rng.random((batch, seqlen)) < reset_frac
+        nres = int(mask.sum())
+        big = rng.uniform(30.0, 40.0, size=(nres, dim)).astype(f32)
+        delta[mask] = big
+    A = a_init(dim, dstate, a_kind, rng)
+    bias = softplus_inverse(dt0).astype(f32)
+    inp = ScanInputs(batch, seqlen, dim, dstate, io, u, delta, z if with_z else None, Bm, Cm, A,
+                     bias if with_bias else None, dskip if with_dskip else None)
+    if io == "bf16":
+        for name in ("u", "delta", "z", "B", "C"):
+            arr = getattr(inp, name)
+            if arr is None:
+                continue
+            bits, widened = bf16_round(arr)
+            setattr(inp, name + "_bits", bits)
+            setattr(inp, name, widened)
+    return inp
+
+
+def generate_workload(name: str) -> ScanInputs:
+    """The seeded inputs of a named workload (decode: the 64 tokens as one (B, 64, D) block)."""
+    w = WORKLOADS[name]
+    return generate(w.batch, w.seqlen, w.dim, w.dstate, w.io, seed=w.seed, reset_frac=w.reset_frac)
+
+
+def channel_subset(inp: ScanInputs, batches, channels) -> ScanInputs:
+    """Inputs restricted to some batch rows and channels (channels are independent SSMs)."""
+    b = np.asarray(batches)
+    d = np.asarray(channels)
+
+    def sel3(x):
+        return None if x is None else np.ascontiguousarray(x[b][:, :, d])
+
+    def sel_bl(x):
+        return None if x is None else np.ascontiguousarray(x[b])
+
+    def sel1(x):
+        return None if x is None else np.ascontiguousarray(x[d])
+
+    out = ScanInputs(len(b), inp.seqlen, len(d), inp.dstate, inp.io, sel3(inp.u), sel3(inp.delta), sel3(inp.z),
+                     sel_bl(inp.B), sel_bl(inp.C), np.ascontiguousarray(inp.A[d]), sel1(inp.delta_bias),
+                     sel1(inp.Dskip), softplus=inp.softplus)
+    return out
