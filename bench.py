@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X selective scan (S6) forward pass.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one mamba_scan_fwd call over the whole workload (all of the
+discretisation, scan, readout and epilogue), inputs already resident in HBM.
+Prints ONE JSON line.  Default workload: the Mamba-3B layer shape
+(batch 4, L 4096, D 5120, N 16, bf16 I/O, fp32 state), seeded synthetic data.
+
+Other workloads (--workload): tiny, mamba130m_layer, million_tokens, decode
+(decode: one step = 64 one-token state updates of (256, 5120, 16)).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+VALU_FP32_PEAK_TFLOPS = 78.6    # 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz, non-packed fp32
+VALU_FP32_PACKED_TFLOPS = 157.3  # published fp32 vector peak (packed fp32, not used by this code)
+# Algorithmic fp32 operations (FMA = 2, other ops and transcendentals = 1):
+FLOPS_PER_ELEMENT = 9.0          # per (b, l, d, n): dt*A, exp, input weight, *B, *x, h FMA, readout FMA
+FLOPS_PER_TOKEN_CHANNEL = 15.0   # per (b, l, d): bias add, softplus (6), skip FMA, SiLU (5), gate mul
+
+
+def algorithmic_bytes(batch, L, D, N, io_bytes, decode=False):
+    """Bytes a perfect kernel must move: each input read once, each output written once."""
+    if decode:  # per step: state read + write, per-token operands
+        return 8 * batch * D * N + 4 * io_bytes * batch * D + 2 * io_bytes * batch * N + 4 * D * N + 8 * D
+    return 4 * io_bytes * batch * L * D + 2 * io_bytes * batch * L * N + 4 * D * N + 8 * D + 4 * batch * D * N
+
+
+def metric_name():
+    try:
+        with open(os.path.join(ROOT, "BASELINE.json")) as f:
+            return json.load(f)["metric"]
+    except Exception:
+        return "selective-scan fwd elements(B*L*D*N)/s + achieved HBM GB/s, Mamba-3B layer"
+
+
+def cpu_baseline(inp, name):
+    """The fp64 oracle on a bounded sample of the same workload, timed on the host cores."""
+    import numpy as np
+
+    import oracle
+    from selective_state_space_22_amd import workloads as W
+
+    rows = {"mamba3b_layer": 2, "mamba130m_layer": 2, "tiny": 1, "million_tokens": 1, "decode": 64}.get(name, 1)
+    if name == "million_tokens":
+        sub = W.channel_subset(inp, [0], np.arange(0, inp.dim, 4))  # 64 channels, all 2^20 tokens
+        what = "batch row 0, 64 of 256 channels, all 1048576 tokens"
+    elif name == "decode":
+        sub = W.channel_subset(inp, np.arange(rows), np.arange(inp.dim))
+        what = f"{rows} of 256 sequences, all 5120 channels, 64 tokens"
+    else:
+        rows = min(rows, inp.batch)
+        sub = W.channel_subset(inp, np.arange(rows), np.arange(inp.dim))
+        what = f"batch rows 0..{rows - 1} of {inp.batch}, all channels and tokens"
+    args = [np.ascontiguousarray(x, np.float64) if x is not None else None
+            for x in (sub.u, sub.delta, sub.A, sub.B, sub.C, sub.delta_bias, sub.Dskip, sub.z)]
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.scan(*args, softplus=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    elems = sub.batch * sub.seqlen * sub.dim * sub.dstate
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}; {elems} elements in {dt:.2f} s wall (fp64, OpenMP over (batch, channel))"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mamba3b_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the scan shards over batch and channels with no "
+              "exchange, which a single GPU cannot show); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from selective_state_space_22_amd import binding
+    from selective_state_space_22_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    inp = W.generate_workload(args.workload)
+    tdt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    io_bytes = 2 if w.io == "bf16" else 4
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev).to(tdt)
+
+    def f(x):
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    u, delta, z, B, C = t(inp.u), t(inp.delta), t(inp.z), t(inp.B), t(inp.C)
+    A, bias, dskip = f(inp.A), f(inp.delta_bias), f(inp.Dskip)
+    decode = w.decode_steps > 0
+    stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+
+    if decode:
+        batch, L, D, N = w.batch, w.seqlen, w.dim, w.dstate
+        steps_in = [(u[:, k].contiguous(), delta[:, k].contiguous(), B[:, k].contiguous(), C[:, k].contiguous(),
+                     z[:, k].contiguous()) for k in range(L)]
+        state = torch.zeros((batch, D, N), dtype=torch.float32, device=dev)
+        outs = [torch.empty_like(steps_in[0][0]) for _ in range(L)]
+
+        def step():  # the state carries over between steps; the work per step is the same
+            for k in range(L):
+                uu, dd, bb, cc, zz = steps_in[k]
+                binding.mamba_state_update(state, uu, dd, A, bb, cc, bias, dskip, zz, True, out=outs[k])
+
+        units = batch * L * D * N
+        bytes_per_step = algorithmic_bytes(batch, L, D, N, io_bytes, decode=True) * L
+    else:
+        out = torch.empty_like(u)
+        last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        ws_bytes = binding.mamba_scan_fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
+                                                         1 if w.io == "bf16" else 0)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.mamba_scan_fwd(u, delta, A, B, C, bias, dskip, z, True, None, out=out, last_state=last,
+                                   workspace=ws)
+
+        units = w.elements
+        bytes_per_step = algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, io_bytes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 2)]
+    if args.flush:
+        total_ms = 0.0
+        for k in range(args.steps):
+            flush_buf.fill_(float(k))
+            ev[2 * k].record(stream)
+            step()
+            ev[2 * k + 1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+    else:
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            step()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        total_ms = ev[0].elapsed_time(ev[1])
+    ms = total_ms / args.steps
+    value = units / (ms * 1e-3)
+    gbps = bytes_per_step / (ms * 1e-3) / 1e9
+    flops = units * FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
+    tflops = flops / (ms * 1e-3) / 1e12
+    if decode:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                "note": "fp32 VALU without packed-fp32 instructions; frac vs the packed 157.3 TFLOP/s "
+                        f"figure: {tflops / VALU_FP32_PACKED_TFLOPS:.4f}"}
+    rec = {
+        "metric": metric_name(),
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "io_dtype": w.io, "state_dtype": "f32",
+                   "flush_infinity_cache": bool(args.flush), "parallelism": "single-gpu"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": bytes_per_step,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.workload)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

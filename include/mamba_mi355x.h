@@ -1,0 +1,120 @@
+/*
+ * mamba_mi355x.h -- C ABI of the MI355X (gfx950) selective scan (S6).
+ *
+ * The operation is the selective state-space layer of Mamba as stated in
+ * "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
+ *   section 2.1, eq. (2)   zero-order hold of a diagonal A:
+ *                          Abar = exp(dt*A_n), Bbar = (exp(dt*A_n) - 1)/(dt*A_n) * dt * B_n
+ *   eq. (3a)/(3b)          h_t = Abar_t * h_{t-1} + Bbar_t * x_t,   y_t = C_t . h_t
+ *   section 3.2            dt, B, C depend on the token: B_t, C_t have width N
+ *                          and are shared by all D channels; dt is per token
+ *                          and channel, made positive by softplus
+ *   Figure 1               each channel is an independent SSM with N states
+ *   Figure 3 caption       the SSM branch is gated by SiLU
+ *   section 4.1            the expanded (batch, L, D, N) state is never
+ *                          written to memory; only (batch, L, D) is
+ *   section 5              recurrent inference advances in constant time per token
+ * with these readings where the page is silent: dt = softplus(delta + bias)
+ * (bias added first); out = (y + Dskip*x) * z * sigmoid(z) when z is given;
+ * the initial state is h0 when given, else zero.
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays,
+ *     each 16-byte aligned.  The library never frees or retains them.
+ *   - "I/O tensors" (u, delta, z, B, C, out) have the element type selected
+ *     by io_dtype: MAMBA_IO_F32 (float) or MAMBA_IO_BF16 (bfloat16 bits,
+ *     rounded to nearest even on output).  A, delta_bias, Dskip, h0, state
+ *     and last_state are always float.
+ *   - Pointers documented as "nullable" may be NULL: delta_bias -> 0,
+ *     Dskip -> 0, z -> no gate, h0 -> zero initial state, last_state -> not
+ *     written.  Every other pointer must be non-NULL whenever the tensor it
+ *     names has at least one element.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued: results are valid after the stream is synchronised.  All
+ *     calls on one stream execute in order; concurrent calls on different
+ *     streams must not share output or workspace buffers.
+ *   - Return value: MAMBA_OK (0) or a mamba_status code.  Argument errors are
+ *     detected on the host before anything is enqueued and leave all buffers
+ *     untouched; MAMBA_ERR_HIP reports a failed kernel launch.  Faults inside
+ *     kernels surface as errors of the later stream synchronisation.
+ *   - Arithmetic is fp32 (state included); the entry points allocate no memory.
+ */
+#ifndef MAMBA_MI355X_H
+#define MAMBA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mamba_status {
+  MAMBA_OK = 0,
+  MAMBA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  MAMBA_ERR_DIM = 2,         /* a size is negative, zero where it must not be, or too large */
+  MAMBA_ERR_UNSUPPORTED = 3, /* dstate not in {1, 2, 4, 8, 16}                       */
+  MAMBA_ERR_DTYPE = 4,       /* io_dtype is not a mamba_io_dtype                     */
+  MAMBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size function says */
+  MAMBA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                     */
+  MAMBA_ERR_HIP = 7          /* the HIP runtime refused a kernel launch              */
+};
+
+enum mamba_io_dtype { MAMBA_IO_F32 = 0, MAMBA_IO_BF16 = 1 };
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mamba_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mamba_status_string(int status);
+
+/*
+ * Bytes of device workspace mamba_scan_fwd needs for this shape (0 when the
+ * plan runs the sequence in one piece).  A pure host function of its
+ * arguments: it needs no GPU and returns the same value on every call.
+ * Returns 0 for arguments mamba_scan_fwd would reject.
+ */
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype);
+
+/*
+ * Forward selective scan over whole sequences (eq. (2), (3a), (3b) above).
+ *   u, delta, z, out : (batch, seqlen, dim)      I/O type
+ *   B, C             : (batch, seqlen, dstate)   I/O type
+ *   A                : (dim, dstate)             float, A[d, n] = A_n of channel d
+ *   delta_bias, Dskip: (dim)                     float, nullable
+ *   h0, last_state   : (batch, dim, dstate)      float, nullable
+ *   delta_softplus   : nonzero -> dt = softplus(delta + bias), else dt = delta + bias
+ *   workspace        : device buffer of at least
+ *                      mamba_scan_fwd_workspace_size(...) bytes (may be NULL
+ *                      when that size is 0); its contents are scratch.
+ * Limits: 0 <= batch <= 65535, seqlen >= 0, dim >= 0, dstate in {1,2,4,8,16}.
+ * seqlen == 0 writes only last_state (= h0 or zero).
+ */
+int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                   const void* u, const void* delta, const float* delta_bias, const float* A,
+                   const void* B, const void* C, const float* Dskip, const void* z,
+                   int delta_softplus, const float* h0,
+                   void* out, float* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step (section 5: constant time per token, the state is
+ * the whole memory): every (batch row, channel) advances by one token.
+ *   state            : (batch, dim, dstate) float, read and overwritten in place
+ *   u, delta, z, out : (batch, dim)      I/O type
+ *   B, C             : (batch, dstate)   I/O type
+ *   A, delta_bias, Dskip, delta_softplus: as for mamba_scan_fwd.
+ * Running it for tokens 0..L-1 from a zero state gives the same outputs and
+ * final state as mamba_scan_fwd over those L tokens.
+ * Limits: batch >= 0, dim >= 0, dstate in {1,2,4,8,16}.
+ */
+int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
+                       const void* u, const void* delta, const float* delta_bias, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z,
+                       int delta_softplus, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_MI355X_H */

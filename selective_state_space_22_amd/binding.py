@@ -1,0 +1,157 @@
+"""Thin ctypes binding of libmamba_mi355x.so (include/mamba_mi355x.h).
+
+The functions keep the C names.  They only marshal torch tensors (device
+memory, the current HIP stream) into the C ABI; every step of the scan runs
+in the library's HIP kernels.  There is no fallback: if the library is
+missing or the tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmamba_mi355x.so")
+
+MAMBA_IO_F32 = 0
+MAMBA_IO_BF16 = 1
+
+_lib = None
+
+
+class MambaError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: status {status} ({status_string(status)})")
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and type the C ABI.  Raises if the shared library is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m selective_state_space_22_amd.build`")
+    lib = ctypes.CDLL(p)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.mamba_version.argtypes = []
+    lib.mamba_version.restype = I
+    lib.mamba_status_string.argtypes = [I]
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    lib.mamba_scan_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I]
+    lib.mamba_scan_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd.argtypes = [I64, I64, I64, I64, I, P, P, P, P, P, P, P, P, I, P, P, P, P, ctypes.c_size_t, P]
+    lib.mamba_scan_fwd.restype = I
+    lib.mamba_state_update.argtypes = [I64, I64, I64, I, P, P, P, P, P, P, P, P, P, I, P, P]
+    lib.mamba_state_update.restype = I
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mamba_status_string(int(status)).decode()
+
+
+def mamba_version() -> int:
+    return int(load_library().mamba_version())
+
+
+def _io_dtype(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return MAMBA_IO_F32
+    if t.dtype == torch.bfloat16:
+        return MAMBA_IO_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t, name, dtype=None, shape=None, device=None):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, io_dtype: int) -> int:
+    return int(load_library().mamba_scan_fwd_workspace_size(batch, seqlen, dim, dstate, io_dtype))
+
+
+def mamba_scan_fwd(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
+                   out=None, last_state=None, workspace=None, return_last_state=True):
+    """Forward selective scan.  u, delta, z: (batch, L, D); B, C: (batch, L, N); A: (D, N) float32.
+
+    Returns (out, last_state); out has u's dtype, last_state is float32 (batch, D, N)."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty_like(u)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, D, N), dtype=f32, device=dev)
+    ws_bytes = mamba_scan_fwd_workspace_size(batch, L, D, N, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, "workspace", device=dev)
+    st = lib.mamba_scan_fwd(
+        batch, L, D, N, io,
+        _ptr(u, "u", u.dtype, (batch, L, D), dev), _ptr(delta, "delta", u.dtype, (batch, L, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev),
+        _ptr(B, "B", u.dtype, (batch, L, N), dev), _ptr(C, "C", u.dtype, (batch, L, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, L, D), dev),
+        int(bool(delta_softplus)), _ptr(h0, "h0", f32, (batch, D, N), dev),
+        _ptr(out, "out", u.dtype, (batch, L, D), dev), _ptr(last_state, "last_state", f32, (batch, D, N), dev),
+        ws_ptr, workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_scan_fwd", st)
+    return out, last_state
+
+
+def mamba_state_update(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True,
+                       out=None):
+    """One decode step in place on state (batch, D, N) float32.  u, delta, z: (batch, D); B, C: (batch, N)."""
+    import torch
+
+    lib = load_library()
+    batch, D = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty_like(u)
+    st = lib.mamba_state_update(
+        batch, D, N, io, _ptr(state, "state", f32, (batch, D, N), dev),
+        _ptr(u, "u", u.dtype, (batch, D), dev), _ptr(delta, "delta", u.dtype, (batch, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev),
+        _ptr(B, "B", u.dtype, (batch, N), dev), _ptr(C, "C", u.dtype, (batch, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, D), dev),
+        int(bool(delta_softplus)), _ptr(out, "out", u.dtype, (batch, D), dev), _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_state_update", st)
+    return out

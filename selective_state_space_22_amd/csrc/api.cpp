@@ -1,0 +1,173 @@
+// api.cpp -- the C ABI declared in include/mamba_mi355x.h.
+//
+// Every entry point validates its arguments on the host before it touches
+// the HIP runtime, then enqueues kernels on the caller's stream and returns.
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/mamba_mi355x.h"
+#include "s6_internal.h"
+
+namespace {
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("MAMBA_MI355X_DEBUG");
+    return v && v[0] && v[0] != '0';
+  }();
+  return on;
+}
+
+int fail(int status, const char* where, const char* what) {
+  if (debug_enabled()) std::fprintf(stderr, "[mamba_mi355x] %s: %s (%s)\n", where, mamba_status_string(status), what);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxBatch = 65535;
+
+// Shape and dtype checks shared by the entry points (MAMBA_OK if usable).
+int check_shape(const char* where, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io) {
+  if (io != MAMBA_IO_F32 && io != MAMBA_IO_BF16) return fail(MAMBA_ERR_DTYPE, where, "io_dtype");
+  if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return fail(MAMBA_ERR_DIM, where, "negative or zero size");
+  if (batch > kMaxBatch) return fail(MAMBA_ERR_DIM, where, "batch > 65535");
+  if (!s6::dstate_supported(dstate)) return fail(MAMBA_ERR_UNSUPPORTED, where, "dstate");
+  // element counts must fit comfortably in 63 bits
+  const double n = (double)batch * (double)(seqlen > 0 ? seqlen : 1) * (double)(dim > 0 ? dim : 1) * (double)dstate;
+  if (n > 4.0e18) return fail(MAMBA_ERR_DIM, where, "tensor too large");
+  return MAMBA_OK;
+}
+
+struct PtrCheck {
+  const char* where;
+  int status = MAMBA_OK;
+  // A tensor that must be present when `needed`; any present pointer must be aligned.
+  void req(const void* p, bool needed, const char* name) {
+    if (status != MAMBA_OK) return;
+    if (!p && needed) status = fail(MAMBA_ERR_NULL, where, name);
+    else if (p && !aligned16(p)) status = fail(MAMBA_ERR_ALIGN, where, name);
+  }
+  void opt(const void* p, const char* name) { req(p, false, name); }
+};
+
+}  // namespace
+
+extern "C" {
+
+int mamba_version(void) { return 100; }
+
+const char* mamba_status_string(int status) {
+  switch (status) {
+    case MAMBA_OK: return "ok";
+    case MAMBA_ERR_NULL: return "a required pointer is NULL";
+    case MAMBA_ERR_DIM: return "invalid size";
+    case MAMBA_ERR_UNSUPPORTED: return "unsupported dstate (supported: 1, 2, 4, 8, 16)";
+    case MAMBA_ERR_DTYPE: return "invalid io_dtype";
+    case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MAMBA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MAMBA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype) {
+  if (check_shape("mamba_scan_fwd_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK) return 0;
+  return s6::plan_scan(batch, seqlen, dim, dstate).ws_bytes;
+}
+
+int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                   const void* u, const void* delta, const float* delta_bias, const float* A,
+                   const void* B, const void* C, const float* Dskip, const void* z,
+                   int delta_softplus, const float* h0,
+                   void* out, float* last_state,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "mamba_scan_fwd";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  const bool tokens = batch > 0 && seqlen > 0 && dim > 0;
+  const bool chans = batch > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(u, tokens, "u");
+  pc.req(delta, tokens, "delta");
+  pc.req(A, tokens, "A");
+  pc.req(B, tokens, "B");
+  pc.req(C, tokens, "C");
+  pc.req(out, tokens, "out");
+  pc.opt(delta_bias, "delta_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(z, "z");
+  pc.opt(h0, "h0");
+  pc.opt(last_state, "last_state");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (!chans) return MAMBA_OK;
+  const s6::ScanPlan plan = s6::plan_scan(batch, seqlen, dim, dstate);
+  if (tokens && plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  s6::ScanArgs a;
+  a.u = u;
+  a.delta = delta;
+  a.bias = delta_bias;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.out = out;
+  a.last = last_state;
+  a.agg_h = static_cast<float*>(workspace);
+  a.agg_s = plan.ws_bytes > 0 ? a.agg_h + (size_t)batch * plan.nchunks * dim * dstate : nullptr;
+  a.batch = batch;
+  a.L = seqlen;
+  a.D = dim;
+  a.chunk_len = plan.chunk_len;
+  a.nchunks = plan.nchunks;
+  a.softplus = delta_softplus != 0;
+  hipError_t e = s6::launch_scan(a, plan, io_dtype, (int)dstate, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
+int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
+                       const void* u, const void* delta, const float* delta_bias, const float* A,
+                       const void* B, const void* C, const float* Dskip, const void* z,
+                       int delta_softplus, void* out, void* stream) {
+  const char* where = "mamba_state_update";
+  int st = check_shape(where, batch, 1, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  const bool any = batch > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(state, any, "state");
+  pc.req(u, any, "u");
+  pc.req(delta, any, "delta");
+  pc.req(A, any, "A");
+  pc.req(B, any, "B");
+  pc.req(C, any, "C");
+  pc.req(out, any, "out");
+  pc.opt(delta_bias, "delta_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(z, "z");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (!any) return MAMBA_OK;
+  s6::StepArgs a;
+  a.state = state;
+  a.u = u;
+  a.delta = delta;
+  a.bias = delta_bias;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.dskip = Dskip;
+  a.z = z;
+  a.out = out;
+  a.batch = batch;
+  a.D = dim;
+  a.softplus = delta_softplus != 0;
+  hipError_t e = s6::launch_step(a, io_dtype, (int)dstate, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,298 @@
+// scan_kernels.hip -- forward selective scan on gfx950.
+//
+// Layout (row-major): u, delta, z, out (batch, L, D); B, C (batch, L, N);
+// A (D, N); bias, Dskip (D); h0, last_state (batch, D, N).
+//
+// Mapping: one lane owns one channel d of one batch row and keeps its N
+// states in VGPRs for the whole chunk; the 64 lanes of a wave are 64
+// consecutive channels, so the per-token loads of u/delta/z and the store of
+// out are 64 consecutive elements, and B_t/C_t (shared by all channels,
+// "Mamba 状态空间模型原理与 Transformer 对比", section 3.2) are wave-uniform
+// scalar loads.  The expanded state (batch, L, D, N) never leaves registers
+// (section 4.1: only the (batch, L, D) output returns to HBM).
+//
+// When batch*D alone cannot fill the GPU, L is cut into chunks (the parallel
+// scan of section 4.1, over chunks): each chunk except the last runs the
+// recurrence from a zero state and keeps only its end state b_g and the sum
+// of dt over the chunk; a carry pass composes them in order with the
+// associative step h_in(g+1) = e^{A * sum dt_g} h_in(g) + b_g (the product of
+// the chunk's Abar is e^{A * sum dt} because A does not vary in time); the
+// output pass then reruns every chunk from its exact carry-in.
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+
+template <typename IO, int N>
+struct BCLoader;
+
+// bf16, even N: N/2 wave-uniform 32-bit words per token.
+template <int N>
+struct BCLoader<uint16_t, N> {
+  static __device__ __forceinline__ void load(const uint16_t* __restrict__ p, float (&v)[N]) {
+    if constexpr (N % 2 == 0) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+      for (int j = 0; j < N / 2; ++j) {
+        uint32_t x = w[j];
+        v[2 * j] = bf16_lo(x);
+        v[2 * j + 1] = bf16_hi(x);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) v[n] = bf16_to_f32(p[n]);
+    }
+  }
+};
+
+template <int N>
+struct BCLoader<float, N> {
+  static __device__ __forceinline__ void load(const float* __restrict__ p, float (&v)[N]) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = p[n];
+  }
+};
+
+// Chunk end states from a zero start (all chunks but the last).
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void scan_chunk_state_kernel(ScanArgs a) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t g = blockIdx.z;
+  if (d >= a.D) return;
+  const int64_t L = a.L, D = a.D;
+  const IO* __restrict__ u = static_cast<const IO*>(a.u);
+  const IO* __restrict__ dl = static_cast<const IO*>(a.delta);
+  const IO* __restrict__ Bp = static_cast<const IO*>(a.B);
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  ChanConst<N> cc;
+  cc.load(a.A + d * N);
+  float h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  float s = 0.0f, sc = 0.0f;  // compensated sum of dt
+  const int64_t t0 = g * a.chunk_len;
+  const int64_t t1 = t0 + a.chunk_len < L ? t0 + a.chunk_len : L;
+  const bool sp = a.softplus != 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    const size_t i = ((size_t)b * L + t) * D + d;
+    float Bt[N];
+    BCLoader<IO, N>::load(Bp + ((size_t)b * L + t) * N, Bt);
+    TokenFront f = make_front(load_io(dl, i), bias, sp);
+    token_step_state<N>(cc, f, load_io(u, i), Bt, h);
+    float yk = f.dt - sc;  // Kahan summation of dt
+    float tk = s + yk;
+    sc = (tk - s) - yk;
+    s = tk;
+  }
+  const size_t base = ((size_t)b * a.nchunks + g) * D + d;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a.agg_h[base * N + n] = h[n];
+  a.agg_s[base] = s;
+}
+
+// Carry pass: one lane per (batch, channel, state), sequential over chunks.
+// On exit agg_h[b, g, d, n] holds the state entering chunk g.
+template <int N>
+__global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs a) {
+  const int64_t lane = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t D = a.D;
+  if (lane >= a.batch * D * N) return;
+  const int64_t n = lane % N;
+  const int64_t d = (lane / N) % D;
+  const int64_t b = lane / (N * D);
+  const float a2 = a.A[d * N + n] * kLog2e;
+  float carry = a.h0 ? a.h0[lane] : 0.0f;
+  const int G = a.nchunks;
+  for (int g = 0; g < G - 1; ++g) {
+    const size_t base = ((size_t)b * G + g) * D + d;
+    const float decay = ex2(a2 * a.agg_s[base]);
+    const float bg = a.agg_h[base * N + n];
+    a.agg_h[base * N + n] = carry;
+    carry = __builtin_fmaf(decay, carry, bg);
+  }
+  a.agg_h[(((size_t)b * G + (G - 1)) * D + d) * N + n] = carry;
+}
+
+// Output pass: every chunk from its carry-in (or h0 / zero when unchunked).
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void scan_output_kernel(ScanArgs a) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t g = blockIdx.z;
+  if (d >= a.D) return;
+  const int64_t L = a.L, D = a.D;
+  const IO* __restrict__ u = static_cast<const IO*>(a.u);
+  const IO* __restrict__ dl = static_cast<const IO*>(a.delta);
+  const IO* __restrict__ zp = static_cast<const IO*>(a.z);
+  const IO* __restrict__ Bp = static_cast<const IO*>(a.B);
+  const IO* __restrict__ Cp = static_cast<const IO*>(a.C);
+  IO* __restrict__ out = static_cast<IO*>(a.out);
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float dskip = a.dskip ? a.dskip[d] : 0.0f;
+  ChanConst<N> cc;
+  cc.load(a.A + d * N);
+  float h[N];
+  if (a.nchunks > 1) {
+    const float* src = a.agg_h + (((size_t)b * a.nchunks + g) * D + d) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = src[n];
+  } else if (a.h0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = a.h0[((size_t)b * D + d) * N + n];
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = 0.0f;
+  }
+  const int64_t t0 = g * a.chunk_len;
+  const int64_t t1 = t0 + a.chunk_len < L ? t0 + a.chunk_len : L;
+  const bool sp = a.softplus != 0;
+  const bool has_z = zp != nullptr;
+  for (int64_t t = t0; t < t1; ++t) {
+    const size_t i = ((size_t)b * L + t) * D + d;
+    float Bt[N], Ct[N];
+    BCLoader<IO, N>::load(Bp + ((size_t)b * L + t) * N, Bt);
+    BCLoader<IO, N>::load(Cp + ((size_t)b * L + t) * N, Ct);
+    const float x = load_io(u, i);
+    TokenFront f = make_front(load_io(dl, i), bias, sp);
+    float y = token_step<N>(cc, f, x, Bt, Ct, h);
+    const float zv = has_z ? load_io(zp, i) : 0.0f;
+    store_io(out, i, epilogue(y, x, dskip, has_z, zv));
+  }
+  if (a.last && g == a.nchunks - 1) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) a.last[((size_t)b * D + d) * N + n] = h[n];
+  }
+}
+
+bool dstate_supported(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
+
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  ScanPlan p;
+  p.block = D >= 256 ? 256 : (int32_t)(((D + 63) / 64) * 64);
+  if (p.block < 64) p.block = 64;
+  // Waves of the unchunked scan; cut L until about two waves per SIMD
+  // (1024 SIMDs on 256 CUs), keeping chunks of at least 256 tokens.
+  const int64_t waves = batch * ((D + 63) / 64);
+  const int64_t target = 2048;
+  int64_t g = waves > 0 ? (target + waves - 1) / waves : 1;
+  const int64_t gmax = L / 256 > 1 ? L / 256 : 1;
+  if (g > gmax) g = gmax;
+  if (g < 1) g = 1;
+  p.chunk_len = L > 0 ? (L + g - 1) / g : 0;
+  p.nchunks = (int32_t)(p.chunk_len > 0 ? (L + p.chunk_len - 1) / p.chunk_len : 1);
+  if (p.nchunks < 1) p.nchunks = 1;
+  p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) : 0;
+  return p;
+}
+
+template <typename IO, int N>
+static hipError_t launch_scan_t(const ScanArgs& a, const ScanPlan& p, hipStream_t s) {
+  const int block = p.block;
+  const dim3 grid_c((unsigned)((a.D + block - 1) / block), (unsigned)a.batch, (unsigned)p.nchunks);
+  if (p.nchunks > 1) {
+    const dim3 grid_a((unsigned)((a.D + block - 1) / block), (unsigned)a.batch, (unsigned)(p.nchunks - 1));
+    hipLaunchKernelGGL((scan_chunk_state_kernel<IO, N>), grid_a, dim3(block), 0, s, a);
+    const int64_t lanes = a.batch * a.D * N;
+    hipLaunchKernelGGL((scan_carry_kernel<N>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL((scan_output_kernel<IO, N>), grid_c, dim3(block), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename IO>
+static hipError_t launch_scan_io(const ScanArgs& a, const ScanPlan& p, int N, hipStream_t s) {
+  switch (N) {
+    case 1: return launch_scan_t<IO, 1>(a, p, s);
+    case 2: return launch_scan_t<IO, 2>(a, p, s);
+    case 4: return launch_scan_t<IO, 4>(a, p, s);
+    case 8: return launch_scan_t<IO, 8>(a, p, s);
+    case 16: return launch_scan_t<IO, 16>(a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// L == 0: no output; the final state is the initial one.
+__global__ __launch_bounds__(256) void scan_empty_kernel(float* last, const float* h0, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) last[i] = h0 ? h0[i] : 0.0f;
+}
+
+hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, hipStream_t s) {
+  if (a.batch == 0 || a.D == 0) return hipSuccess;
+  if (a.L == 0) {
+    if (!a.last) return hipSuccess;
+    const int64_t count = a.batch * a.D * N;
+    hipLaunchKernelGGL(scan_empty_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, a.last, a.h0, count);
+    return hipGetLastError();
+  }
+  return io == kIoBF16 ? launch_scan_io<uint16_t>(a, p, N, s) : launch_scan_io<float>(a, p, N, s);
+}
+
+// ----------------------------------------------------------------- decode
+
+// One token for every (batch, channel): lane = (b, d), state read and written in place.
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.batch * a.D) return;
+  const int64_t d = idx % a.D;
+  const int64_t b = idx / a.D;
+  const IO* __restrict__ Bp = static_cast<const IO*>(a.B) + b * N;
+  const IO* __restrict__ Cp = static_cast<const IO*>(a.C) + b * N;
+  float Bt[N], Ct[N], h[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    Bt[n] = load_io(Bp, n);
+    Ct[n] = load_io(Cp, n);
+  }
+  float* __restrict__ st = a.state + (size_t)idx * N;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j) {
+      float4 v = reinterpret_cast<const float4*>(st)[j];
+      h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = st[n];
+  }
+  ChanConst<N> cc;
+  cc.load(a.A + d * N);
+  const float x = load_io(static_cast<const IO*>(a.u), idx);
+  TokenFront f = make_front(load_io(static_cast<const IO*>(a.delta), idx), a.bias ? a.bias[d] : 0.0f, a.softplus != 0);
+  float y = token_step<N>(cc, f, x, Bt, Ct, h);
+  const bool has_z = a.z != nullptr;
+  const float zv = has_z ? load_io(static_cast<const IO*>(a.z), idx) : 0.0f;
+  store_io(static_cast<IO*>(a.out), idx, epilogue(y, x, a.dskip ? a.dskip[d] : 0.0f, has_z, zv));
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j)
+      reinterpret_cast<float4*>(st)[j] = make_float4(h[4 * j], h[4 * j + 1], h[4 * j + 2], h[4 * j + 3]);
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) st[n] = h[n];
+  }
+}
+
+template <typename IO>
+static hipError_t launch_step_io(const StepArgs& a, int N, hipStream_t s) {
+  const int64_t lanes = a.batch * a.D;
+  const dim3 grid((unsigned)((lanes + 255) / 256));
+  switch (N) {
+    case 1: hipLaunchKernelGGL((state_update_kernel<IO, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((state_update_kernel<IO, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((state_update_kernel<IO, 4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((state_update_kernel<IO, 8>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((state_update_kernel<IO, 16>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const StepArgs& a, int io, int N, hipStream_t s) {
+  if (a.batch == 0 || a.D == 0) return hipSuccess;
+  return io == kIoBF16 ? launch_step_io<uint16_t>(a, N, s) : launch_step_io<float>(a, N, s);
+}
+
+}  // namespace s6

@@ -9,13 +9,14 @@ A-initialisation ablation (kb.agiseed.tech Mamba overview, section 6.5).
 
 Distributions (all drawn in float32 from numpy PCG64):
   dt0    ~ exp(U(ln 1e-3, ln 1e-1))        per channel, delta_bias = softplus^-1(dt0)
+  A      : A[d, n] = -(n + 1) unless another real initialisation is asked for
   Dskip  ~ N(0, 1)                          per channel
   u, z   ~ N(0, 1)                          (batch, L, D)
   delta  ~ U(-4, -2)                        (batch, L, D), raw (pre-softplus)
   B, C   ~ N(0, 1)                          (batch, L, N)
   reset  (million-token workload only): Bernoulli(0.01) per (batch row, token),
          shared by all channels; at those tokens delta ~ U(30, 40).
-Draw order: dt0, Dskip, u, z, delta, B, C, [reset mask, reset deltas].
+Each tensor is drawn from its own seed stream (see ``generate``).
 bf16 workloads draw in float32 and round once to bf16 (round to nearest even).
 """
 from __future__ import annotations
@@ -26,6 +27,7 @@ import math
 import numpy as np
 
 SEED_BASE = 22_000
+_BLOCK = 1 << 22  # elements per independently seeded / processed block of a large tensor
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,18 +64,36 @@ WORKLOADS = {
 
 
 def bf16_round(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
-    """Round float32 -> bf16 with round-to-nearest-even.
+    """Round float32 -> bf16 with round-to-nearest-even (NaN stays NaN).
 
     Returns (bits as uint16, the same values widened back to float32)."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    nan = np.isnan(x)
-    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    r = ((u + bias) >> 16).astype(np.uint16)
-    if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
-    widened = (r.astype(np.uint32) << 16).view(np.float32)
-    return r, widened
+    from concurrent.futures import ThreadPoolExecutor
+
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    bits = np.empty(x.shape, dtype=np.uint16)
+    widened = np.empty(x.shape, dtype=np.float32)
+
+    def one(j):
+        sl = slice(j * _BLOCK, (j + 1) * _BLOCK)
+        u = x[sl].view(np.uint32)
+        r = (u >> np.uint32(16)) & np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += u
+        r >>= np.uint32(16)
+        nan = np.isnan(x[sl])
+        if nan.any():
+            r[nan] = (u[nan] >> np.uint32(16)) | np.uint32(0x40)
+        bits[sl] = r
+        r <<= np.uint32(16)
+        widened[sl] = r.view(np.float32)
+
+    nblk = max(1, -(-x.size // _BLOCK))
+    if nblk == 1:
+        one(0)
+    else:
+        with ThreadPoolExecutor(min(16, nblk)) as ex:
+            list(ex.map(one, range(nblk)))
+    return bits, widened
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -133,29 +153,60 @@ class ScanInputs:
         return getattr(self, name)
 
 
+def _fill(seq: np.random.SeedSequence, shape, kind: str, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """Draw a float32 tensor from its own seed stream, in fixed-size blocks with
+    per-block child streams (so the values do not depend on the thread count)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    nblk = max(1, -(-flat.size // _BLOCK))
+    kids = seq.spawn(nblk)
+
+    def one(j):
+        g = np.random.Generator(np.random.PCG64(kids[j]))
+        part = flat[j * _BLOCK:(j + 1) * _BLOCK]
+        if kind == "normal":
+            g.standard_normal(out=part, dtype=np.float32)
+        else:  # uniform on [lo, hi)
+            g.random(out=part, dtype=np.float32)
+            part *= np.float32(hi - lo)
+            part += np.float32(lo)
+
+    if nblk == 1:
+        one(0)
+    else:
+        with ThreadPoolExecutor(min(16, nblk)) as ex:
+            list(ex.map(one, range(nblk)))
+    return out
+
+
 def generate(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32", seed: int = SEED_BASE,
              reset_frac: float = 0.0, a_kind: str = "s4d_real", with_z: bool = True,
              with_dskip: bool = True, with_bias: bool = True) -> ScanInputs:
-    """Draw one scan problem with the workload distributions above."""
+    """Draw one scan problem with the workload distributions above.
+
+    Every tensor has its own stream: SeedSequence(seed).spawn(8) in the order
+    dt0, Dskip, u, z, delta, B, C, reset; large tensors are drawn in blocks of
+    2^22 elements, each from a child stream of the tensor's stream."""
     if io not in ("f32", "bf16"):
         raise ValueError(io)
-    rng = np.random.Generator(np.random.PCG64(seed))
-    f32 = np.float32
-    dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), size=dim)).astype(np.float64)
-    dskip = rng.standard_normal(dim, dtype=f32)
-    u = rng.standard_normal((batch, seqlen, dim), dtype=f32)
-    z = rng.standard_normal((batch, seqlen, dim), dtype=f32)
-    delta = rng.uniform(-4.0, -2.0, size=(batch, seqlen, dim)).astype(f32)
-    Bm = rng.standard_normal((batch, seqlen, dstate), dtype=f32)
-    Cm = rng.standard_normal((batch, seqlen, dstate), dtype=f32)
+    seqs = np.random.SeedSequence(seed).spawn(8)
+    dt0 = np.exp(_fill(seqs[0], (dim,), "uniform", math.log(1e-3), math.log(1e-1)).astype(np.float64))
+    dskip = _fill(seqs[1], (dim,), "normal")
+    u = _fill(seqs[2], (batch, seqlen, dim), "normal")
+    z = _fill(seqs[3], (batch, seqlen, dim), "normal") if with_z else None
+    delta = _fill(seqs[4], (batch, seqlen, dim), "uniform", -4.0, -2.0)
+    Bm = _fill(seqs[5], (batch, seqlen, dstate), "normal")
+    Cm = _fill(seqs[6], (batch, seqlen, dstate), "normal")
     if reset_frac > 0:
-        mask = rng.random((batch, seqlen)) < reset_frac
+        g = np.random.Generator(np.random.PCG64(seqs[7]))
+        mask = g.random((batch, seqlen)) < reset_frac
         nres = int(mask.sum())
-        big = rng.uniform(30.0, 40.0, size=(nres, dim)).astype(f32)
-        delta[mask] = big
-    A = a_init(dim, dstate, a_kind, rng)
-    bias = softplus_inverse(dt0).astype(f32)
-    inp = ScanInputs(batch, seqlen, dim, dstate, io, u, delta, z if with_z else None, Bm, Cm, A,
+        delta[mask] = g.uniform(30.0, 40.0, size=(nres, dim)).astype(np.float32)
+    A = a_init(dim, dstate, a_kind, np.random.Generator(np.random.PCG64(seed + 1_000_000)))
+    bias = softplus_inverse(dt0).astype(np.float32)
+    inp = ScanInputs(batch, seqlen, dim, dstate, io, u, delta, z, Bm, Cm, A,
                      bias if with_bias else None, dskip if with_dskip else None)
     if io == "bf16":
         for name in ("u", "delta", "z", "B", "C"):
@@ -163,8 +214,8 @@ def generate(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32", se
             if arr is None:
                 continue
             bits, widened = bf16_round(arr)
-            setattr(inp, name + "_bits", bits)
-            setattr(inp, name, widened)
+            setattr(inp, name + "_bits", bits.reshape(arr.shape))
+            setattr(inp, name, widened.reshape(arr.shape))
     return inp
 
 

@@ -1,0 +1,131 @@
+"""C ABI of libmamba_mi355x.so on the host: symbols, status strings, workspace
+sizing and argument validation.  No kernel is launched: every call here is
+rejected by the host-side checks before the HIP runtime is touched (the fake
+device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_22_amd import binding
+from selective_state_space_22_amd import build as lib_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba_mi355x.h")
+
+OK, ERR_NULL, ERR_DIM, ERR_UNSUPPORTED, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        lib_build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["mamba_scan_fwd", "mamba_scan_fwd_workspace_size", "mamba_state_update",
+                                    "mamba_status_string", "mamba_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mamba_version() == 100
+    seen = set()
+    for st in range(8):
+        s = binding.status_string(st)
+        assert s and s not in seen
+        seen.add(s)
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_workspace_size_is_a_pure_function_of_shape(lib):
+    ws = binding.mamba_scan_fwd_workspace_size
+    # one-piece plans need no workspace
+    assert ws(4, 4096, 5120, 16, 1) == ws(4, 4096, 5120, 16, 1)
+    assert ws(1, 256, 64, 16, 0) == 0
+    # the million-token plan cuts L: workspace holds (batch, chunks, D, N+1) floats
+    w = ws(1, 1 << 20, 256, 16, 0)
+    assert w > 0 and w % (256 * 17 * 4) == 0
+    # rejected shapes report 0
+    assert ws(1, 16, 64, 3, 0) == 0
+    assert ws(1, 16, 64, 16, 7) == 0
+    assert ws(-1, 16, 64, 16, 0) == 0
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def scan_call(lib, batch=1, L=8, D=64, N=16, io=0, u=FAKE, delta=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE,
+              Dskip=None, z=None, h0=None, out=FAKE, last=None, ws=None, ws_bytes=0):
+    return lib.mamba_scan_fwd(batch, L, D, N, io, u, delta, bias, A, B, C, Dskip, z, 1, h0, out, last, ws, ws_bytes,
+                              None)
+
+
+def step_call(lib, batch=2, D=64, N=16, io=0, state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, out=FAKE,
+              z=None):
+    return lib.mamba_state_update(batch, D, N, io, state, u, delta, None, A, B, C, None, z, 1, out, None)
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "out"])
+def test_scan_rejects_null_required_pointer(lib, field):
+    assert scan_call(lib, N=3, **{field: None}) == ERR_UNSUPPORTED  # shape checks come first
+    assert scan_call(lib, **{field: None}) == ERR_NULL
+
+
+def test_scan_rejects_bad_shapes_and_dtype(lib):
+    assert scan_call(lib, io=2) == ERR_DTYPE
+    assert scan_call(lib, batch=-1) == ERR_DIM
+    assert scan_call(lib, L=-5) == ERR_DIM
+    assert scan_call(lib, N=0) == ERR_DIM
+    assert scan_call(lib, batch=70000) == ERR_DIM
+    for n in (3, 5, 17, 32):
+        assert scan_call(lib, N=n) == ERR_UNSUPPORTED
+
+
+def test_scan_rejects_misaligned_pointers(lib):
+    for field in ("u", "delta", "A", "B", "C", "out", "bias", "Dskip", "z", "h0", "last"):
+        assert scan_call(lib, **{field: FAKE + 2}) == ERR_ALIGN, field
+
+
+def test_scan_rejects_missing_or_small_workspace(lib):
+    need = binding.mamba_scan_fwd_workspace_size(1, 1 << 20, 256, 16, 0)
+    assert need > 0
+    assert scan_call(lib, L=1 << 20, D=256) == ERR_WORKSPACE
+    assert scan_call(lib, L=1 << 20, D=256, ws=FAKE, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def test_state_update_validation(lib):
+    assert step_call(lib, io=5) == ERR_DTYPE
+    assert step_call(lib, N=7) == ERR_UNSUPPORTED
+    assert step_call(lib, D=-1) == ERR_DIM
+    for field in ("state", "u", "delta", "A", "B", "C", "out"):
+        assert step_call(lib, **{field: None}) == ERR_NULL, field
+        assert step_call(lib, **{field: FAKE + 4}) == ERR_ALIGN, field
+    assert step_call(lib, z=FAKE + 8) == ERR_ALIGN
+
+
+def test_empty_problems_need_no_pointers(lib):
+    # nothing to read or write: accepted without touching the device
+    assert scan_call(lib, batch=0, u=None, delta=None, A=None, B=None, C=None, out=None) == OK
+    assert scan_call(lib, D=0, u=None, delta=None, A=None, B=None, C=None, out=None) == OK
+    assert step_call(lib, batch=0, state=None, u=None, delta=None, A=None, B=None, C=None, out=None) == OK
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    u = torch.zeros(1, 4, 64)
+    with pytest.raises((ValueError, TypeError)):
+        binding.mamba_scan_fwd(u, u, torch.zeros(64, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
