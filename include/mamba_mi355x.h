@@ -69,10 +69,12 @@ int mamba_version(void);
 const char* mamba_status_string(int status);
 
 /*
- * Bytes of device workspace mamba_scan_fwd needs for this shape (0 when the
- * plan runs the sequence in one piece).  A pure host function of its
- * arguments: it needs no GPU and returns the same value on every call.
- * Returns 0 for arguments mamba_scan_fwd would reject.
+ * Bytes of device workspace mamba_scan_fwd needs for this shape: work
+ * counters, the state handed between sequence chunks, or per-chunk aggregates
+ * (about 4*N bytes per (batch row, channel) and chunk; 0 for some small
+ * shapes).  A pure host function of its arguments: it needs no GPU and returns
+ * the same value on every call.  Returns 0 for arguments mamba_scan_fwd would
+ * reject.
  */
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype);
 
@@ -87,8 +89,8 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim,
  *   workspace        : device buffer of at least
  *                      mamba_scan_fwd_workspace_size(...) bytes (may be NULL
  *                      when that size is 0); its contents are scratch.
- * Limits: 0 <= batch <= 65535, seqlen >= 0, dim >= 0, dstate in {1,2,4,8,16}.
- * seqlen == 0 writes only last_state (= h0 or zero).
+ * Limits: 0 <= batch <= 65535, seqlen >= 0, 0 <= dim <= 4194304,
+ * dstate in {1,2,4,8,16}.  seqlen == 0 writes only last_state (= h0 or zero).
  */
 int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
                    const void* u, const void* delta, const float* delta_bias, const float* A,
@@ -106,7 +108,7 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
  *   A, delta_bias, Dskip, delta_softplus: as for mamba_scan_fwd.
  * Running it for tokens 0..L-1 from a zero state gives the same outputs and
  * final state as mamba_scan_fwd over those L tokens.
- * Limits: batch >= 0, dim >= 0, dstate in {1,2,4,8,16}.
+ * Limits: 0 <= batch <= 65535, 0 <= dim <= 4194304, dstate in {1,2,4,8,16}.
  */
 int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
                        const void* u, const void* delta, const float* delta_bias, const float* A,

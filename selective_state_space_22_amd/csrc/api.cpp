@@ -26,12 +26,14 @@ int fail(int status, const char* where, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t kMaxDim = int64_t(1) << 22;
 
 // Shape and dtype checks shared by the entry points (MAMBA_OK if usable).
 int check_shape(const char* where, int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io) {
   if (io != MAMBA_IO_F32 && io != MAMBA_IO_BF16) return fail(MAMBA_ERR_DTYPE, where, "io_dtype");
   if (batch < 0 || seqlen < 0 || dim < 0 || dstate <= 0) return fail(MAMBA_ERR_DIM, where, "negative or zero size");
   if (batch > kMaxBatch) return fail(MAMBA_ERR_DIM, where, "batch > 65535");
+  if (dim > kMaxDim) return fail(MAMBA_ERR_DIM, where, "dim > 4194304");
   if (!s6::dstate_supported(dstate)) return fail(MAMBA_ERR_UNSUPPORTED, where, "dstate");
   // element counts must fit comfortably in 63 bits
   const double n = (double)batch * (double)(seqlen > 0 ? seqlen : 1) * (double)(dim > 0 ? dim : 1) * (double)dstate;
@@ -117,15 +119,15 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   a.h0 = h0;
   a.out = out;
   a.last = last_state;
-  a.agg_h = static_cast<float*>(workspace);
-  a.agg_s = plan.ws_bytes > 0 ? a.agg_h + (size_t)batch * plan.nchunks * dim * dstate : nullptr;
+  a.agg_h = nullptr;
+  a.agg_s = nullptr;
   a.batch = batch;
   a.L = seqlen;
   a.D = dim;
   a.chunk_len = plan.chunk_len;
   a.nchunks = plan.nchunks;
   a.softplus = delta_softplus != 0;
-  hipError_t e = s6::launch_scan(a, plan, io_dtype, (int)dstate, static_cast<hipStream_t>(stream));
+  hipError_t e = s6::launch_scan(a, plan, io_dtype, (int)dstate, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
   return MAMBA_OK;
 }

@@ -46,20 +46,58 @@ struct StepArgs {
   int32_t softplus;
 };
 
+// Engines of the forward scan.
+enum Engine {
+  kEngineLane = 0,  // one lane owns all N states of a channel (any supported N)
+  kEngineWg = 1,    // a workgroup owns 64 channels, its waves split the N states (N = 8, 16)
+};
+
+// Modes of the workgroup engine.
+enum WgMode {
+  kModeChained = 0,  // chunks of a channel block run in order, carried through the workspace
+  kModeAgg = 1,      // chunk end states from zero and chunk sums of dt (first pass of the split scan)
+  kModeOut = 2,      // outputs of every chunk from precomputed carry-ins (second pass)
+};
+
+// Arguments of the workgroup engine on top of the scan arguments.
+struct WgArgs {
+  ScanArgs s;
+  uint32_t* ticket;   // work counter of this launch (zeroed before the launch)
+  uint32_t* flags;    // chained mode: chunks finished per channel block (zeroed before the launch)
+  uint32_t* err;      // set nonzero if a wait ever exceeded its bound (never expected)
+  float* carry;       // chained mode: (chains, 64, N) state handed from chunk to chunk
+  int32_t chains;     // batch * blocks_per_row: independent (batch row, 64-channel block) pairs
+  int32_t blocks_per_row;
+  int32_t nitems;     // work items of this launch
+};
+
 // Execution plan of a forward scan, a pure function of the shape.
 struct ScanPlan {
+  int32_t engine;     // Engine
+  int32_t split;      // workgroup engine: 0 chained, 1 two passes (aggregates, carry, outputs)
+  int32_t waves;      // workgroup engine: waves per workgroup
   int32_t nchunks;    // L is cut into this many chunks of chunk_len tokens
   int64_t chunk_len;
-  int32_t block;      // threads per workgroup (64 channels per wave)
-  size_t ws_bytes;    // workspace the plan needs (0 when nchunks == 1)
+  int32_t block;      // lane engine: threads per workgroup (64 channels per wave)
+  int32_t grid;       // workgroup engine: persistent workgroups
+  size_t ws_ctrl;     // bytes of counters and flags at the start of the workspace
+  size_t ws_bytes;    // workspace the plan needs in total (0 when nothing is needed)
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N);
 
+// Workgroup engine (scan_wg.hip).
+hipError_t launch_scan_wg(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
+bool wg_supported(int64_t N);
+int wg_waves(int64_t N);
+int wg_tile(int64_t N);
+
 bool dstate_supported(int64_t N);
 
 // Enqueue the kernels of one scan / one decode step on `stream`.
-hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
+// Carry pass over (batch, chunk, D, N) chunk aggregates (both engines' split modes).
+hipError_t launch_chunk_carry(const ScanArgs& a, int N, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int io, int N, hipStream_t stream);
 
 }  // namespace s6

@@ -18,6 +18,8 @@
 // associative step h_in(g+1) = e^{A * sum dt_g} h_in(g) + b_g (the product of
 // the chunk's Abar is e^{A * sum dt} because A does not vary in time); the
 // output pass then reruns every chunk from its exact carry-in.
+#include <cstdlib>
+
 #include "s6_device.h"
 #include "s6_internal.h"
 
@@ -167,8 +169,24 @@ __global__ __launch_bounds__(256) void scan_output_kernel(ScanArgs a) {
 
 bool dstate_supported(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 
-ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
-  ScanPlan p;
+namespace {
+
+int64_t env_int(const char* name, int64_t dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !v[0]) return dflt;
+  char* end = nullptr;
+  long long x = std::strtoll(v, &end, 10);
+  return (end && *end == 0 && x > 0) ? (int64_t)x : dflt;
+}
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+constexpr int64_t kGridMax = 256;           // persistent workgroups: one per CU of an MI355X
+constexpr int64_t kChainedMinChains = 128;  // below this many channel blocks, long sequences use two passes
+
+ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  ScanPlan p{};
+  p.engine = kEngineLane;
   p.block = D >= 256 ? 256 : (int32_t)(((D + 63) / 64) * 64);
   if (p.block < 64) p.block = 64;
   // Waves of the unchunked scan; cut L until about two waves per SIMD
@@ -176,14 +194,68 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
   const int64_t waves = batch * ((D + 63) / 64);
   const int64_t target = 2048;
   int64_t g = waves > 0 ? (target + waves - 1) / waves : 1;
-  const int64_t gmax = L / 256 > 1 ? L / 256 : 1;
+  int64_t gmax = L / 256 > 1 ? L / 256 : 1;
+  if (gmax > 65535) gmax = 65535;
   if (g > gmax) g = gmax;
   if (g < 1) g = 1;
   p.chunk_len = L > 0 ? (L + g - 1) / g : 0;
   p.nchunks = (int32_t)(p.chunk_len > 0 ? (L + p.chunk_len - 1) / p.chunk_len : 1);
   if (p.nchunks < 1) p.nchunks = 1;
+  p.ws_ctrl = 0;
   p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) : 0;
   return p;
+}
+
+ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  ScanPlan p{};
+  p.engine = kEngineWg;
+  p.waves = wg_waves(N);
+  const int64_t T = wg_tile(N);
+  const int64_t chains = batch * ((D + 63) / 64);
+  const int64_t tiles = (L + T - 1) / T;
+  // A chunk's token rows, plus the up to four tiles the pipeline reads past its
+  // end, must span less than 2^31 bytes: buffer offsets are 32-bit and the
+  // out-of-range offset 2^31 must never wrap back into range.
+  int64_t cap = ((int64_t)0x7fffffff / (D * 4) - 4 * T) / T * T;
+  if (cap < T) cap = T;
+  if (chains >= kChainedMinChains || tiles < 32) {
+    // Chained chunks.  With more channel blocks than workgroups, chunks of
+    // about 512 tokens let the persistent grid balance the blocks.
+    p.split = 0;
+    int64_t chunk = L;
+    if (chains > kGridMax) chunk = env_int("MAMBA_MI355X_CHUNK", 512);
+    chunk = ((chunk + T - 1) / T) * T;
+    if (chunk > cap) chunk = cap;
+    if (chunk >= L) chunk = L;
+    p.chunk_len = chunk;
+    p.nchunks = (int32_t)((L + chunk - 1) / chunk);
+    p.grid = (int32_t)(chains < kGridMax ? chains : kGridMax);
+    p.ws_ctrl = round_up(256 + 4 * (size_t)chains, 256);
+    p.ws_bytes = p.ws_ctrl + (size_t)chains * 64 * N * sizeof(float);
+  } else {
+    // Two passes over independent chunks: about 1024 work items.
+    p.split = 1;
+    int64_t g = (1024 + chains - 1) / chains;
+    if (g > tiles / 4) g = tiles / 4;
+    if (g < 2) g = 2;
+    int64_t chunk = (L + g - 1) / g;
+    chunk = ((chunk + T - 1) / T) * T;
+    if (chunk > cap) chunk = cap;
+    p.chunk_len = chunk;
+    p.nchunks = (int32_t)((L + chunk - 1) / chunk);
+    p.grid = (int32_t)kGridMax;
+    p.ws_ctrl = 256;
+    p.ws_bytes = p.ws_ctrl + (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float);
+  }
+  return p;
+}
+
+}  // namespace
+
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0)
+    return plan_wg(batch, L, D, N);
+  return plan_lane(batch, L, D, N);
 }
 
 template <typename IO, int N>
@@ -198,6 +270,20 @@ static hipError_t launch_scan_t(const ScanArgs& a, const ScanPlan& p, hipStream_
   }
   hipLaunchKernelGGL((scan_output_kernel<IO, N>), grid_c, dim3(block), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_chunk_carry(const ScanArgs& a, int N, hipStream_t s) {
+  const int64_t lanes = a.batch * a.D * N;
+  const dim3 grid((unsigned)((lanes + 255) / 256));
+  switch (N) {
+    case 1: hipLaunchKernelGGL((scan_carry_kernel<1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((scan_carry_kernel<2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((scan_carry_kernel<4>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((scan_carry_kernel<8>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((scan_carry_kernel<16>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
 }
 
 template <typename IO>
@@ -218,14 +304,20 @@ __global__ __launch_bounds__(256) void scan_empty_kernel(float* last, const floa
   if (i < count) last[i] = h0 ? h0[i] : 0.0f;
 }
 
-hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, hipStream_t s) {
-  if (a.batch == 0 || a.D == 0) return hipSuccess;
-  if (a.L == 0) {
-    if (!a.last) return hipSuccess;
-    const int64_t count = a.batch * a.D * N;
-    hipLaunchKernelGGL(scan_empty_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, a.last, a.h0, count);
+hipError_t launch_scan(const ScanArgs& in, const ScanPlan& p, int io, int N, void* workspace, hipStream_t s) {
+  if (in.batch == 0 || in.D == 0) return hipSuccess;
+  if (in.L == 0) {
+    if (!in.last) return hipSuccess;
+    const int64_t count = in.batch * in.D * N;
+    hipLaunchKernelGGL(scan_empty_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, in.last, in.h0, count);
     return hipGetLastError();
   }
+  ScanArgs a = in;
+  a.chunk_len = p.chunk_len;
+  a.nchunks = p.nchunks;
+  if (p.engine == kEngineWg) return launch_scan_wg(a, p, io, N, workspace, s);
+  a.agg_h = static_cast<float*>(workspace);
+  a.agg_s = p.ws_bytes > 0 ? a.agg_h + (size_t)a.batch * p.nchunks * a.D * N : nullptr;
   return io == kIoBF16 ? launch_scan_io<uint16_t>(a, p, N, s) : launch_scan_io<float>(a, p, N, s);
 }
 

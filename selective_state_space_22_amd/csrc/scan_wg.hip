@@ -1,0 +1,456 @@
+// scan_wg.hip -- workgroup-cooperative forward selective scan on gfx950.
+//
+// A workgroup owns one (batch row, block of 64 channels) at a time: lane l of
+// every wave is channel block*64 + l, and the W waves split the N states of
+// those channels (S = N/W states per wave, kept in VGPRs).  Each token still
+// costs one v_exp_f32 per (channel, state), but the work per token is spread
+// over W waves, so a (batch*D)-sized problem fills W times more SIMDs than a
+// lane-owns-all-states mapping.
+//
+// Per 16-token tile (one LDS barrier per tile, LDS slots rotating):
+//   front   (token j handled by wave j % W): dt = softplus(raw + bias), its
+//           square, the input x and the gate z go to LDS; all threads stage
+//           B_t and C_t of the tile (shared by all channels: page section 3.2)
+//           into LDS.
+//   scan    every wave advances its S states over the tile's tokens
+//           (eq. (2) discretisation, eq. (3a) recurrence) and writes its partial
+//           readout sum_s C_t[s] h_t[s] (eq. (3b)) to LDS.
+//   epilogue (token j by wave j % W): y = sum of the W partials, then
+//           y + Dskip x, times SiLU(z), one store per (token, channel).
+// Global loads for tile k+2 are issued while tile k is computed; every access
+// goes through a bounds-checked buffer resource based at the chunk, so tails
+// need no branches (out-of-range reads return zero, stores are dropped).
+//
+// Sequence length is cut into chunks.  In the chained mode the chunks of a
+// channel block run in order on whichever workgroup takes them: a persistent
+// grid takes work items from a ticket counter in chunk-major order, waits
+// until the previous chunk of its channel block has published its end state,
+// continues from that state and publishes its own.  A ticket is only handed
+// to a running workgroup, and a chunk's predecessor always has a smaller
+// ticket, so every wait ends.  In the split mode (few channel blocks, long
+// sequences) the chunks run independently in two passes with a carry pass in
+// between (the associative composition of chunk aggregates).
+#include <cstdlib>
+
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+namespace {
+
+constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr int32_t kBufferDword3 = 0x00020000;  // raw (untyped) buffer access on the gfx9 family
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offset beyond every buffer: loads 0, stores dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
+}
+
+// One I/O element through a buffer resource (bounds-checked by the hardware).
+template <typename IO>
+struct BufIo;
+template <>
+struct BufIo<uint16_t> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw << 16); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+  }
+};
+template <>
+struct BufIo<float> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+  }
+};
+
+// Wait for every outstanding vector-memory access (the item's constants and
+// initial state), so that later waits only have to cover the tile prefetches.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <typename IO, int N, int W, int T, int MODE>
+struct WgScan {
+  static constexpr int S = N / W;                 // states per wave
+  static constexpr int TW = T / W;                // front-end / epilogue tokens per wave per tile
+  static constexpr int NT = 64 * W;               // threads
+  static constexpr int BCV = 2 * T * N / NT;      // B/C elements staged per thread per tile
+  static_assert(N % W == 0 && T % W == 0 && W % 2 == 0 && (2 * T * N) % NT == 0 && BCV >= 1 && N % BCV == 0,
+                "tile shape");
+  static constexpr bool kOut = MODE != kModeAgg;
+  static constexpr uint32_t kIo = sizeof(IO);
+
+  // Buffers of tile k: fr and bc in slot k % 3, yp in slot k % 2.  With one
+  // barrier per tile (between the scan and the epilogue of tile k) this is
+  // race-free: the front end of tile k+1 (start of iteration k) overwrites the
+  // slot last read by the epilogue of tile k-2, which every wave finished
+  // before the barrier of tile k-1; the scan of tile k+2 overwrites the yp slot
+  // of tile k after the barrier of tile k+1, which follows every wave's
+  // epilogue of tile k.
+  static constexpr int BCW = (2 * S + 3) / 4 * 4;  // bc row per (token, wave), padded to float4
+
+  struct Lds {
+    float4 fr[3][T][64];                         // (dt, dt^2, x, z) per (token, channel)
+    __attribute__((aligned(16))) float bc[3][T][W][BCW];  // per token and wave: B of its states, then C
+    float yp[kOut ? 2 : 1][T][W][64];            // partial readouts
+    float sdt[W][64];                            // split mode: partial sums of dt
+    int item[2];
+  };
+
+  struct Regs {  // raw prefetched global data of one tile
+    uint32_t dl[TW], uu[TW], zz[TW];
+    uint32_t bcv[BCV];
+  };
+
+  const WgArgs& A;
+  Lds& sm;
+  const int lane, w;
+  // current item
+  int64_t b, d, t0, t1;
+  bool dvalid;
+  uint32_t chan_off;  // byte offset of this lane's channel in a token row (out of range if d >= D)
+  __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_out, r_B, r_C;
+  float a2[S], ka[S], ah[S], h[S];
+  float bias, dskip;
+  float dsum, dcomp;  // compensated sum of dt (split mode, first pass)
+
+  // The wave index is made a scalar (readfirstlane) so that everything derived
+  // from it -- which states a wave owns, which of B/C it stages -- stays uniform.
+  __device__ WgScan(const WgArgs& a, Lds& s)
+      : A(a), sm(s), lane(threadIdx.x & 63), w(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {}
+
+  __device__ __forceinline__ int tile_valid(int k) const {
+    const int64_t tk = t0 + (int64_t)k * T;
+    const int64_t r = t1 - tk;
+    return r <= 0 ? 0 : (r >= T ? T : (int)r);
+  }
+
+  // Global loads of tile k.  Unconditional: rows past the chunk and lanes past D
+  // are out of the buffers' range and read as zero.
+  __device__ __forceinline__ void load(Regs& r, int k) const {
+    const uint32_t row = (uint32_t)(A.s.D * kIo);
+    const uint32_t base = chan_off + (uint32_t)(k * T + w) * row;  // one vector add per tile
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const uint32_t off = base + (uint32_t)(W * i) * row;
+      r.dl[i] = BufIo<IO>::load(r_dl, off);
+      r.uu[i] = BufIo<IO>::load(r_u, off);
+      if (kOut) r.zz[i] = BufIo<IO>::load(r_z, off);
+    }
+    // The first half of the waves stage B, the second half C (uniform per wave).
+    const __amdgpu_buffer_rsrc_t rbc = w < W / 2 ? r_B : r_C;
+#pragma unroll
+    for (int v = 0; v < BCV; ++v) {
+      const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;  // element of the tile's B (or C) block
+      r.bcv[v] = BufIo<IO>::load(rbc, (uint32_t)(k * T * N + e) * kIo);
+    }
+  }
+
+  // Front end of tile k into slot f3 of fr and bc.
+  __device__ __forceinline__ void front(const Regs& r, int k, int f3) {
+    const int nv = tile_valid(k);
+    const bool sp = A.s.softplus != 0;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int j = w + W * i;
+      const float x = BufIo<IO>::widen(r.uu[i]);
+      TokenFront f = make_front(BufIo<IO>::widen(r.dl[i]), bias, sp);
+      sm.fr[f3][j][lane] = make_float4(f.dt, f.dt2, x, kOut ? BufIo<IO>::widen(r.zz[i]) : 0.0f);
+      if (MODE == kModeAgg) {  // Kahan sum of dt over this wave's valid tokens
+        const float yk = (j < nv ? f.dt : 0.0f) - dcomp;
+        const float tk = dsum + yk;
+        dcomp = (tk - dsum) - yk;
+        dsum = tk;
+      }
+    }
+    const int c = w < W / 2 ? 0 : 1;
+#pragma unroll
+    for (int v = 0; v < BCV; ++v) {
+      const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;
+      const int j = e / N, n = e % N;
+      sm.bc[f3][j][n / S][c * S + n % S] = BufIo<IO>::widen(r.bcv[v]);
+    }
+  }
+
+  struct Tok {  // LDS operands of one token for this lane and wave
+    float4 fv;   // dt, dt^2, x, z
+    float bc[BCW];
+  };
+
+  __device__ __forceinline__ void read_tok(Tok& t, int f3, int j) const {
+    t.fv = sm.fr[f3][j][lane];
+#pragma unroll
+    for (int q = 0; q < BCW; q += 4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&sm.bc[f3][j][w][q]);
+      t.bc[q] = v4.x;
+      t.bc[q + 1] = v4.y;
+      t.bc[q + 2] = v4.z;
+      t.bc[q + 3] = v4.w;
+    }
+  }
+
+  // One token of the recurrence for this wave's S states (eq. (2), (3a)) and
+  // its partial readout sum_s C_t[s] h_t[s] (eq. (3b)).
+  __device__ __forceinline__ void step(const Tok& t, int y2, int j) {
+    float y = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float x2 = t.fv.x * a2[s];
+      const float abar = ex2(x2);
+      const float beta = input_weight(abar, x2, t.fv.x, t.fv.y, ka[s], ah[s]);
+      h[s] = __builtin_fmaf(abar, h[s], beta * (t.bc[s] * t.fv.z));
+      if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
+    }
+    if (kOut) sm.yp[y2][j][w][lane] = y;
+  }
+
+  // Recurrence over tile k from slot f3; partial readouts to yp slot y2.
+  // Full tiles are unrolled (constant LDS offsets) with the next token's
+  // operands read before the current token is computed.
+  __device__ __forceinline__ void scan(int k, int f3, int y2) {
+    const int nv = tile_valid(k);
+    if (nv == T) {
+      Tok t[2];
+      read_tok(t[0], f3, 0);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        if (j + 1 < T) read_tok(t[(j + 1) & 1], f3, j + 1);
+        step(t[j & 1], y2, j);
+      }
+    } else {
+      for (int j = 0; j < nv; ++j) {
+        Tok t;
+        read_tok(t, f3, j);
+        step(t, y2, j);
+      }
+    }
+  }
+
+  // Readout sum, skip, gate and store for this wave's tokens of tile k
+  // (rows past the chunk and lanes past D fall outside the output buffer).
+  __device__ __forceinline__ void epilogue(int k, int f3, int y2) {
+    if (!kOut) return;
+    const bool has_z = A.s.z != nullptr;
+    const uint32_t row = (uint32_t)(A.s.D * kIo);
+    const uint32_t base = chan_off + (uint32_t)(k * T + w) * row;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int j = w + W * i;
+      float y = sm.yp[y2][j][0][lane];
+#pragma unroll
+      for (int q = 1; q < W; ++q) y += sm.yp[y2][j][q][lane];
+      const float4 fv = sm.fr[f3][j][lane];
+      const float o = s6::epilogue(y, fv.z, dskip, has_z, fv.w);
+      BufIo<IO>::store(o, r_out, base + (uint32_t)(W * i) * row);
+    }
+  }
+
+  __device__ void run_item(int chain, int g) {
+    const int G = A.s.nchunks;
+    b = chain / A.blocks_per_row;
+    d = (int64_t)(chain % A.blocks_per_row) * 64 + lane;
+    dvalid = d < A.s.D;
+    t0 = (int64_t)g * A.s.chunk_len;
+    t1 = t0 + A.s.chunk_len < A.s.L ? t0 + A.s.chunk_len : A.s.L;
+    chan_off = dvalid ? (uint32_t)(d * kIo) : kOutOfRange;
+    {
+      const size_t row0 = ((size_t)b * A.s.L + t0);
+      const uint32_t span = (uint32_t)((t1 - t0) * A.s.D * kIo);
+      const uint32_t bspan = (uint32_t)((t1 - t0) * N * kIo);
+      r_u = make_rsrc(static_cast<const IO*>(A.s.u) + row0 * A.s.D, span);
+      r_dl = make_rsrc(static_cast<const IO*>(A.s.delta) + row0 * A.s.D, span);
+      r_z = make_rsrc(A.s.z ? static_cast<const IO*>(A.s.z) + row0 * A.s.D : static_cast<const IO*>(A.s.u),
+                      A.s.z ? span : 0u);
+      r_out = make_rsrc(static_cast<const IO*>(A.s.out) + row0 * A.s.D, kOut ? span : 0u);
+      r_B = make_rsrc(static_cast<const IO*>(A.s.B) + row0 * N, bspan);
+      r_C = make_rsrc(static_cast<const IO*>(A.s.C) + row0 * N, bspan);
+    }
+    const int nstate0 = w * S;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float a = dvalid ? A.s.A[d * N + nstate0 + s] : -1.0f;
+      a2[s] = a * kLog2e;
+      ka[s] = 1.0f / a;
+      ah[s] = 0.5f * a;
+    }
+    bias = (dvalid && A.s.bias) ? A.s.bias[d] : 0.0f;
+    dskip = (dvalid && A.s.dskip) ? A.s.dskip[d] : 0.0f;
+    dsum = 0.0f;
+    dcomp = 0.0f;
+
+    // state entering the chunk
+#pragma unroll
+    for (int s = 0; s < S; ++s) h[s] = 0.0f;
+    if (MODE == kModeChained) {
+      if (g == 0) {
+        if (A.s.h0 && dvalid) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) h[s] = A.s.h0[((size_t)b * A.s.D + d) * N + nstate0 + s];
+        }
+      } else {
+        if (threadIdx.x == 0) {
+          uint32_t spins = 0;
+          while (__hip_atomic_load(A.flags + chain, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)g) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kSpinLimit) {
+              __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+        // Thread 0's acquire load (which invalidates this CU's caches) is
+        // ordered before the other waves' reads of the carry by the barrier.
+        __syncthreads();
+        const float* src = A.carry + ((size_t)chain * 64 + lane) * N + nstate0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) h[s] = src[s];
+      }
+    } else if (MODE == kModeOut) {
+      if (dvalid) {
+        const float* src = A.s.agg_h + (((size_t)b * G + g) * A.s.D + d) * N + nstate0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) h[s] = src[s];
+      }
+    }
+    wait_vmem();
+
+    // tile pipeline: global loads one tile ahead, LDS slots rotating
+    const int ntiles = (int)((t1 - t0 + T - 1) / T);
+    Regs r;
+    load(r, 0);
+    front(r, 0, 0);
+    load(r, 1);
+    __syncthreads();
+    int f3 = 0;  // slot of tile k
+    for (int k = 0; k < ntiles; ++k) {
+      const int f3n = f3 == 2 ? 0 : f3 + 1;
+      front(r, k + 1, f3n);
+      load(r, k + 2);
+      scan(k, f3, k & 1);
+      __syncthreads();
+      epilogue(k, f3, k & 1);
+      f3 = f3n;
+    }
+
+    // publish the chunk's end
+    if (MODE == kModeChained) {
+      if (g < G - 1) {
+        float* dst = A.carry + ((size_t)chain * 64 + lane) * N + nstate0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) dst[s] = h[s];
+        // Every wave's carry stores complete (reach L2) before the barrier;
+        // thread 0's release store then writes the L2 back once for all of
+        // them before the flag becomes visible.
+        wait_vmem();
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_store(A.flags + chain, (uint32_t)(g + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (A.s.last && dvalid) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) A.s.last[((size_t)b * A.s.D + d) * N + nstate0 + s] = h[s];
+      }
+    } else if (MODE == kModeAgg) {
+      const size_t base = ((size_t)b * G + g) * A.s.D + d;
+      if (dvalid) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) A.s.agg_h[base * N + nstate0 + s] = h[s];
+      }
+      sm.sdt[w][lane] = dsum;
+      __syncthreads();
+      if (w == 0 && dvalid) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int q = 0; q < W; ++q) tot += sm.sdt[q][lane];
+        A.s.agg_s[base] = tot;
+      }
+    } else {  // kModeOut
+      if (g == G - 1 && A.s.last && dvalid) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) A.s.last[((size_t)b * A.s.D + d) * N + nstate0 + s] = h[s];
+      }
+    }
+  }
+};
+
+template <typename IO, int N, int W, int T, int MODE>
+__global__ __launch_bounds__(64 * W, 1) void scan_wg_kernel(WgArgs a) {
+  using K = WgScan<IO, N, W, T, MODE>;
+  __shared__ typename K::Lds sm;
+  K k(a, sm);
+  for (int round = 0;; ++round) {
+    if (threadIdx.x == 0) sm.item[round & 1] = (int)atomicAdd(a.ticket, 1u);
+    __syncthreads();
+    const int item = sm.item[round & 1];
+    if (item >= a.nitems) break;
+    k.run_item(item % a.chains, item / a.chains);
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <typename IO, int N, int W, int T>
+hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  WgArgs a;
+  a.s = s;
+  a.blocks_per_row = (int32_t)((s.D + 63) / 64);
+  a.chains = (int32_t)(s.batch * a.blocks_per_row);
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(base);
+  a.err = ctrl + 2;
+  a.flags = ctrl + 64;
+  const int64_t ctrl_words = (int64_t)(p.ws_ctrl / 4);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((ctrl_words + 255) / 256)), dim3(256), 0, st, ctrl,
+                     ctrl_words);
+  const dim3 block(64 * W);
+  if (!p.split) {
+    a.ticket = ctrl;
+    a.carry = reinterpret_cast<float*>(base + p.ws_ctrl);
+    a.nitems = a.chains * p.nchunks;
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained>), dim3(p.grid), block, 0, st, a);
+  } else {
+    a.s.agg_h = reinterpret_cast<float*>(base + p.ws_ctrl);
+    a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N;
+    a.carry = nullptr;
+    a.ticket = ctrl;
+    a.nitems = a.chains * (p.nchunks - 1);
+    const unsigned g1 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg>), dim3(g1), block, 0, st, a);
+    launch_chunk_carry(a.s, N, st);
+    a.ticket = ctrl + 1;
+    a.nitems = a.chains * p.nchunks;
+    const unsigned g2 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut>), dim3(g2), block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool wg_supported(int64_t N) { return N == 16 || N == 8; }
+int wg_waves(int64_t N) {
+  const char* v = std::getenv("MAMBA_MI355X_WG_WAVES");
+  if (N == 16 && v && v[0] == '4') return 4;
+  return N == 16 ? 8 : 4;
+}
+int wg_tile(int64_t) { return 16; }
+
+hipError_t launch_scan_wg(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
+  const bool bf = io == kIoBF16;
+  if (N == 16 && p.waves == 8)
+    return bf ? launch_wg_t<uint16_t, 16, 8, 16>(s, p, ws, st) : launch_wg_t<float, 16, 8, 16>(s, p, ws, st);
+  if (N == 16 && p.waves == 4)
+    return bf ? launch_wg_t<uint16_t, 16, 4, 16>(s, p, ws, st) : launch_wg_t<float, 16, 4, 16>(s, p, ws, st);
+  if (N == 8)
+    return bf ? launch_wg_t<uint16_t, 8, 4, 16>(s, p, ws, st) : launch_wg_t<float, 8, 4, 16>(s, p, ws, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace s6

@@ -53,12 +53,18 @@ def test_version_and_status_strings(lib):
 
 def test_workspace_size_is_a_pure_function_of_shape(lib):
     ws = binding.mamba_scan_fwd_workspace_size
-    # one-piece plans need no workspace
     assert ws(4, 4096, 5120, 16, 1) == ws(4, 4096, 5120, 16, 1)
-    assert ws(1, 256, 64, 16, 0) == 0
-    # the million-token plan cuts L: workspace holds (batch, chunks, D, N+1) floats
+    # the workgroup engine (N = 8, 16) keeps a work counter, per-block flags and the
+    # handed-over state: a few KB beyond the 64*N floats per channel block
+    chains = 4 * 5120 // 64
+    w = ws(4, 4096, 5120, 16, 1)
+    assert chains * 64 * 16 * 4 <= w <= chains * 64 * 16 * 4 + 4096 + 4 * chains
+    # the lane engine (other N) runs short sequences in one piece: no workspace
+    assert ws(1, 256, 64, 4, 0) == 0
+    # few channel blocks and a long sequence: two passes over chunks, the workspace
+    # holds the (batch, chunks, D, N+1) chunk aggregates after a 256-byte header
     w = ws(1, 1 << 20, 256, 16, 0)
-    assert w > 0 and w % (256 * 17 * 4) == 0
+    assert w > 256 and (w - 256) % (256 * 17 * 4) == 0
     # rejected shapes report 0
     assert ws(1, 16, 64, 3, 0) == 0
     assert ws(1, 16, 64, 16, 7) == 0

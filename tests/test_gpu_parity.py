@@ -158,18 +158,70 @@ EDGE = [
 ]
 
 
+ENGINES = ["default", "lane"]
+
+
+def _engine(monkeypatch, engine):
+    """The library picks its engine from the shape; MAMBA_MI355X_LANE_ENGINE=1 forces the
+    lane-per-channel engine so that both engines are covered on the same cases."""
+    if engine == "lane":
+        monkeypatch.setenv("MAMBA_MI355X_LANE_ENGINE", "1")
+    else:
+        monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
+
+
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("case", EDGE, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}_{i}" for i, c in enumerate(EDGE)])
-def test_edge_cases(case):
+def test_edge_cases(case, engine, monkeypatch):
     _need_gpu()
+    _engine(monkeypatch, engine)
     batch, L, D, N, io, kw = case
-    _announce(f"edge case {case}")
+    _announce(f"edge case {case} engine={engine}")
     inp = W.generate(batch, L, D, N, io, seed=500 + L + D + N, **kw)
-    check(inp, label=str(case))
+    check(inp, label=f"{case} {engine}")
 
 
-@pytest.mark.parametrize("chunked", [False, True])
-def test_initial_state(chunked):
+# Shapes that reach every mode of the workgroup engine (N = 16 and 8):
+#   chained, one chunk per channel block (<= 256 channel blocks);
+#   chained, several chunks per block handed between workgroups (> 256 blocks);
+#   split into two passes (few blocks, long sequence).
+WG_CASES = [
+    (3, 700, 4096, 16, "bf16"),    # 192 blocks, chained, one chunk
+    (5, 1100, 4096, 16, "bf16"),   # 320 blocks, chained, 3 chunks (last one ragged)
+    (3, 1500, 6000, 16, "f32"),    # 282 blocks with a ragged channel tail, 3 chunks
+    (1, 4096, 64, 16, "f32"),      # 1 block, split into 64 chunks
+    (2, 3000, 200, 16, "bf16"),    # 8 blocks with a ragged tail, split
+    (3, 900, 4096, 8, "f32"),      # N = 8: 4 waves per workgroup
+    (1, 5000, 128, 8, "bf16"),     # N = 8, split
+]
+
+
+@pytest.mark.parametrize("case", WG_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in WG_CASES])
+def test_workgroup_engine_modes(case, monkeypatch):
     _need_gpu()
+    _engine(monkeypatch, "default")
+    batch, L, D, N, io = case
+    _announce(f"workgroup engine case {case}")
+    inp = W.generate(batch, L, D, N, io, seed=900 + L + D + N)
+    eo, el = check(inp, label=str(case))
+    print(f"{case}: out err {eo:.3e} last err {el:.3e}")
+
+
+@pytest.mark.parametrize("case", [(5, 1100, 4096, 16, "f32"), (1, 4096, 64, 16, "f32")], ids=["chained", "split"])
+def test_workgroup_engine_initial_state(case, monkeypatch):
+    _need_gpu()
+    _engine(monkeypatch, "default")
+    batch, L, D, N, io = case
+    inp = W.generate(batch, L, D, N, io, seed=77)
+    h0 = np.random.default_rng(78).standard_normal((batch, D, N)).astype(np.float32)
+    check(inp, h0=h0, label=f"h0 {case}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("chunked", [False, True])
+def test_initial_state(chunked, engine, monkeypatch):
+    _need_gpu()
+    _engine(monkeypatch, engine)
     L = 4096 if chunked else 200
     inp = W.generate(2, L, 64, 16, "f32", seed=71)
     h0 = np.random.default_rng(72).standard_normal((2, 64, 16)).astype(np.float32)
@@ -206,9 +258,11 @@ def _run(inp, **kw):
     return gpu_scan(inp, **kw)
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("L", [300, 3000])
-def test_causality_bit_exact(L):
+def test_causality_bit_exact(L, engine, monkeypatch):
     _need_gpu()
+    _engine(monkeypatch, engine)
     inp = W.generate(2, L, 128, 16, "f32", seed=80)
     o1, _ = _run(inp)
     t0 = L // 2 + 3
@@ -222,9 +276,11 @@ def test_causality_bit_exact(L):
         assert not np.array_equal(o1[:, t0:], o2[:, t0:]), name
 
 
-def test_hold_is_exact():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_hold_is_exact(engine, monkeypatch):
     """dt = 0 (no softplus, raw = -bias) keeps the state bit-exactly."""
     _need_gpu()
+    _engine(monkeypatch, engine)
     inp = W.generate(2, 400, 64, 16, "f32", seed=81)
     inp.delta = np.broadcast_to(-inp.delta_bias, inp.u.shape).astype(np.float32).copy()
     h0 = np.random.default_rng(82).standard_normal((2, 64, 16)).astype(np.float32)
@@ -234,9 +290,11 @@ def test_hold_is_exact():
     assert parity_error(o, ro) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("L", [200, 3000])
-def test_reset_forgets_the_prefix_exactly(L):
+def test_reset_forgets_the_prefix_exactly(L, engine, monkeypatch):
     _need_gpu()
+    _engine(monkeypatch, engine)
     inp = W.generate(1, L, 64, 16, "f32", seed=83)
     tr = L // 2 + 11
     inp.delta[:, tr] = 60.0  # dt*A <= -60 * log2(e): Abar underflows to exactly 0
@@ -249,9 +307,11 @@ def test_reset_forgets_the_prefix_exactly(L):
     assert np.array_equal(o1[:, tr:], o2[:, tr:]) and np.array_equal(l1, l2)
 
 
-def test_run_to_run_determinism():
+@pytest.mark.parametrize("shape", [(2, 3000, 256), (5, 1100, 4096)], ids=["split", "chained"])
+def test_run_to_run_determinism(shape):
+    """Also a race smoke test: the chained mode hands states between workgroups."""
     _need_gpu()
-    inp = W.generate(2, 3000, 256, 16, "bf16", seed=85)
+    inp = W.generate(*shape, 16, "bf16", seed=85)
     d = to_device(inp)
     a = gpu_scan(inp, dev_inputs=d)
     b = gpu_scan(inp, dev_inputs=d)
