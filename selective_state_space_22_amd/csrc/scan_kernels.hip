@@ -220,10 +220,10 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
   if (cap < T) cap = T;
   if (chains >= kChainedMinChains || tiles < 32) {
     // Chained chunks.  With more channel blocks than workgroups, chunks of
-    // about 512 tokens let the persistent grid balance the blocks.
+    // about 1024 tokens let the persistent grid balance the blocks.
     p.split = 0;
     int64_t chunk = L;
-    if (chains > kGridMax) chunk = env_int("MAMBA_MI355X_CHUNK", 512);
+    if (chains > kGridMax) chunk = env_int("MAMBA_MI355X_CHUNK", 1024);
     chunk = ((chunk + T - 1) / T) * T;
     if (chunk > cap) chunk = cap;
     if (chunk >= L) chunk = L;

@@ -385,7 +385,7 @@ __global__ __launch_bounds__(64 * W, 1) void scan_wg_kernel(WgArgs a) {
   for (int round = 0;; ++round) {
     if (threadIdx.x == 0) sm.item[round & 1] = (int)atomicAdd(a.ticket, 1u);
     __syncthreads();
-    const int item = sm.item[round & 1];
+    const int item = __builtin_amdgcn_readfirstlane(sm.item[round & 1]);
     if (item >= a.nitems) break;
     k.run_item(item % a.chains, item / a.chains);
   }
