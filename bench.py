@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--workload", default="mamba3b_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -146,6 +148,22 @@ def main():
         units = w.elements
         bytes_per_step = algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, io_bytes)
 
+    use_graph = args.graph == "on" or (args.graph == "auto" and decode)
+    if use_graph:
+        eager_step = step
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            eager_step()  # warm up on a side stream before capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+
+        def step():
+            graph.replay()
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -195,7 +213,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "state_dtype": "f32",
-                   "flush_infinity_cache": bool(args.flush), "parallelism": "single-gpu"},
+                   "flush_infinity_cache": bool(args.flush), "hip_graph": bool(use_graph),
+                   "parallelism": "single-gpu"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": bytes_per_step,

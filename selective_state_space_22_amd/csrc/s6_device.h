@@ -69,7 +69,7 @@ struct ChanConst {
     for (int n = 0; n < N; ++n) {
       float a = A_row[n];
       a2[n] = a * kLog2e;
-      ka[n] = 1.0f / a;  // IEEE division; inf for A_n = 0, never selected (see token_step)
+      ka[n] = rcp(a);  // v_rcp_f32 (<1 ulp); inf for A_n = 0, never selected (see input_weight)
       ah[n] = 0.5f * a;
     }
   }

@@ -323,34 +323,68 @@ hipError_t launch_scan(const ScanArgs& in, const ScanPlan& p, int io, int N, voi
 
 // ----------------------------------------------------------------- decode
 
-// One token for every (batch, channel): lane = (b, d), state read and written in place.
+// One token for every (batch, channel): lane = channel d of batch row
+// blockIdx.y, all N states read and written in place as float4.  B_t and C_t
+// of the row are shared by the row's channels (page section 3.2): they are read
+// once per wave through the scalar cache (whole dwords through the constant
+// address space: the kernel never writes them), A as float4.
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.batch * a.D) return;
-  const int64_t d = idx % a.D;
-  const int64_t b = idx / a.D;
-  const IO* __restrict__ Bp = static_cast<const IO*>(a.B) + b * N;
-  const IO* __restrict__ Cp = static_cast<const IO*>(a.C) + b * N;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y;
   float Bt[N], Ct[N], h[N];
+  if constexpr (sizeof(IO) == 2 && N % 2 == 0) {
+    using CW = __attribute__((address_space(4))) const uint32_t;
+    const CW* Bw = (const CW*)(static_cast<const uint32_t*>(a.B)) + b * (N / 2);
+    const CW* Cw = (const CW*)(static_cast<const uint32_t*>(a.C)) + b * (N / 2);
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    Bt[n] = load_io(Bp, n);
-    Ct[n] = load_io(Cp, n);
+    for (int q = 0; q < N / 2; ++q) {
+      const uint32_t wb = Bw[q], wc = Cw[q];
+      Bt[2 * q] = bf16_lo(wb);
+      Bt[2 * q + 1] = bf16_hi(wb);
+      Ct[2 * q] = bf16_lo(wc);
+      Ct[2 * q + 1] = bf16_hi(wc);
+    }
+  } else if constexpr (sizeof(IO) == 4) {
+    using CF = __attribute__((address_space(4))) const float;
+    const CF* Bf = (const CF*)(static_cast<const float*>(a.B)) + b * N;
+    const CF* Cf = (const CF*)(static_cast<const float*>(a.C)) + b * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      Bt[n] = Bf[n];
+      Ct[n] = Cf[n];
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      Bt[n] = load_io(static_cast<const IO*>(a.B) + b * N, n);
+      Ct[n] = load_io(static_cast<const IO*>(a.C) + b * N, n);
+    }
   }
+  if (d >= a.D) return;
+  const int64_t idx = b * a.D + d;
   float* __restrict__ st = a.state + (size_t)idx * N;
+  ChanConst<N> cc;
   if constexpr (N % 4 == 0) {
+    float av[N];
 #pragma unroll
     for (int j = 0; j < N / 4; ++j) {
-      float4 v = reinterpret_cast<const float4*>(st)[j];
+      const float4 v = reinterpret_cast<const float4*>(st)[j];
       h[4 * j] = v.x; h[4 * j + 1] = v.y; h[4 * j + 2] = v.z; h[4 * j + 3] = v.w;
+      const float4 q = reinterpret_cast<const float4*>(a.A + d * N)[j];
+      av[4 * j] = q.x; av[4 * j + 1] = q.y; av[4 * j + 2] = q.z; av[4 * j + 3] = q.w;
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      cc.a2[n] = av[n] * kLog2e;
+      cc.ka[n] = rcp(av[n]);
+      cc.ah[n] = 0.5f * av[n];
     }
   } else {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = st[n];
+    cc.load(a.A + d * N);
   }
-  ChanConst<N> cc;
-  cc.load(a.A + d * N);
   const float x = load_io(static_cast<const IO*>(a.u), idx);
   TokenFront f = make_front(load_io(static_cast<const IO*>(a.delta), idx), a.bias ? a.bias[d] : 0.0f, a.softplus != 0);
   float y = token_step<N>(cc, f, x, Bt, Ct, h);
@@ -369,8 +403,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
 
 template <typename IO>
 static hipError_t launch_step_io(const StepArgs& a, int N, hipStream_t s) {
-  const int64_t lanes = a.batch * a.D;
-  const dim3 grid((unsigned)((lanes + 255) / 256));
+  const dim3 grid((unsigned)((a.D + 255) / 256), (unsigned)a.batch);
   switch (N) {
     case 1: hipLaunchKernelGGL((state_update_kernel<IO, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((state_update_kernel<IO, 2>), grid, dim3(256), 0, s, a); break;

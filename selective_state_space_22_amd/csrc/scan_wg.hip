@@ -85,13 +85,13 @@ struct WgScan {
   static constexpr bool kOut = MODE != kModeAgg;
   static constexpr uint32_t kIo = sizeof(IO);
 
-  // Buffers of tile k: fr and bc in slot k % 3, yp in slot k % 2.  With one
-  // barrier per tile (between the scan and the epilogue of tile k) this is
-  // race-free: the front end of tile k+1 (start of iteration k) overwrites the
-  // slot last read by the epilogue of tile k-2, which every wave finished
-  // before the barrier of tile k-1; the scan of tile k+2 overwrites the yp slot
-  // of tile k after the barrier of tile k+1, which follows every wave's
-  // epilogue of tile k.
+  // Buffers of tile k: fr and bc in slot k % 3, yp in slot k % 2.  Iteration
+  // k runs front(k+1), epilogue(k-1), scan(k), then the tile's one barrier.
+  // Race-free: front(k+1) overwrites the fr/bc slot of tile k-2, whose last
+  // readers (scan(k-2), epilogue(k-2)) finished before the barrier of
+  // iteration k-1; scan(k) overwrites the yp slot of tile k-2, last read by
+  // epilogue(k-2) before that same barrier; epilogue(k-1) reads what scan(k-1)
+  // wrote before the barrier of iteration k-1.
   static constexpr int BCW = (2 * S + 3) / 4 * 4;  // bc row per (token, wave), padded to float4
 
   struct Lds {
@@ -275,7 +275,7 @@ struct WgScan {
     for (int s = 0; s < S; ++s) {
       const float a = dvalid ? A.s.A[d * N + nstate0 + s] : -1.0f;
       a2[s] = a * kLog2e;
-      ka[s] = 1.0f / a;
+      ka[s] = rcp(a);
       ah[s] = 0.5f * a;
     }
     bias = (dvalid && A.s.bias) ? A.s.bias[d] : 0.0f;
@@ -326,16 +326,23 @@ struct WgScan {
     front(r, 0, 0);
     load(r, 1);
     __syncthreads();
-    int f3 = 0;  // slot of tile k
+    // The epilogue of tile k-1 runs in the same barrier interval as the scan
+    // of tile k: it reads the yp slot of k-1 (next written by the scan of k+1,
+    // after this interval's barrier) and the fr slot of k-1 (next written by
+    // the front end of k+2, also after it).
+    int f3 = 0;   // slot of tile k
+    int f3p = 2;  // slot of tile k - 1
     for (int k = 0; k < ntiles; ++k) {
       const int f3n = f3 == 2 ? 0 : f3 + 1;
       front(r, k + 1, f3n);
       load(r, k + 2);
+      if (k > 0) epilogue(k - 1, f3p, (k - 1) & 1);
       scan(k, f3, k & 1);
       __syncthreads();
-      epilogue(k, f3, k & 1);
+      f3p = f3;
       f3 = f3n;
     }
+    if (ntiles > 0) epilogue(ntiles - 1, f3p, (ntiles - 1) & 1);
 
     // publish the chunk's end
     if (MODE == kModeChained) {

@@ -1,0 +1,103 @@
+"""The C-ABI calls captured in a HIP graph (through torch.cuda.CUDAGraph): each
+replay, with eager work and synchronisation in between, must reproduce the
+eager result bit for bit.  The scan's work counters are cleared by a small
+fill kernel (no memset node), which is what these replays exercise."""
+import numpy as np
+import pytest
+
+from gpu_util import to_device
+from selective_state_space_22_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("shape", [(5, 1100, 4096, 16, "bf16"), (1, 4096, 64, 16, "f32"), (1, 300, 64, 4, "f32")],
+                         ids=["chained", "split", "lane"])
+def test_scan_graph_replays_match_eager(shape):
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+
+    batch, L, D, N, io = shape
+    print(f"\n[gpu-test] graph replay of mamba_scan_fwd {shape}", flush=True)
+    inp = W.generate(batch, L, D, N, io, seed=123)
+    d = to_device(inp)
+    out = torch.empty_like(d["u"])
+    last = torch.empty((batch, D, N), dtype=torch.float32, device="cuda")
+    ws_bytes = binding.mamba_scan_fwd_workspace_size(batch, L, D, N, 1 if io == "bf16" else 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.mamba_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["delta_bias"], d["Dskip"], d["z"], True,
+                               None, out=out, last_state=last, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_last = out.clone(), last.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm the stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        last.fill_(float("nan"))
+        ws.fill_(rep * 37 % 256)  # scratch contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {rep}: out differs"
+        assert torch.equal(last, ref_last), f"replay {rep}: last_state differs"
+        _ = (d["u"].float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_decode_graph_replays_match_eager():
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_state_update
+
+    print("\n[gpu-test] graph replay of 16 decode steps", flush=True)
+    inp = W.generate(8, 16, 640, 16, "bf16", seed=321)
+    d = to_device(inp)
+    steps = [{k: d[k][:, t].contiguous() for k in ("u", "delta", "B", "C", "z")} for t in range(16)]
+    state = torch.zeros((8, 640, 16), dtype=torch.float32, device="cuda")
+    outs = [torch.empty_like(steps[0]["u"]) for _ in range(16)]
+
+    def run():
+        for t in range(16):
+            st = steps[t]
+            mamba_state_update(state, st["u"], st["delta"], d["A"], st["B"], st["C"], d["delta_bias"], d["Dskip"],
+                               st["z"], True, out=outs[t])
+
+    run()
+    torch.cuda.synchronize()
+    ref_outs = [o.clone() for o in outs]
+    ref_state = state.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        state.zero_()
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        state.zero_()
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref_outs)), f"replay {rep}: outputs differ"
+        assert torch.equal(state, ref_state), f"replay {rep}: state differs"
+        _ = float(np.asarray(state[0, 0].cpu()).sum())
