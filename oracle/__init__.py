@@ -8,7 +8,9 @@ Two independent implementations of the same definition live here:
   * ``scan`` / ``step``: the C oracle ``s6_oracle.c`` (fp64, libm, OpenMP over
     (batch, channel)), called through ctypes;
   * ``scan_numpy``: a numpy fp64 twin vectorised over (batch, channel, state)
-    with a Python loop over tokens, used to cross-check the C code.
+    with a Python loop over tokens, used to cross-check the C code;
+  * ``scan_bwd``: the C oracle's backward, the derivative of the same
+    definition, pinned against central finite differences of ``scan``.
 Both follow "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
 section 2.1 eq. (2) (ZOH), eq. (3a)/(3b) (recurrence and readout),
 section 3.2 (selection: per-token dt through softplus, B/C shared by channels)
@@ -53,6 +55,8 @@ def _load():
         lib.s6_oracle_scan.restype = ctypes.c_int
         lib.s6_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_int]
         lib.s6_oracle_step.restype = ctypes.c_int
+        lib.s6_oracle_scan_bwd.argtypes = [I64, I64, I64, I64] + [P] * 8 + [ctypes.c_int] + [P] * 12 + [ctypes.c_int]
+        lib.s6_oracle_scan_bwd.restype = ctypes.c_int
         lib.s6_oracle_max_threads.argtypes = []
         lib.s6_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -109,6 +113,34 @@ def step(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus
     if rc != 0:
         raise RuntimeError(f"s6_oracle_step failed with {rc}")
     return out, st
+
+
+def scan_bwd(u, delta, A, B, C, dout, delta_bias=None, Dskip=None, z=None, softplus=True, h0=None, dlast=None,
+             nthreads: int | None = None):
+    """fp64 gradients of sum(dout*out) + sum(dlast*last_state).
+
+    Returns a dict with du, ddelta, dA, dB, dC and, when the matching input is
+    given, dDskip, dz, dbias, dh0."""
+    u, delta, A, B, C, dout = (_f64(x) for x in (u, delta, A, B, C, dout))
+    delta_bias, Dskip, z, h0, dlast = (_f64(x) for x in (delta_bias, Dskip, z, h0, dlast))
+    batch, L, D = u.shape
+    N = A.shape[1]
+    assert dout.shape == u.shape and (dlast is None or dlast.shape == (batch, D, N))
+    g = {"du": np.empty((batch, L, D)), "ddelta": np.empty((batch, L, D)), "dA": np.empty((D, N)),
+         "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N))}
+    g["dDskip"] = np.empty(D) if Dskip is not None else None
+    g["dz"] = np.empty((batch, L, D)) if z is not None else None
+    g["dbias"] = np.empty(D) if delta_bias is not None else None
+    g["dh0"] = np.empty((batch, D, N)) if h0 is not None else None
+    nt = nthreads if nthreads else max_threads()
+    rc = _load().s6_oracle_scan_bwd(batch, L, D, N, _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B),
+                                    _ptr(C), _ptr(Dskip), _ptr(z), int(bool(softplus)), _ptr(h0), _ptr(dout),
+                                    _ptr(dlast), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                    _ptr(g["dC"]), _ptr(g["dDskip"]), _ptr(g["dz"]), _ptr(g["dbias"]),
+                                    _ptr(g["dh0"]), nt)
+    if rc != 0:
+        raise RuntimeError(f"s6_oracle_scan_bwd failed with {rc}")
+    return {k: v for k, v in g.items() if v is not None}
 
 
 def scan_inputs(inp, h0=None, nthreads=None, softplus=None):

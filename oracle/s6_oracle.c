@@ -135,3 +135,130 @@ int s6_oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of s6_oracle_scan: gradients of the scalar
+ *     sum(dout * out) + sum(dlast * last_state)
+ * with respect to every input, by differentiating the forward definition
+ * above step by step (the backward pass itself is not on the page; it is
+ * the derivative of eq. (2), (3a), (3b), the softplus front end and the SiLU
+ * gate).  For one channel, with x = dt*A_n, a = e^x, beta = (a - 1)/A_n:
+ *     d a / d dt    = A_n a            d a / d A_n    = dt a
+ *     d beta / d dt = a                d beta / d A_n = dt^2 psi(x),
+ *     psi(x) = (x e^x - e^x + 1) / x^2  (psi(0) = 1/2)
+ * and the state gradient runs backwards: g_{t-1} = a_t g_t + dy_{t-1} C_{t-1}.
+ * The forward states are recomputed and kept per channel (plain, slow).
+ * Outputs (all overwritten; nullable ones are skipped when NULL):
+ *   du, ddelta, dz (nullable) : (batch, L, D)
+ *   dB, dC : (batch, L, N)      dA : (D, N)
+ *   dDskip, dbias (nullable) : (D)      dh0 (nullable) : (batch, D, N)
+ * dlast (nullable) is the gradient arriving at last_state.
+ * ------------------------------------------------------------------------ */
+static double psi_fn(double x) {
+    if (fabs(x) < 1e-3) /* series of (x e^x - e^x + 1)/x^2 */
+        return 0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x * (1.0 / 144.0))));
+    return (x * exp(x) - expm1(x)) / (x * x);
+}
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int s6_oracle_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N,
+                       const double* u, const double* delta, const double* delta_bias,
+                       const double* A, const double* B, const double* C,
+                       const double* Dskip, const double* z, int softplus_flag,
+                       const double* h0, const double* dout, const double* dlast,
+                       double* du, double* ddelta, double* dA, double* dB, double* dC,
+                       double* dDskip, double* dz, double* dbias, double* dh0, int nthreads) {
+    if (batch < 0 || L < 0 || D < 0 || N <= 0 || !A || !dA || !dout || !du || !ddelta || !dB || !dC) return 1;
+    if (nthreads <= 0) nthreads = 1;
+    for (int64_t i = 0; i < D * N; ++i) dA[i] = 0.0;
+    if (dDskip) for (int64_t i = 0; i < D; ++i) dDskip[i] = 0.0;
+    if (dbias) for (int64_t i = 0; i < D; ++i) dbias[i] = 0.0;
+    for (int64_t i = 0; i < batch * L * N; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+    int bad = 0;
+    /* channels in parallel; the reductions over channels (dB, dC) and over
+       (batch, token) (dA, dDskip, dbias) are accumulated per thread and added
+       under a critical section in channel order per thread */
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+    {
+        double* hs = (double*)malloc((size_t)(L + 1) * N * sizeof(double)); /* h_{-1..L-1} */
+        double* g = (double*)malloc((size_t)N * sizeof(double));
+        double* dA_loc = (double*)calloc((size_t)D * N, sizeof(double));
+        double* dD_loc = (double*)calloc((size_t)D, sizeof(double));
+        double* db_loc = (double*)calloc((size_t)D, sizeof(double));
+        double* dB_loc = (double*)calloc((size_t)batch * L * N, sizeof(double));
+        double* dC_loc = (double*)calloc((size_t)batch * L * N, sizeof(double));
+        if (!hs || !g || !dA_loc || !dD_loc || !db_loc || !dB_loc || !dC_loc) bad |= 1;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t unit = 0; unit < batch * D; ++unit) {
+            if (bad) continue;
+            int64_t b = unit / D, d = unit % D;
+            const double* Ar = A + d * N;
+            /* forward, keeping every state: row k of hs is h_{k-1} */
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t i = (b * L + t) * D + d;
+                double dt = token_dt(delta[i], delta_bias, d, softplus_flag);
+                for (int64_t n = 0; n < N; ++n) hs[(t + 1) * N + n] = hs[t * N + n];
+                (void)s6_token(N, dt, u[i], Ar, B + (b * L + t) * N, C + (b * L + t) * N, hs + (t + 1) * N);
+            }
+            /* backward */
+            for (int64_t n = 0; n < N; ++n) g[n] = dlast ? dlast[(b * D + d) * N + n] : 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                int64_t i = (b * L + t) * D + d;
+                const double* Bt = B + (b * L + t) * N;
+                const double* Ct = C + (b * L + t) * N;
+                const double* h_t = hs + (t + 1) * N;
+                const double* h_p = hs + t * N;
+                double v = delta[i] + (delta_bias ? delta_bias[d] : 0.0);
+                double dt = softplus_flag ? softplus_exact(v) : v;
+                double x = u[i];
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) y += Ct[n] * h_t[n];
+                double o = y + (Dskip ? Dskip[d] * x : 0.0);
+                double dy;
+                if (z) {
+                    double s = sigmoid(z[i]);
+                    if (dz) dz[i] = dout[i] * o * (s + z[i] * s * (1.0 - s));
+                    dy = dout[i] * z[i] * s;
+                } else {
+                    dy = dout[i];
+                }
+                double dx = Dskip ? Dskip[d] * dy : 0.0;
+                if (Dskip) dD_loc[d] += dy * x;
+                double ddt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    double xa = dt * Ar[n];
+                    double a = exp(xa);
+                    double phi = (xa == 0.0) ? 1.0 : expm1(xa) / xa;
+                    double beta = phi * dt;
+                    g[n] += dy * Ct[n];                 /* dL/dh_t */
+                    dC_loc[(b * L + t) * N + n] += dy * h_t[n];
+                    double da = g[n] * h_p[n];
+                    double dbeta = g[n] * Bt[n] * x;
+                    dB_loc[(b * L + t) * N + n] += g[n] * beta * x;
+                    dx += g[n] * beta * Bt[n];
+                    ddt += da * Ar[n] * a + dbeta * a;
+                    dA_loc[d * N + n] += da * dt * a + dbeta * dt * dt * psi_fn(xa);
+                    g[n] *= a;                          /* dL/dh_{t-1} from h_t */
+                }
+                du[i] = dx;
+                double dv = softplus_flag ? ddt * sigmoid(v) : ddt;
+                ddelta[i] = dv;
+                db_loc[d] += dv;
+            }
+            if (dh0) for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = g[n];
+        }
+#pragma omp critical
+        {
+            if (!bad) {
+                for (int64_t k = 0; k < D * N; ++k) dA[k] += dA_loc[k];
+                if (dDskip) for (int64_t k = 0; k < D; ++k) dDskip[k] += dD_loc[k];
+                if (dbias) for (int64_t k = 0; k < D; ++k) dbias[k] += db_loc[k];
+                for (int64_t k = 0; k < batch * L * N; ++k) { dB[k] += dB_loc[k]; dC[k] += dC_loc[k]; }
+            }
+        }
+        free(hs); free(g); free(dA_loc); free(dD_loc); free(db_loc); free(dB_loc); free(dC_loc);
+    }
+    return bad ? 2 : 0;
+}
