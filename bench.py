@@ -75,6 +75,50 @@ def cpu_baseline(inp, name):
             "sample": f"{what}; {elems} elements in {dt:.2f} s wall (fp64, OpenMP over (batch, channel))"}
 
 
+def source_sha256():
+    """Hash of the HIP sources: counter readings taken on other sources do not apply."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_22_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed PMC readings, or None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_sha256():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else int(w["bytes"])
+
+
+def calibrate_copy(torch, dev, mib, steps):
+    """A plain copy of known size: each launch reads and writes exactly mib MiB."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": steps + 1,
+                      "ms_per_copy": ms, "gbps": 8 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +129,8 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -103,6 +149,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
+        return
     w = W.WORKLOADS[args.workload]
     inp = W.generate_workload(args.workload)
     tdt = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -190,12 +239,15 @@ def main():
     gbps = bytes_per_step / (ms * 1e-3) / 1e9
     flops = units * FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
     tflops = flops / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload)
     if decode:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": bytes_per_step // L}
     else:
         roof = {"bound": "alu", "achieved": round(tflops, 2), "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / VALU_FP32_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(tflops / VALU_FP32_PEAK_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": bytes_per_step,
                 "note": "fp32 VALU without packed-fp32 instructions; frac vs the packed 157.3 TFLOP/s "
                         f"figure: {tflops / VALU_FP32_PACKED_TFLOPS:.4f}"}
     rec = {
