@@ -29,6 +29,9 @@ VALU_FP32_PACKED_TFLOPS = 157.3  # published fp32 vector peak (packed fp32, not 
 # Algorithmic fp32 operations (FMA = 2, other ops and transcendentals = 1):
 FLOPS_PER_ELEMENT = 9.0          # per (b, l, d, n): dt*A, exp, input weight, *B, *x, h FMA, readout FMA
 FLOPS_PER_TOKEN_CHANNEL = 15.0   # per (b, l, d): bias add, softplus (6), skip FMA, SiLU (5), gate mul
+# Backward, per (b, l, d, n) on top of the recomputed forward: gradient recurrence FMA, dC and dB products,
+# du FMA, d(beta) and d(Abar) products, ddt FMAs, d beta/d A (series or difference), two dA FMAs, state-gradient decay
+BWD_FLOPS_PER_ELEMENT = 22.0
 
 
 def algorithmic_bytes(batch, L, D, N, io_bytes, decode=False):
@@ -46,7 +49,7 @@ def metric_name():
         return "selective-scan fwd elements(B*L*D*N)/s + achieved HBM GB/s, Mamba-3B layer"
 
 
-def cpu_baseline(inp, name):
+def cpu_baseline(inp, name, which="fwd"):
     """The fp64 oracle on a bounded sample of the same workload, timed on the host cores."""
     import numpy as np
 
@@ -67,9 +70,22 @@ def cpu_baseline(inp, name):
     args = [np.ascontiguousarray(x, np.float64) if x is not None else None
             for x in (sub.u, sub.delta, sub.A, sub.B, sub.C, sub.delta_bias, sub.Dskip, sub.z)]
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.scan(*args, softplus=True, nthreads=threads)
-    dt = time.perf_counter() - t0
+    if which == "bwd":
+        if name != "million_tokens":  # one batch row: the backward oracle is ~3x the forward's work
+            sub = W.channel_subset(inp, [0], np.arange(inp.dim))
+            what = f"batch row 0 of {inp.batch}, all channels and tokens"
+            args = [np.ascontiguousarray(x, np.float64) if x is not None else None
+                    for x in (sub.u, sub.delta, sub.A, sub.B, sub.C, sub.delta_bias, sub.Dskip, sub.z)]
+        gi = W.grad_inputs(sub.batch, sub.seqlen, sub.dim, sub.dstate, "f32", seed=1)
+        t0 = time.perf_counter()
+        oracle.scan_bwd(args[0], args[1], args[2], args[3], args[4], gi.dout, args[5], args[6], args[7],
+                        softplus=True, dlast=gi.dlast, nthreads=threads)
+        dt = time.perf_counter() - t0
+        what += " (backward)"
+    else:
+        t0 = time.perf_counter()
+        oracle.scan(*args, softplus=True, nthreads=threads)
+        dt = time.perf_counter() - t0
     elems = sub.batch * sub.seqlen * sub.dim * sub.dstate
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{what}; {elems} elements in {dt:.2f} s wall (fp64, OpenMP over (batch, channel))"}
@@ -129,6 +145,8 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd: mamba_scan_fwd (the headline); bwd: mamba_scan_bwd on the same workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -153,6 +171,9 @@ def main():
         calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
         return
     w = W.WORKLOADS[args.workload]
+    if args.which == "bwd" and w.decode_steps > 0:
+        print("bench.py: --pass bwd applies to the full-sequence workloads, not decode", file=sys.stderr)
+        sys.exit(2)
     inp = W.generate_workload(args.workload)
     tdt = torch.bfloat16 if w.io == "bf16" else torch.float32
     io_bytes = 2 if w.io == "bf16" else 4
@@ -183,6 +204,30 @@ def main():
 
         units = batch * L * D * N
         bytes_per_step = algorithmic_bytes(batch, L, D, N, io_bytes, decode=True) * L
+    elif args.which == "bwd":
+        from selective_state_space_22_amd import workloads as Wl
+
+        gi = Wl.grad_inputs(w.batch, w.seqlen, w.dim, w.dstate, w.io, seed=w.seed)
+        dout, dlast = t(gi.dout), f(gi.dlast)
+        grads = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u), "dz": torch.empty_like(u),
+                 "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+                 "dA": torch.empty((w.dim, w.dstate), dtype=torch.float32, device=dev),
+                 "dDskip": torch.empty(w.dim, dtype=torch.float32, device=dev),
+                 "ddelta_bias": torch.empty(w.dim, dtype=torch.float32, device=dev),
+                 "dh0": torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)}
+        ws_bytes = binding.mamba_scan_bwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
+                                                         1 if w.io == "bf16" else 0)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.mamba_scan_bwd(u, delta, A, B, C, dout, bias, dskip, z, True, None, dlast, grads=grads,
+                                   workspace=ws)
+
+        units = w.elements
+        # inputs u, delta, z, dout, B, C read once; du, ddelta, dz, dB, dC written once
+        bytes_per_step = (4 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
+                          + 3 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
+                          + 8 * w.dim * w.dstate + 16 * w.dim + 8 * w.batch * w.dim * w.dstate)
     else:
         out = torch.empty_like(u)
         last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
@@ -239,7 +284,11 @@ def main():
     gbps = bytes_per_step / (ms * 1e-3) / 1e9
     flops = units * FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload) if args.which == "fwd" else None
+    if args.which == "bwd":
+        # per (b, l, d, n): forward recompute (9) as above plus the reverse step (~20 fp32 ops, FMA = 2)
+        flops = units * (FLOPS_PER_ELEMENT + BWD_FLOPS_PER_ELEMENT) + (units / w.dstate) * 30.0
+        tflops = flops / (ms * 1e-3) / 1e12
     if decode:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -251,7 +300,8 @@ def main():
                 "note": "fp32 VALU without packed-fp32 instructions; frac vs the packed 157.3 TFLOP/s "
                         f"figure: {tflops / VALU_FP32_PACKED_TFLOPS:.4f}"}
     rec = {
-        "metric": metric_name(),
+        "metric": metric_name() if args.which == "fwd" else
+        "selective-scan bwd elements(B*L*D*N)/s (all gradients, states recomputed)",
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,
@@ -263,7 +313,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+        "config": {"workload": args.workload, "pass": args.which, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "state_dtype": "f32",
                    "flush_infinity_cache": bool(args.flush), "hip_graph": bool(use_graph),
                    "parallelism": "single-gpu"},
@@ -273,7 +323,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, args.workload)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.workload, args.which)
     print(json.dumps(rec), flush=True)
 
 

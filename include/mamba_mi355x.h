@@ -115,6 +115,53 @@ int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                        const void* B, const void* C, const float* Dskip, const void* z,
                        int delta_softplus, void* out, void* stream);
 
+/*
+ * Bytes of device workspace mamba_scan_bwd needs for this shape: per-chunk
+ * state and gradient carries, the state at the start of every 8-token tile
+ * (4*dstate bytes per (batch row, token/8, channel)), and per-channel-block
+ * partial sums of dB and dC (8*dstate bytes per (batch row, token, 64
+ * channels)).  A pure host function; 0 for arguments mamba_scan_bwd would
+ * reject and for shapes with no tokens.
+ */
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype);
+
+/*
+ * Backward of mamba_scan_fwd: gradients of
+ *     sum(dout * out) + sum(dlast_state * last_state)
+ * with respect to every input, where out and last_state are what
+ * mamba_scan_fwd computes from the same inputs.  The expanded states are
+ * recomputed from the inputs, not read from a saved forward (section 4.1,
+ * recomputation); nothing of the forward call is needed.
+ *   inputs u ... h0  : exactly as for mamba_scan_fwd (same nullability)
+ *   dout             : (batch, seqlen, dim)    I/O type, gradient at out
+ *   dlast_state      : (batch, dim, dstate)    float, nullable (zero)
+ * Outputs (all overwritten, never accumulated into):
+ *   du, ddelta       : (batch, seqlen, dim)    I/O type; ddelta is the gradient
+ *                      at the raw delta (through the softplus when it is on)
+ *   dz               : (batch, seqlen, dim)    I/O type, nullable; written only
+ *                      when z is given
+ *   dB, dC           : (batch, seqlen, dstate) I/O type
+ *   dA               : (dim, dstate)           float
+ *   dDskip           : (dim)                   float, nullable
+ *   ddelta_bias      : (dim)                   float, nullable
+ *   dh0              : (batch, dim, dstate)    float, nullable; gradient at the
+ *                      initial state (defined also when h0 is NULL)
+ *   workspace        : device buffer of at least mamba_scan_bwd_workspace_size()
+ *                      bytes when the shape has tokens; contents are scratch.
+ * dA, dDskip, ddelta_bias, dB and dC are sums over batch rows, tokens or
+ * channels formed in a fixed order: repeated calls give identical bits.
+ * Limits as for mamba_scan_fwd.  seqlen == 0 writes dA = dDskip =
+ * ddelta_bias = 0 and dh0 = dlast_state (or 0).
+ */
+int mamba_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                   const void* u, const void* delta, const float* delta_bias, const float* A,
+                   const void* B, const void* C, const float* Dskip, const void* z,
+                   int delta_softplus, const float* h0,
+                   const void* dout, const float* dlast_state,
+                   void* du, void* ddelta, float* dA, void* dB, void* dC,
+                   float* dDskip, void* dz, float* ddelta_bias, float* dh0,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -189,7 +189,7 @@ int s6_oracle_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N,
         double* dB_loc = (double*)calloc((size_t)batch * L * N, sizeof(double));
         double* dC_loc = (double*)calloc((size_t)batch * L * N, sizeof(double));
         if (!hs || !g || !dA_loc || !dD_loc || !db_loc || !dB_loc || !dC_loc) bad |= 1;
-#pragma omp for schedule(dynamic, 1)
+#pragma omp for schedule(static)
         for (int64_t unit = 0; unit < batch * D; ++unit) {
             if (bad) continue;
             int64_t b = unit / D, d = unit % D;

@@ -1,13 +1,15 @@
 """MI355X (gfx950) selective scan (S6): HIP kernels behind a C ABI.
 
-    from selective_state_space_22_amd import mamba_scan_fwd, mamba_state_update
+    from selective_state_space_22_amd import mamba_scan_fwd, mamba_scan_bwd, mamba_state_update
 
 The functions are thin ctypes wrappers of libmamba_mi355x.so (see
 include/mamba_mi355x.h); build the library with
 ``python -m selective_state_space_22_amd.build``.
 """
-from .binding import (MAMBA_IO_BF16, MAMBA_IO_F32, MambaError, load_library, mamba_scan_fwd,
-                      mamba_scan_fwd_workspace_size, mamba_state_update, mamba_version, status_string)
+from .binding import (MAMBA_IO_BF16, MAMBA_IO_F32, MambaError, load_library, mamba_scan_bwd,
+                      mamba_scan_bwd_workspace_size, mamba_scan_fwd, mamba_scan_fwd_workspace_size,
+                      mamba_state_update, mamba_version, status_string)
 
-__all__ = ["mamba_scan_fwd", "mamba_state_update", "mamba_scan_fwd_workspace_size", "mamba_version",
-           "status_string", "load_library", "MambaError", "MAMBA_IO_F32", "MAMBA_IO_BF16"]
+__all__ = ["mamba_scan_fwd", "mamba_scan_bwd", "mamba_state_update", "mamba_scan_fwd_workspace_size",
+           "mamba_scan_bwd_workspace_size", "mamba_version", "status_string", "load_library", "MambaError",
+           "MAMBA_IO_F32", "MAMBA_IO_BF16"]

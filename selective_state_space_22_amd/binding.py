@@ -47,6 +47,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_scan_fwd.restype = I
     lib.mamba_state_update.argtypes = [I64, I64, I64, I, P, P, P, P, P, P, P, P, P, I, P, P]
     lib.mamba_state_update.restype = I
+    lib.mamba_scan_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I]
+    lib.mamba_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd.argtypes = [I64, I64, I64, I64, I] + [P] * 8 + [I, P, P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
+    lib.mamba_scan_bwd.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -155,3 +159,57 @@ def mamba_state_update(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=
     if st != 0:
         raise MambaError("mamba_state_update", st)
     return out
+
+
+def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, io_dtype: int) -> int:
+    return int(load_library().mamba_scan_bwd_workspace_size(batch, seqlen, dim, dstate, io_dtype))
+
+
+def mamba_scan_bwd(u, delta, A, B, C, dout, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
+                   dlast_state=None, grads=None, workspace=None, want=("dDskip", "dz", "ddelta_bias", "dh0")):
+    """Backward of mamba_scan_fwd: gradients of sum(dout*out) + sum(dlast_state*last_state).
+
+    Returns a dict with du, ddelta, dA, dB, dC and those of dDskip, dz (only
+    with z), ddelta_bias, dh0 named in ``want``.  Preallocated outputs may be
+    passed in ``grads`` (same keys)."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    g = dict(grads or {})
+    shapes = {"du": ((batch, L, D), u.dtype), "ddelta": ((batch, L, D), u.dtype), "dA": ((D, N), f32),
+              "dB": ((batch, L, N), u.dtype), "dC": ((batch, L, N), u.dtype), "dDskip": ((D,), f32),
+              "dz": ((batch, L, D), u.dtype), "ddelta_bias": ((D,), f32), "dh0": ((batch, D, N), f32)}
+    need = ["du", "ddelta", "dA", "dB", "dC"] + [k for k in want if k != "dz" or z is not None]
+    for k in need:
+        if k not in g:
+            shp, dt = shapes[k]
+            g[k] = torch.empty(shp, dtype=dt, device=dev)
+    ws_bytes = mamba_scan_bwd_workspace_size(batch, L, D, N, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def gp(k):
+        if k not in g:
+            return None
+        shp, dt = shapes[k]
+        return _ptr(g[k], k, dt, shp, dev)
+
+    st = lib.mamba_scan_bwd(
+        batch, L, D, N, io,
+        _ptr(u, "u", u.dtype, (batch, L, D), dev), _ptr(delta, "delta", u.dtype, (batch, L, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev),
+        _ptr(B, "B", u.dtype, (batch, L, N), dev), _ptr(C, "C", u.dtype, (batch, L, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, L, D), dev),
+        int(bool(delta_softplus)), _ptr(h0, "h0", f32, (batch, D, N), dev),
+        _ptr(dout, "dout", u.dtype, (batch, L, D), dev), _ptr(dlast_state, "dlast_state", f32, (batch, D, N), dev),
+        gp("du"), gp("ddelta"), gp("dA"), gp("dB"), gp("dC"), gp("dDskip"), gp("dz"), gp("ddelta_bias"), gp("dh0"),
+        _ptr(workspace, "workspace", device=dev),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_scan_bwd", st)
+    return {k: g[k] for k in need}

@@ -172,4 +172,94 @@ int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
   return MAMBA_OK;
 }
 
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype) {
+  if (check_shape("mamba_scan_bwd_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK) return 0;
+  return s6::plan_bwd(batch, seqlen, dim, dstate).ws_bytes;
+}
+
+int mamba_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                   const void* u, const void* delta, const float* delta_bias, const float* A,
+                   const void* B, const void* C, const float* Dskip, const void* z,
+                   int delta_softplus, const float* h0,
+                   const void* dout, const float* dlast_state,
+                   void* du, void* ddelta, float* dA, void* dB, void* dC,
+                   float* dDskip, void* dz, float* ddelta_bias, float* dh0,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "mamba_scan_bwd";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  const bool tokens = batch > 0 && seqlen > 0 && dim > 0;
+  const bool chans = batch > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(u, tokens, "u");
+  pc.req(delta, tokens, "delta");
+  pc.req(A, tokens, "A");
+  pc.req(B, tokens, "B");
+  pc.req(C, tokens, "C");
+  pc.req(dout, tokens, "dout");
+  pc.req(du, tokens, "du");
+  pc.req(ddelta, tokens, "ddelta");
+  pc.req(dA, dim > 0, "dA");
+  pc.req(dB, tokens, "dB");
+  pc.req(dC, tokens, "dC");
+  pc.opt(delta_bias, "delta_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(z, "z");
+  pc.opt(h0, "h0");
+  pc.opt(dlast_state, "dlast_state");
+  pc.opt(dDskip, "dDskip");
+  pc.opt(dz, "dz");
+  pc.opt(ddelta_bias, "ddelta_bias");
+  pc.opt(dh0, "dh0");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (dim == 0) return MAMBA_OK;
+  const s6::BwdPlan plan = s6::plan_bwd(batch, seqlen, dim, dstate);
+  if (tokens && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  s6::BwdArgs a{};
+  a.u = u;
+  a.delta = delta;
+  a.bias = delta_bias;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.dout = dout;
+  a.dlast = dlast_state;
+  a.du = du;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dDskip = dDskip;
+  a.dz = dz;
+  a.dbias = ddelta_bias;
+  a.dh0 = dh0;
+  if (tokens) {
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.hs = reinterpret_cast<float*>(w + plan.off_hs);
+    a.gq = reinterpret_cast<float*>(w + plan.off_gq);
+    a.sdt = reinterpret_cast<float*>(w + plan.off_sdt);
+    a.srel = reinterpret_cast<float*>(w + plan.off_srel);
+    a.cdt = reinterpret_cast<float*>(w + plan.off_cdt);
+    a.pbc = reinterpret_cast<float*>(w + plan.off_pbc);
+    a.pA = reinterpret_cast<float*>(w + plan.off_pA);
+    a.pD = reinterpret_cast<float*>(w + plan.off_pD);
+  }
+  a.batch = chans ? batch : 0;
+  a.L = seqlen;
+  a.D = dim;
+  a.chunk_len = plan.chunk_len;
+  a.nchunks = plan.nchunks;
+  a.tpc = plan.tpc;
+  a.nblk = plan.nblk;
+  a.softplus = delta_softplus != 0;
+  hipError_t e = s6::launch_bwd(a, io_dtype, (int)dstate, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
 }  // extern "C"

@@ -94,6 +94,57 @@ int wg_tile(int64_t N);
 
 bool dstate_supported(int64_t N);
 
+// ---------------------------------------------------------------- backward (scan_bwd.hip)
+
+constexpr int kBwdTile = 8;  // tokens per tile of the backward passes
+
+// Arguments of one backward scan; pointers are device pointers.
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* bias;   // may be null
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* dskip;  // may be null
+  const void* z;       // may be null
+  const float* h0;     // may be null
+  const void* dout;
+  const float* dlast;  // may be null
+  void* du;
+  void* ddelta;
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dDskip;       // may be null
+  void* dz;            // may be null
+  float* dbias;        // may be null
+  float* dh0;          // may be null
+  // workspace
+  float* hs;    // (batch, G, N, D) chunk end state from zero, then the state entering the chunk
+  float* gq;    // (batch, G, N, D) chunk gradient aggregate, then the gradient arriving at the chunk end
+  float* sdt;   // (batch, G, D) sum of dt over the chunk
+  float* srel;  // (batch, G, tpc, N, D) state at each tile start, relative to a zero chunk start
+  float* cdt;   // (batch, G, tpc, D) sum of dt from the chunk start to each tile start
+  float* pbc;   // (batch, nblk, L, 2, N) per-block partial dB (0) and dC (1)
+  float* pA;    // (batch * G, N, D) per-chunk partial dA
+  float* pD;    // (batch * G, 2, D) per-chunk partial dDskip (0) and bias gradient (1)
+  int64_t batch, L, D;
+  int64_t chunk_len;
+  int32_t nchunks, tpc, nblk;
+  int32_t softplus;
+};
+
+struct BwdPlan {
+  int64_t chunk_len;
+  int32_t nchunks, tpc, nblk;
+  size_t off_hs, off_gq, off_sdt, off_srel, off_cdt, off_pbc, off_pA, off_pD;
+  size_t ws_bytes;
+};
+
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N);
+hipError_t launch_bwd(const BwdArgs& a, int io, int N, hipStream_t stream);
+
 // Enqueue the kernels of one scan / one decode step on `stream`.
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
 // Carry pass over (batch, chunk, D, N) chunk aggregates (both engines' split modes).

@@ -1,0 +1,784 @@
+// scan_bwd.hip -- backward of the selective scan (S6) on gfx950.
+//
+// Gradients of  sum(dout * out) + sum(dlast * last_state)  with respect to
+// u, delta, A, B, C, Dskip, z, the dt bias and the initial state, where out and
+// last_state are the forward of "Mamba 状态空间模型原理与 Transformer 对比"
+// (kb.agiseed.tech): section 2.1 eq. (2) (zero-order hold), eq. (3a)/(3b)
+// (recurrence, readout), the section 3.2 softplus front end and the Figure 3
+// SiLU gate.  Section 4.1 (its third technique, recomputation) keeps the
+// expanded state out of HBM in the forward and rebuilds it from the inputs in
+// the backward; this follows that choice: no (batch, L, D, N) tensor is ever
+// written.
+//
+// Per state n of channel d, with x = dt A_n, a = e^x, beta = (a - 1)/A_n and
+// G_t the gradient at h_t (it runs backwards: G_{t-1} gets a_t G_t):
+//   G_t     = a_{t+1} G_{t+1} + dy_t C_t          dy = dout * SiLU(z)
+//   dC_t   += dy_t h_t        (summed over channels)
+//   dB_t   += G_t beta_t x_t  (summed over channels)
+//   du_t    = Dskip dy_t + sum_n G_t beta_t B_t
+//   ddt_t   = sum_n a_t (G_t h_{t-1} A_n + G_t B_t x_t)    (d beta/d dt = a)
+//   dA_n   += G_t h_{t-1} dt a + G_t B_t x_t * d beta/d A_n
+//   ddelta  = ddt * sigmoid(raw + bias) under the softplus, ddt otherwise.
+//
+// Passes (all chunk-parallel; the sequence is cut into chunks of K tokens and
+// chunks into tiles of T tokens):
+//   1. aggregate: per (batch row, chunk, 64-channel block) the state at every
+//      tile start relative to a zero state at the chunk start, the chunk's
+//      end state from zero, its sum of dt and the gradient aggregate
+//      Q = sum_t (prod_{r<=t} a_r) dy_t C_t (what the chunk's outputs send
+//      back to the state just before it);
+//   2. carry: per (batch row, channel, state), the absolute state entering
+//      every chunk (forward over chunks) and the gradient arriving at every
+//      chunk end (backward over chunks), by the associative composition of
+//      the chunk aggregates;
+//   3. main: per (batch row, chunk, block), tiles in reverse order: the
+//      tile-start state is rebuilt from pass 1 and 2, the tile's T states are
+//      recomputed in registers, then the reverse recurrence produces every
+//      gradient; sums over the N states go through LDS, sums over the 64
+//      channels of a wave through a cross-lane reduce-scatter, and sums over
+//      channel blocks and chunks through per-block partials;
+//   4. reduce: the partials of dB, dC, dA, dDskip and the dt bias, in a fixed
+//      order (the result does not depend on scheduling).
+#include <cstdlib>
+
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+namespace {
+
+constexpr int32_t kBufferDword3 = 0x00020000;  // raw (untyped) buffer access on the gfx9 family
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offset beyond every buffer: loads 0, stores dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
+}
+
+template <typename IO>
+struct Io;
+template <>
+struct Io<uint16_t> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw << 16); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+  }
+};
+template <>
+struct Io<float> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float ldf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void stf(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ float sigmoid(float v) { return rcp(1.0f + ex2(-v * kLog2e)); }
+
+// d beta / d A_n for one state, beta = (e^x - 1)/A_n, x = dt A_n (x2 = x log2 e):
+//   dt^2 psi(x),  psi(x) = (x e^x - e^x + 1)/x^2 = 1/2 + x/3 + x^2/8 + x^3/30 + ...
+// For |x| < 0.1 the four-term series (truncation below 1.4e-6 relative); above
+// it (dt a - beta)/A_n, whose cancellation costs ~2 * 0.74 ulp / x^2 < 9e-6
+// there (beta itself carries 0.74 ulp / |x| from v_exp_f32).
+constexpr float kPsiSeriesX2 = 0.1f * kLog2e;
+__device__ __forceinline__ float dbeta_dA(float abar, float beta, float x2, float dt, float dt2, float ka) {
+  constexpr float c1 = kLn2 / 3.0f;
+  constexpr float c2 = kLn2 * kLn2 / 8.0f;
+  constexpr float c3 = kLn2 * kLn2 * kLn2 / 30.0f;
+  const float big = __builtin_fmaf(dt, abar, -beta) * ka;
+  const float psi = __builtin_fmaf(x2, __builtin_fmaf(x2, __builtin_fmaf(x2, c3, c2), c1), 0.5f);
+  return fabsf(x2) < kPsiSeriesX2 ? dt2 * psi : big;
+}
+
+// ---------------------------------------------------------------- reduce-scatter over the 64 lanes of a wave
+//
+// v[0..NV-1] per lane -> lane l ends with the sum over all 64 lanes of
+// v[l >> (6 - log2 NV)] (lanes sharing a value hold the same total).  Each
+// level pairs lanes that differ in one lane bit, from bit 5 down to bit 0; a
+// lane keeps the upper half of its values when that bit is set.  Bits 5 and 4
+// use the gfx950 row-swap instructions (one swap serves two values); bits 3..0
+// use DPP lane permutations fused into the add.
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {  // quad_perm [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1,0,3,2]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+
+template <int C, int BIT>
+__device__ __forceinline__ void rs_level(float* v, int lane) {
+  if (BIT == 5) {
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + C / 2]), false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else if (BIT == 4) {
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+      auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + C / 2]), false, false);
+      v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+      const float keep = hi ? v[i + C / 2] : v[i];
+      const float send = hi ? v[i] : v[i + C / 2];
+      float got;
+      if (BIT == 3) got = dpp_ror8(send);
+      else if (BIT == 2) got = dpp_half_mirror(send);
+      else if (BIT == 1) got = dpp_xor2(send);
+      else got = dpp_xor1(send);
+      v[i] = keep + got;
+    }
+  }
+}
+
+// Plain butterfly add at a lane bit (both partners end with the pair's sum).
+template <int BIT>
+__device__ __forceinline__ float bf_level(float v) {
+  if (BIT == 5) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if (BIT == 4) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if (BIT == 3) {
+    return v + dpp_ror8(v);
+  } else if (BIT == 2) {
+    return v + dpp_half_mirror(v);
+  } else if (BIT == 1) {
+    return v + dpp_xor2(v);
+  }
+  return v + dpp_xor1(v);
+}
+
+template <int NV>
+__device__ __forceinline__ float reduce_scatter(float (&v)[NV], int lane) {
+  static_assert(NV == 16 || NV == 32 || NV == 64, "values per lane");
+  rs_level<NV, 5>(v, lane);
+  rs_level<NV / 2, 4>(v, lane);
+  rs_level<NV / 4, 3>(v, lane);
+  rs_level<NV / 8, 2>(v, lane);
+  float r;
+  if (NV == 16) {
+    r = bf_level<1>(v[0]);
+    r = bf_level<0>(r);
+  } else if (NV == 32) {
+    rs_level<NV / 16, 1>(v, lane);
+    r = bf_level<0>(v[0]);
+  } else {
+    rs_level<NV / 16, 1>(v, lane);
+    rs_level<NV / 32, 0>(v, lane);
+    r = v[0];
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- the per-item machinery shared by passes 1 and 3
+
+template <typename IO, int N, int W, int T>
+struct BwdTile {
+  static constexpr int S = N / W;             // states per wave (lane = channel)
+  static constexpr int TW = T / W;            // front / epilogue tokens per wave per tile
+  static constexpr int NT = 64 * W;           // threads
+  static constexpr int BCW = (2 * S + 3) / 4 * 4;
+  static constexpr uint32_t kIo = sizeof(IO);
+  static_assert(N % W == 0 && T % W == 0 && 2 * T * N <= NT, "tile shape");
+
+  struct Raw {  // prefetched global data of this thread's share of one tile
+    uint32_t dl[TW], uu[TW], zz[TW], go[TW];
+    uint32_t bcv;
+  };
+
+  const BwdArgs& A;
+  const int lane, w;
+  int64_t b, d, t0, t1;
+  int g;
+  bool dvalid;
+  uint32_t chan_off;
+  __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_go, r_B, r_C;
+  float a2[S], ka[S], ah[S], av[S];
+  float bias, dskip;
+
+  __device__ BwdTile(const BwdArgs& a)
+      : A(a), lane(threadIdx.x & 63), w(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {}
+
+  __device__ __forceinline__ void setup(int item) {
+    const int blk = item % A.nblk;
+    const int bg = item / A.nblk;
+    g = bg % A.nchunks;
+    b = bg / A.nchunks;
+    d = (int64_t)blk * 64 + lane;
+    dvalid = d < A.D;
+    t0 = (int64_t)g * A.chunk_len;
+    t1 = t0 + A.chunk_len < A.L ? t0 + A.chunk_len : A.L;
+    chan_off = dvalid ? (uint32_t)(d * kIo) : kOutOfRange;
+    const size_t row0 = (size_t)b * A.L + t0;
+    const uint32_t span = (uint32_t)((t1 - t0) * A.D * kIo);
+    const uint32_t bspan = (uint32_t)((t1 - t0) * N * kIo);
+    r_u = make_rsrc(static_cast<const IO*>(A.u) + row0 * A.D, span);
+    r_dl = make_rsrc(static_cast<const IO*>(A.delta) + row0 * A.D, span);
+    r_z = make_rsrc(A.z ? static_cast<const IO*>(A.z) + row0 * A.D : static_cast<const IO*>(A.u), A.z ? span : 0u);
+    r_go = make_rsrc(static_cast<const IO*>(A.dout) + row0 * A.D, span);
+    r_B = make_rsrc(static_cast<const IO*>(A.B) + row0 * N, bspan);
+    r_C = make_rsrc(static_cast<const IO*>(A.C) + row0 * N, bspan);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float a = dvalid ? A.A[d * N + w * S + s] : -1.0f;
+      a2[s] = a * kLog2e;
+      ka[s] = rcp(a);
+      ah[s] = 0.5f * a;
+      av[s] = a;
+    }
+    bias = (dvalid && A.bias) ? A.bias[d] : 0.0f;
+    dskip = (dvalid && A.dskip) ? A.dskip[d] : 0.0f;
+  }
+
+  __device__ __forceinline__ int ntiles() const { return (int)((t1 - t0 + T - 1) / T); }
+  __device__ __forceinline__ int tile_valid(int k) const {
+    const int64_t r = t1 - (t0 + (int64_t)k * T);
+    return r <= 0 ? 0 : (r >= T ? T : (int)r);
+  }
+
+  // Global loads of tile k (unconditional; out of range reads zero).
+  __device__ __forceinline__ void load(Raw& r, int k) const {
+    const uint32_t row = (uint32_t)(A.D * kIo);
+    const uint32_t base = chan_off + (uint32_t)(k * T + w) * row;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const uint32_t off = base + (uint32_t)(W * i) * row;
+      r.dl[i] = Io<IO>::load(r_dl, off);
+      r.uu[i] = Io<IO>::load(r_u, off);
+      r.zz[i] = Io<IO>::load(r_z, off);
+      r.go[i] = Io<IO>::load(r_go, off);
+    }
+    // thread e < 2TN stages element e of the tile's B block (e < TN) or C block;
+    // both buffers are addressed so that the resource stays wave-uniform
+    const int e = threadIdx.x;
+    const int q = e / (T * N);
+    const int rem = e - q * (T * N);
+    const uint32_t off = (uint32_t)(k * T * N + rem) * kIo;
+    const uint32_t vb = Io<IO>::load(r_B, q == 0 ? off : kOutOfRange);
+    const uint32_t vc = Io<IO>::load(r_C, q == 1 ? off : kOutOfRange);
+    r.bcv = q == 0 ? vb : vc;
+  }
+
+  // Per-token front end: dt, its square, x, dy = dout*SiLU(z); for the main
+  // pass also sigmoid(raw + bias) (softplus derivative) and dout*SiLU'(z).
+  // Tokens past the chunk end give all zeros, which leaves every state and
+  // gradient unchanged and contributes nothing.
+  struct Front {
+    float dt, dt2, x, dy, sg, dzf;
+  };
+  __device__ __forceinline__ Front front_one(const Raw& r, int i, bool valid) const {
+    Front f;
+    const float v = Io<IO>::widen(r.dl[i]) + bias;
+    const bool sp = A.softplus != 0;
+    const float dt = sp ? softplus(v) : v;
+    const float go = Io<IO>::widen(r.go[i]);
+    float dy = go, dzf = 0.0f;
+    if (A.z) {
+      const float z = Io<IO>::widen(r.zz[i]);
+      const float sz = sigmoid(z);
+      dy = go * (z * sz);
+      dzf = go * (sz * __builtin_fmaf(z, 1.0f - sz, 1.0f));
+    }
+    f.dt = valid ? dt : 0.0f;
+    f.dt2 = f.dt * f.dt;
+    f.x = valid ? Io<IO>::widen(r.uu[i]) : 0.0f;
+    f.dy = valid ? dy : 0.0f;
+    f.sg = valid ? (sp ? sigmoid(v) : 1.0f) : 0.0f;
+    f.dzf = valid ? dzf : 0.0f;
+    return f;
+  }
+
+  __device__ __forceinline__ void stage_bc(const Raw& r, float (*bc)[W][BCW]) const {
+    const int e = threadIdx.x;
+    if (e < 2 * T * N) {
+      const int q = e / (T * N);
+      const int rem = e - q * (T * N);
+      const int j = rem / N, n = rem % N;
+      bc[j][n / S][q * S + n % S] = Io<IO>::widen(r.bcv);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- pass 1: chunk aggregates
+
+template <typename IO, int N, int W, int T>
+__global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
+  using K = BwdTile<IO, N, W, T>;
+  constexpr int S = K::S, TW = K::TW, BCW = K::BCW;
+  __shared__ float4 fr[2][T][64];  // dt, dt^2, x, dy
+  __shared__ __attribute__((aligned(16))) float bc[2][T][W][BCW];
+  K k(a);
+  k.setup(blockIdx.x);
+  const int nt = k.ntiles();
+  const int64_t bg = k.b * a.nchunks + k.g;
+  const uint32_t dbytes = (uint32_t)(k.d * 4);
+  const bool dv = k.dvalid;
+  // workspace buffers of this (batch row, chunk)
+  const __amdgpu_buffer_rsrc_t r_srel =
+      make_rsrc(a.srel + (size_t)bg * a.tpc * N * a.D, (uint32_t)((size_t)a.tpc * N * a.D * 4));
+  const __amdgpu_buffer_rsrc_t r_cdt = make_rsrc(a.cdt + (size_t)bg * a.tpc * a.D, (uint32_t)((size_t)a.tpc * a.D * 4));
+
+  float h[S], p[S], q[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    h[s] = 0.0f;
+    q[s] = 0.0f;
+  }
+  float csum = 0.0f, ccomp = 0.0f;  // compensated running sum of dt (identical in every wave)
+
+  typename K::Raw r;
+  auto front = [&](int kt, int slot) {
+    const int nv = k.tile_valid(kt);
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int j = k.w + W * i;
+      const typename K::Front f = k.front_one(r, i, j < nv);
+      fr[slot][j][k.lane] = make_float4(f.dt, f.dt2, f.x, f.dy);
+    }
+    k.stage_bc(r, bc[slot]);
+  };
+  k.load(r, 0);
+  front(0, 0);
+  k.load(r, 1);
+  __syncthreads();
+  for (int kt = 0; kt < nt; ++kt) {
+    const int slot = kt & 1;
+    front(kt + 1, slot ^ 1);
+    k.load(r, kt + 2);
+    // tile start: state relative to the chunk start, cumulative dt
+    const float cs = csum - ccomp;
+    const uint32_t toff = (uint32_t)kt * (uint32_t)(N * a.D * 4);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      stf(h[s], r_srel, dv ? toff + (uint32_t)((k.w * S + s) * a.D * 4) + dbytes : kOutOfRange);
+      p[s] = ex2(k.a2[s] * cs);  // product of Abar over the chunk so far, re-anchored per tile
+    }
+    if (k.w == 0) stf(cs, r_cdt, dv ? (uint32_t)kt * (uint32_t)(a.D * 4) + dbytes : kOutOfRange);
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const float4 fv = fr[slot][j][k.lane];
+      const float4 b4 = *reinterpret_cast<const float4*>(&bc[slot][j][k.w][0]);
+      const float bcs[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float x2 = fv.x * k.a2[s];
+        const float ab = ex2(x2);
+        const float be = input_weight(ab, x2, fv.x, fv.y, k.ka[s], k.ah[s]);
+        h[s] = __builtin_fmaf(ab, h[s], be * (bcs[s] * fv.z));
+        p[s] *= ab;
+        q[s] = __builtin_fmaf(p[s], fv.w * bcs[S + s], q[s]);
+      }
+      const float yk = fv.x - ccomp;
+      const float tk = csum + yk;
+      ccomp = (tk - csum) - yk;
+      csum = tk;
+    }
+    __syncthreads();
+  }
+  // chunk end: state from zero, gradient aggregate, sum of dt
+  if (dv) {
+    const size_t cb = (size_t)bg * N * a.D + (size_t)k.d;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      a.hs[cb + (size_t)(k.w * S + s) * a.D] = h[s];
+      a.gq[cb + (size_t)(k.w * S + s) * a.D] = q[s];
+    }
+    if (k.w == 0) a.sdt[(size_t)bg * a.D + k.d] = csum - ccomp;
+  }
+}
+
+// ---------------------------------------------------------------- pass 2: carries over chunks
+
+template <int N>
+__global__ void bwd_carry_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, n, d), d fastest
+  const int64_t total = a.batch * N * a.D;
+  if (i >= total) return;
+  const int64_t d = i % a.D;
+  const int n = (int)((i / a.D) % N);
+  const int64_t b = i / (a.D * N);
+  const float a2 = a.A[d * N + n] * kLog2e;
+  const int G = a.nchunks;
+  float hcur = a.h0 ? a.h0[(b * a.D + d) * N + n] : 0.0f;
+  for (int c = 0; c < G; ++c) {
+    const size_t idx = ((size_t)(b * G + c) * N + n) * a.D + d;
+    const float send = a.hs[idx];
+    const float P = ex2(a2 * a.sdt[(size_t)(b * G + c) * a.D + d]);
+    a.hs[idx] = hcur;  // state entering chunk c
+    hcur = __builtin_fmaf(P, hcur, send);
+  }
+  float gcur = a.dlast ? a.dlast[(b * a.D + d) * N + n] : 0.0f;
+  for (int c = G - 1; c >= 0; --c) {
+    const size_t idx = ((size_t)(b * G + c) * N + n) * a.D + d;
+    const float qc = a.gq[idx];
+    const float P = ex2(a2 * a.sdt[(size_t)(b * G + c) * a.D + d]);
+    a.gq[idx] = gcur;  // gradient arriving at the end of chunk c from later tokens
+    gcur = __builtin_fmaf(P, gcur, qc);
+  }
+}
+
+// ---------------------------------------------------------------- pass 3: main backward
+
+template <typename IO, int N, int W, int T>
+struct MainLds {
+  float4 fr[3][T][64];                       // dt, dt^2, x, dy
+  float2 fe[3][T][64];                       // sigmoid(raw+bias) (or 1), dout*SiLU'(z)
+  __attribute__((aligned(16))) float bc[3][T][W][BwdTile<IO, N, W, T>::BCW];
+  float ex[2][3][T][W][64];                  // per-wave partial sums over states: readout, du, ddt
+};
+
+template <typename IO, int N, int W, int T>
+__global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
+  using K = BwdTile<IO, N, W, T>;
+  constexpr int S = K::S, TW = K::TW;
+  constexpr int NV = 2 * T * S;
+  __shared__ MainLds<IO, N, W, T> sm;
+  K k(a);
+  k.setup(blockIdx.x);
+  const int nt = k.ntiles();
+  const int lane = k.lane, w = k.w;
+  const int64_t bg = k.b * a.nchunks + k.g;
+  const bool dv = k.dvalid;
+  const uint32_t dbytes = (uint32_t)(k.d * 4);
+  const int blk = blockIdx.x % a.nblk;
+  const __amdgpu_buffer_rsrc_t r_srel =
+      make_rsrc(a.srel + (size_t)bg * a.tpc * N * a.D, (uint32_t)((size_t)a.tpc * N * a.D * 4));
+  const __amdgpu_buffer_rsrc_t r_cdt = make_rsrc(a.cdt + (size_t)bg * a.tpc * a.D, (uint32_t)((size_t)a.tpc * a.D * 4));
+  // outputs of this chunk
+  const size_t row0 = (size_t)k.b * a.L + k.t0;
+  const uint32_t span = (uint32_t)((k.t1 - k.t0) * a.D * K::kIo);
+  const __amdgpu_buffer_rsrc_t r_du = make_rsrc(static_cast<IO*>(a.du) + row0 * a.D, span);
+  const __amdgpu_buffer_rsrc_t r_dd = make_rsrc(static_cast<IO*>(a.ddelta) + row0 * a.D, span);
+  const bool want_dz = a.z && a.dz;
+  const __amdgpu_buffer_rsrc_t r_dz =
+      make_rsrc(want_dz ? static_cast<IO*>(a.dz) + row0 * a.D : static_cast<IO*>(a.du), want_dz ? span : 0u);
+  // partial dB/dC of this (batch row, block): (L, 2, N) floats, rows of this chunk
+  const __amdgpu_buffer_rsrc_t r_pbc =
+      make_rsrc(a.pbc + (((size_t)k.b * a.nblk + blk) * a.L + k.t0) * 2 * N, (uint32_t)((k.t1 - k.t0) * 2 * N * 4));
+
+  // chunk entry state and the gradient arriving at the chunk end
+  float hs0[S], g[S], dacc[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const size_t idx = ((size_t)bg * N + w * S + s) * a.D + k.d;
+    hs0[s] = dv ? a.hs[idx] : 0.0f;
+    g[s] = dv ? a.gq[idx] : 0.0f;
+    dacc[s] = 0.0f;
+  }
+  float dsk = 0.0f, dbs = 0.0f;  // this wave's share of the dDskip and bias sums
+
+  typename K::Raw r;
+  auto front = [&](int kt, int slot) {
+    const int nv = k.tile_valid(kt);
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int j = w + W * i;
+      const typename K::Front f = k.front_one(r, i, j < nv);
+      sm.fr[slot][j][lane] = make_float4(f.dt, f.dt2, f.x, f.dy);
+      sm.fe[slot][j][lane] = make_float2(f.sg, f.dzf);
+    }
+    k.stage_bc(r, sm.bc[slot]);
+  };
+  // tile-start data (relative state and cumulative dt) of tile kt into registers
+  float srel[S], cdt;
+  auto load_start = [&](int kt) {
+    const uint32_t toff = (uint32_t)(kt < 0 ? 0 : kt) * (uint32_t)(N * a.D * 4);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      srel[s] = ldf(r_srel, dv && kt >= 0 ? toff + (uint32_t)((w * S + s) * a.D * 4) + dbytes : kOutOfRange);
+    cdt = ldf(r_cdt, dv && kt >= 0 ? (uint32_t)kt * (uint32_t)(a.D * 4) + dbytes : kOutOfRange);
+  };
+
+  // epilogue of tile kt: sums over the W waves, skip and gate terms, stores
+  auto epilogue = [&](int kt, int slot, int eslot) {
+    const uint32_t row = (uint32_t)(a.D * K::kIo);
+    const uint32_t base = k.chan_off + (uint32_t)(kt * T + w) * row;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int j = w + W * i;
+      float ys = sm.ex[eslot][0][j][0][lane], dxs = sm.ex[eslot][1][j][0][lane], dts = sm.ex[eslot][2][j][0][lane];
+#pragma unroll
+      for (int q = 1; q < W; ++q) {
+        ys += sm.ex[eslot][0][j][q][lane];
+        dxs += sm.ex[eslot][1][j][q][lane];
+        dts += sm.ex[eslot][2][j][q][lane];
+      }
+      const float4 fv = sm.fr[slot][j][lane];
+      const float2 fe = sm.fe[slot][j][lane];
+      const float o = __builtin_fmaf(k.dskip, fv.z, ys);
+      const float du = __builtin_fmaf(k.dskip, fv.w, dxs);
+      const float dvv = dts * fe.x;
+      const uint32_t off = base + (uint32_t)(W * i) * row;
+      Io<IO>::store(du, r_du, off);
+      Io<IO>::store(dvv, r_dd, off);
+      if (want_dz) Io<IO>::store(fe.y * o, r_dz, off);
+      dsk = __builtin_fmaf(fv.w, fv.z, dsk);
+      dbs += dvv;
+    }
+  };
+
+  // one tile: rebuild the start state, recompute the tile's states, reverse
+  auto scan = [&](int kt, int slot, int eslot) {
+    float hh[T][S], ab[T][S], be[T][S];
+    float hst[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) hst[s] = __builtin_fmaf(ex2(k.a2[s] * cdt), hs0[s], srel[s]);
+    load_start(kt - 1);
+    // forward recompute (eq. (2), (3a)) and partial readouts (eq. (3b))
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const float4 fv = sm.fr[slot][j][lane];
+      const float4 b4 = *reinterpret_cast<const float4*>(&sm.bc[slot][j][w][0]);
+      const float bcs[4] = {b4.x, b4.y, b4.z, b4.w};
+      float y = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float x2 = fv.x * k.a2[s];
+        ab[j][s] = ex2(x2);
+        be[j][s] = input_weight(ab[j][s], x2, fv.x, fv.y, k.ka[s], k.ah[s]);
+        const float hp = j == 0 ? hst[s] : hh[j - 1][s];
+        hh[j][s] = __builtin_fmaf(ab[j][s], hp, be[j][s] * (bcs[s] * fv.z));
+        y = __builtin_fmaf(bcs[S + s], hh[j][s], y);
+      }
+      sm.ex[eslot][0][j][w][lane] = y;
+    }
+    // reverse
+    float red[NV];
+#pragma unroll
+    for (int j = T - 1; j >= 0; --j) {
+      const float4 fv = sm.fr[slot][j][lane];
+      const float4 b4 = *reinterpret_cast<const float4*>(&sm.bc[slot][j][w][0]);
+      const float bcs[4] = {b4.x, b4.y, b4.z, b4.w};
+      float dxp = 0.0f, dtp = 0.0f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float Bv = bcs[s], Cv = bcs[S + s];
+        g[s] = __builtin_fmaf(fv.w, Cv, g[s]);          // gradient at h_t
+        red[(j * 2 + 1) * S + s] = fv.w * hh[j][s];     // dC contribution
+        const float gb = g[s] * be[j][s];
+        red[(j * 2) * S + s] = gb * fv.z;               // dB contribution
+        dxp = __builtin_fmaf(gb, Bv, dxp);
+        const float qq = g[s] * (Bv * fv.z);            // gradient at beta_t
+        const float hp = j == 0 ? hst[s] : hh[j - 1][s];
+        const float da = g[s] * hp;                      // gradient at Abar_t
+        dtp = __builtin_fmaf(ab[j][s], __builtin_fmaf(da, k.av[s], qq), dtp);
+        const float x2 = fv.x * k.a2[s];
+        dacc[s] = __builtin_fmaf(da * ab[j][s], fv.x, dacc[s]);
+        dacc[s] = __builtin_fmaf(qq, dbeta_dA(ab[j][s], be[j][s], x2, fv.x, fv.y, k.ka[s]), dacc[s]);
+        g[s] *= ab[j][s];                                // gradient at h_{t-1} through h_t
+      }
+      sm.ex[eslot][1][j][w][lane] = dxp;
+      sm.ex[eslot][2][j][w][lane] = dtp;
+    }
+    // dB, dC: sum over this wave's 64 channels; lane l holds value l >> (6 - log2 NV)
+    const float tot = reduce_scatter<NV>(red, lane);
+    constexpr int SH = NV == 64 ? 0 : (NV == 32 ? 1 : 2);
+    const int v = lane >> SH;
+    const int j = v / (2 * S), qv = (v / S) & 1, s = v % S;
+    const bool owner = (lane & ((1 << SH) - 1)) == 0 && j < k.tile_valid(kt);
+    stf(tot, r_pbc, owner ? (uint32_t)(((kt * T + j) * 2 + qv) * N + w * S + s) * 4u : kOutOfRange);
+  };
+
+  // reverse tile pipeline: iteration for tile kt runs front(kt-1), load(kt-2),
+  // epilogue(kt+1), scan(kt), then the one barrier.  fr/fe/bc rotate over 3
+  // slots and ex over 2 (slot = tile index mod 3 / mod 2).
+  if (nt > 0) {
+    const int last = nt - 1;
+    k.load(r, last);
+    front(last, last % 3);
+    k.load(r, last - 1);
+    load_start(last);
+    __syncthreads();
+    for (int kt = last; kt >= 0; --kt) {
+      const int slot = kt % 3;
+      if (kt > 0) front(kt - 1, (kt - 1) % 3);
+      k.load(r, kt - 2);
+      if (kt < last) epilogue(kt + 1, (kt + 1) % 3, (kt + 1) & 1);
+      scan(kt, slot, kt & 1);
+      __syncthreads();
+    }
+    epilogue(0, 0, 0);
+  }
+
+  // per-item partials: dA over this chunk, dDskip and bias sums over the waves' tokens
+  if (dv) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) a.pA[((size_t)bg * N + w * S + s) * a.D + k.d] = dacc[s];
+  }
+  __syncthreads();
+  float* red2 = &sm.ex[0][0][0][0][0];
+  red2[w * 64 + lane] = dsk;
+  red2[(W + w) * 64 + lane] = dbs;
+  __syncthreads();
+  if (w == 0 && dv) {
+    float t0s = 0.0f, t1s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      t0s += red2[q * 64 + lane];
+      t1s += red2[(W + q) * 64 + lane];
+    }
+    a.pD[((size_t)bg * 2 + 0) * a.D + k.d] = t0s;
+    a.pD[((size_t)bg * 2 + 1) * a.D + k.d] = t1s;
+  }
+  if (k.g == 0 && a.dh0 && dv) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) a.dh0[((size_t)k.b * a.D + k.d) * N + w * S + s] = g[s];
+  }
+}
+
+// ---------------------------------------------------------------- pass 4: reductions
+
+template <typename IO, int N>
+__global__ void bwd_reduce_bc_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, q, n)
+  const int64_t total = a.batch * a.L * 2 * N;
+  if (i >= total) return;
+  const int64_t per_b = a.L * 2 * N;
+  const int64_t b = i / per_b;
+  const int64_t rest = i - b * per_b;
+  const int64_t t = rest / (2 * N);
+  const int q = (int)((rest / N) & 1);
+  const int n = (int)(rest % N);
+  const float* p = a.pbc + (size_t)b * a.nblk * per_b + rest;
+  float acc = 0.0f;
+  for (int k = 0; k < a.nblk; ++k) acc += p[(size_t)k * per_b];
+  IO* dst = static_cast<IO*>(q == 0 ? a.dB : a.dC);
+  store_io(dst, (size_t)(b * a.L + t) * N + n, acc);
+}
+
+template <int N>
+__global__ void bwd_reduce_param_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (n, d) for dA, then d for the vectors
+  const int64_t nbg = a.batch * a.nchunks;
+  if (i < (int64_t)N * a.D) {
+    const int64_t n = i / a.D, d = i % a.D;
+    float acc = 0.0f;
+    for (int64_t k = 0; k < nbg; ++k) acc += a.pA[(size_t)(k * N + n) * a.D + d];
+    a.dA[d * N + n] = acc;
+  } else if (i < (int64_t)N * a.D + a.D) {
+    const int64_t d = i - (int64_t)N * a.D;
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int64_t k = 0; k < nbg; ++k) {
+      s0 += a.pD[(size_t)(k * 2 + 0) * a.D + d];
+      s1 += a.pD[(size_t)(k * 2 + 1) * a.D + d];
+    }
+    if (a.dDskip) a.dDskip[d] = s0;
+    if (a.dbias) a.dbias[d] = s1;
+  }
+}
+
+// L = 0 (or an empty batch): parameter gradients are zero, dh0 = dlast.
+template <int N>
+__global__ void bwd_empty_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (int64_t)N * a.D) a.dA[i] = 0.0f;
+  if (i < a.D) {
+    if (a.dDskip) a.dDskip[i] = 0.0f;
+    if (a.dbias) a.dbias[i] = 0.0f;
+  }
+  if (a.dh0 && i < a.batch * a.D * N) a.dh0[i] = a.dlast ? a.dlast[i] : 0.0f;
+}
+
+unsigned blocks_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+template <typename IO, int N, int W>
+hipError_t launch_bwd_t(const BwdArgs& a0, hipStream_t st) {
+  constexpr int T = kBwdTile;
+  BwdArgs a = a0;
+  if (a.batch == 0 || a.D == 0 || a.L == 0) {
+    const int64_t n = a.batch * a.D * N > (int64_t)N * a.D ? a.batch * a.D * N : (int64_t)N * a.D;
+    if (n > 0) hipLaunchKernelGGL((bwd_empty_kernel<N>), dim3(blocks_for(n, 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  const unsigned items = (unsigned)(a.batch * a.nchunks * a.nblk);
+  hipLaunchKernelGGL((bwd_aggregate_kernel<IO, N, W, T>), dim3(items), dim3(64 * W), 0, st, a);
+  hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(blocks_for(a.batch * N * a.D, 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_main_kernel<IO, N, W, T>), dim3(items), dim3(64 * W), 0, st, a);
+  hipLaunchKernelGGL((bwd_reduce_bc_kernel<IO, N>), dim3(blocks_for(a.batch * a.L * 2 * N, 256)), dim3(256), 0, st,
+                     a);
+  hipLaunchKernelGGL((bwd_reduce_param_kernel<N>), dim3(blocks_for((int64_t)N * a.D + a.D, 256)), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_bwd_io(const BwdArgs& a, int N, hipStream_t st) {
+  switch (N) {
+    case 16: return launch_bwd_t<IO, 16, 8>(a, st);
+    case 8: return launch_bwd_t<IO, 8, 4>(a, st);
+    case 4: return launch_bwd_t<IO, 4, 2>(a, st);
+    case 2: return launch_bwd_t<IO, 2, 1>(a, st);
+    case 1: return launch_bwd_t<IO, 1, 1>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  BwdPlan p{};
+  const int64_t T = kBwdTile;
+  p.nblk = (int32_t)((D + 63) / 64);
+  if (batch <= 0 || L <= 0 || D <= 0) return p;
+  // Chunks of 512 tokens, shorter when that leaves fewer than ~4 work items per CU.
+  int64_t K = 512;
+  const int64_t units = batch * p.nblk;
+  while (K > 64 && units * ((L + K - 1) / K) < 1024) K /= 2;
+  const int64_t Lr = (L + T - 1) / T * T;
+  if (K > Lr) K = Lr;
+  if (const char* v = std::getenv("MAMBA_MI355X_BWD_CHUNK")) {
+    const long c = std::atol(v);
+    if (c >= T && c % T == 0) K = c;
+  }
+  // every per-chunk buffer (token rows, tile-start states) must span < 2^31 bytes
+  const int64_t cap_tok = ((int64_t(1) << 31) - 1) / (D * 4) / T * T;
+  const int64_t cap_st = ((int64_t(1) << 31) - 1) / (N * D * 4) * T;
+  if (K > cap_tok) K = cap_tok;
+  if (K > cap_st) K = cap_st;
+  if (K < T) K = T;
+  p.chunk_len = K;
+  p.nchunks = (int32_t)((L + K - 1) / K);
+  p.tpc = (int32_t)(K / T);
+  const size_t bgd = (size_t)batch * p.nchunks * D;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  p.off_hs = off;   off += al(bgd * N * 4);
+  p.off_gq = off;   off += al(bgd * N * 4);
+  p.off_sdt = off;  off += al(bgd * 4);
+  p.off_srel = off; off += al(bgd * p.tpc * N * 4);
+  p.off_cdt = off;  off += al(bgd * p.tpc * 4);
+  p.off_pbc = off;  off += al((size_t)batch * p.nblk * L * 2 * N * 4);
+  p.off_pA = off;   off += al(bgd * N * 4);
+  p.off_pD = off;   off += al(bgd * 2 * 4);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int io, int N, hipStream_t st) {
+  return io == kIoBF16 ? launch_bwd_io<uint16_t>(a, N, st) : launch_bwd_io<float>(a, N, st);
+}
+
+}  // namespace s6

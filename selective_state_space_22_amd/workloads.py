@@ -219,6 +219,26 @@ def generate(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32", se
     return inp
 
 
+@dataclasses.dataclass
+class GradInputs:
+    """Upstream gradients for the backward: dout (batch, L, D) in the I/O type, dlast (batch, D, N) float32."""
+    dout: np.ndarray
+    dlast: np.ndarray | None
+
+
+def grad_inputs(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32", seed: int = SEED_BASE,
+                with_dlast: bool = True) -> GradInputs:
+    """Seeded upstream gradients, dout ~ N(0, 1) and dlast ~ N(0, 1), from their own
+    streams (SeedSequence(seed + 500000).spawn(2)); bf16 dout is rounded once (RNE)."""
+    seqs = np.random.SeedSequence(seed + 500_000).spawn(2)
+    dout = _fill(seqs[0], (batch, seqlen, dim), "normal")
+    if io == "bf16":
+        _, widened = bf16_round(dout)
+        dout = widened.reshape(dout.shape)
+    dlast = _fill(seqs[1], (batch, dim, dstate), "normal") if with_dlast else None
+    return GradInputs(dout, dlast)
+
+
 def generate_workload(name: str) -> ScanInputs:
     """The seeded inputs of a named workload (decode: the 64 tokens as one (B, 64, D) block)."""
     w = WORKLOADS[name]

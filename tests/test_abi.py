@@ -31,8 +31,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mamba_scan_fwd", "mamba_scan_fwd_workspace_size", "mamba_state_update",
-                                    "mamba_status_string", "mamba_version"]
+    assert declared_functions() == ["mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
+                                    "mamba_scan_fwd_workspace_size", "mamba_state_update", "mamba_status_string",
+                                    "mamba_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -135,3 +136,45 @@ def test_python_binding_refuses_cpu_tensors(lib):
     u = torch.zeros(1, 4, 64)
     with pytest.raises((ValueError, TypeError)):
         binding.mamba_scan_fwd(u, u, torch.zeros(64, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+
+
+def bwd_call(lib, batch=1, L=8, D=64, N=16, io=0, u=FAKE, delta=FAKE, bias=None, A=FAKE, B=FAKE, C=FAKE,
+             Dskip=None, z=None, h0=None, dout=FAKE, dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE,
+             dDskip=None, dz=None, dbias=None, dh0=None, ws=None, ws_bytes=0):
+    return lib.mamba_scan_bwd(batch, L, D, N, io, u, delta, bias, A, B, C, Dskip, z, 1, h0, dout, dlast, du, ddelta,
+                              dA, dB, dC, dDskip, dz, dbias, dh0, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size(lib):
+    ws = binding.mamba_scan_bwd_workspace_size
+    # per-chunk carries, tile-start states every 8 tokens and per-block dB/dC partials
+    batch, L, D, N = 4, 4096, 5120, 16
+    w = ws(batch, L, D, N, 1)
+    assert w == ws(batch, L, D, N, 1)
+    tile_states = batch * (L // 8) * D * N * 4
+    partials = batch * (D // 64) * L * 2 * N * 4
+    assert tile_states + partials < w < 1.2 * (tile_states + partials)
+    assert ws(1, 0, 64, 16, 0) == 0
+    assert ws(1, 16, 64, 3, 0) == 0 and ws(1, 16, 64, 16, 9) == 0
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC"])
+def test_bwd_rejects_null_required_pointer(lib, field):
+    need = binding.mamba_scan_bwd_workspace_size(1, 8, 64, 16, 0)
+    assert bwd_call(lib, N=5, ws=FAKE, ws_bytes=need, **{field: None}) == ERR_UNSUPPORTED
+    assert bwd_call(lib, ws=FAKE, ws_bytes=need, **{field: None}) == ERR_NULL
+
+
+def test_bwd_rejects_misaligned_pointers_and_small_workspace(lib):
+    need = binding.mamba_scan_bwd_workspace_size(1, 8, 64, 16, 0)
+    for field in ("u", "delta", "A", "B", "C", "dout", "du", "ddelta", "dA", "dB", "dC", "bias", "Dskip", "z", "h0",
+                  "dlast", "dDskip", "dz", "dbias", "dh0"):
+        assert bwd_call(lib, ws=FAKE, ws_bytes=need, **{field: FAKE + 4}) == ERR_ALIGN, field
+    assert bwd_call(lib) == ERR_WORKSPACE
+    assert bwd_call(lib, ws=FAKE, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert bwd_call(lib, io=3) == ERR_DTYPE and bwd_call(lib, L=-1) == ERR_DIM
+
+
+def test_bwd_empty_channel_dimension_is_a_no_op(lib):
+    assert bwd_call(lib, D=0, u=None, delta=None, A=None, B=None, C=None, dout=None, du=None, ddelta=None, dA=None,
+                    dB=None, dC=None) == OK

@@ -1,0 +1,260 @@
+"""Parity of the HIP backward (mamba_scan_bwd, through the C ABI) with the fp64
+oracle backward, on the GPU.
+
+Every gradient is compared element by element with parity_error (max |g - r|
+over max(|r|, rms(r))).  Tolerances: the elementwise gradients (du, ddelta,
+dz, dh0) and the channel or token sums (dB, dC, dA, dDskip, dbias) are held to
+the forward's bounds, 1e-4 for fp32 I/O and 2e-2 for bf16 I/O, except that the
+sums get 5e-4 in fp32: they add up to 16 k (tokens) or 5 k (channels) fp32
+terms of both signs, and a sum that cancels to a small value keeps the
+absolute rounding error of its terms (about sqrt(n) * 2^-24 of their size).
+
+Full-size workloads are run whole on the GPU; the oracle covers every batch
+row and channel where that takes seconds, otherwise a subset whose gradients
+it can compute exactly (channels are independent SSMs; dB and dC of a batch
+row need all of its channels, dA, dDskip and dbias of a channel need all of
+its batch rows)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import parity_error, to_device, to_host, torch_io
+from selective_state_space_22_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ELEMENTWISE = ("du", "ddelta", "dz", "dh0")
+SUMS = ("dA", "dB", "dC", "dDskip", "dbias")
+TOL_BWD = {"f32": {**{k: 1e-4 for k in ELEMENTWISE}, **{k: 5e-4 for k in SUMS}},
+           "bf16": {k: 2e-2 for k in ELEMENTWISE + SUMS}}
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _announce(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+def gpu_bwd(inp, gi, h0=None, softplus=None, dev=None):
+    from selective_state_space_22_amd import mamba_scan_bwd
+
+    d = dev or to_device(inp)
+    dout = torch_io(gi.dout, inp.io, "cuda")
+    dlast = None if gi.dlast is None else torch.from_numpy(np.ascontiguousarray(gi.dlast, np.float32)).cuda()
+    h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, np.float32)).cuda()
+    g = mamba_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["delta_bias"], d["Dskip"], d["z"],
+                       inp.softplus if softplus is None else softplus, h0t, dlast)
+    torch.cuda.synchronize()
+    out = {k: to_host(v) for k, v in g.items()}
+    out["dbias"] = out.pop("ddelta_bias")
+    return out
+
+
+def oracle_bwd(inp, gi, h0=None, softplus=None):
+    """Oracle gradients; absent bias / Dskip / h0 enter as zeros so that their
+    gradients are defined (the forward is the same)."""
+    D, N = inp.dim, inp.dstate
+    bias = inp.delta_bias if inp.delta_bias is not None else np.zeros(D)
+    dsk = inp.Dskip if inp.Dskip is not None else np.zeros(D)
+    h0v = h0 if h0 is not None else np.zeros((inp.batch, D, N))
+    return oracle.scan_bwd(inp.u, inp.delta, inp.A, inp.B, inp.C, gi.dout, bias, dsk, inp.z,
+                           inp.softplus if softplus is None else softplus, h0v, gi.dlast)
+
+
+def compare(got, ref, io, label, keys=None):
+    tol = TOL_BWD[io]
+    errs = {}
+    for k in keys or sorted(ref):
+        if k not in got:
+            continue
+        assert got[k].shape == ref[k].shape, f"{label} {k}: shape {got[k].shape} vs {ref[k].shape}"
+        assert np.isfinite(got[k]).all(), f"{label} {k}: non-finite values"
+        errs[k] = parity_error(got[k], ref[k])
+    print(f"{label}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if v > tol[k]}
+    assert not bad, f"{label}: over tolerance {bad}"
+    return errs
+
+
+class chunk_len:
+    """Force the backward's chunk length (plan override read at every call)."""
+
+    def __init__(self, k):
+        self.k = k
+
+    def __enter__(self):
+        self.old = os.environ.get("MAMBA_MI355X_BWD_CHUNK")
+        if self.k is not None:
+            os.environ["MAMBA_MI355X_BWD_CHUNK"] = str(self.k)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("MAMBA_MI355X_BWD_CHUNK", None)
+        else:
+            os.environ["MAMBA_MI355X_BWD_CHUNK"] = self.old
+
+
+def run_case(batch, L, D, N, io, seed, chunk=None, h0=False, dlast=True, gate=True, skip=True, bias=True,
+             softplus=True, label=""):
+    inp = W.generate(batch, L, D, N, io, seed=seed, with_z=gate, with_dskip=skip, with_bias=bias)
+    if not softplus:  # raw dt used as is: keep it positive and moderate
+        inp.delta = np.random.default_rng(seed).uniform(1e-3, 0.2, inp.delta.shape).astype(np.float32)
+        if io == "bf16":
+            inp.delta = W.bf16_round(inp.delta)[1].reshape(inp.delta.shape)
+    gi = W.grad_inputs(batch, L, D, N, io, seed=seed, with_dlast=dlast)
+    h0v = np.random.default_rng(seed + 7).standard_normal((batch, D, N)).astype(np.float32) if h0 else None
+    with chunk_len(chunk):
+        got = gpu_bwd(inp, gi, h0=h0v, softplus=softplus)
+    ref = oracle_bwd(inp, gi, h0=h0v, softplus=softplus)
+    if not gate:
+        assert "dz" not in got
+    return compare(got, ref, io, label or f"({batch},{L},{D},{N}) {io}")
+
+
+def test_tiny_workload_full():
+    _need_gpu()
+    _announce("backward, tiny workload (1, 256, 64, 16) fp32")
+    run_case(1, 256, 64, 16, "f32", seed=W.SEED_BASE, label="tiny")
+
+
+@pytest.mark.parametrize("case", [
+    dict(batch=2, L=77, D=100, N=16, io="f32", chunk=16),        # ragged L and D, 5 chunks, last one partial
+    dict(batch=2, L=77, D=100, N=16, io="f32", chunk=16, h0=True),
+    dict(batch=3, L=300, D=130, N=16, io="f32", chunk=64, h0=True),
+    dict(batch=1, L=1, D=64, N=16, io="f32"),
+    dict(batch=2, L=7, D=65, N=16, io="f32"),
+    dict(batch=2, L=8, D=64, N=16, io="f32", dlast=False),
+    dict(batch=2, L=50, D=70, N=8, io="f32", chunk=16),
+    dict(batch=2, L=50, D=70, N=4, io="f32", chunk=24),
+    dict(batch=2, L=50, D=70, N=2, io="f32", chunk=8),
+    dict(batch=2, L=50, D=70, N=1, io="f32", chunk=32),
+    dict(batch=2, L=200, D=96, N=16, io="f32", gate=False),
+    dict(batch=2, L=200, D=96, N=16, io="f32", skip=False, bias=False),
+    dict(batch=2, L=200, D=96, N=16, io="f32", softplus=False, bias=False, h0=True),
+    dict(batch=2, L=600, D=200, N=16, io="bf16", chunk=128, h0=True),
+    dict(batch=2, L=333, D=128, N=8, io="bf16", chunk=64),
+], ids=lambda c: ",".join(f"{k}={v}" for k, v in c.items()))
+def test_edge_cases(case):
+    _need_gpu()
+    _announce(f"backward edge case {case}")
+    run_case(seed=W.SEED_BASE + 100 + case["L"] + case["N"], **case)
+
+
+def test_empty_sequence():
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_scan_bwd
+
+    _announce("backward, seqlen 0")
+    D, N = 64, 16
+    e = torch.empty((2, 0, D), device="cuda")
+    eb = torch.empty((2, 0, N), device="cuda")
+    A = -torch.ones((D, N), device="cuda")
+    dl = torch.randn((2, D, N), device="cuda")
+    g = mamba_scan_bwd(e, e, A, eb, eb, e, None, torch.ones(D, device="cuda"), None, True, None, dl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dl)
+    assert not g["dA"].any() and not g["dDskip"].any() and not g["ddelta_bias"].any()
+
+
+def test_repeat_calls_are_bit_identical():
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_scan_bwd
+
+    _announce("backward determinism (3, 700, 300, 16) bf16")
+    inp = W.generate(3, 700, 300, 16, "bf16", seed=77)
+    gi = W.grad_inputs(3, 700, 300, 16, "bf16", seed=77)
+    d = to_device(inp)
+    dout = torch_io(gi.dout, "bf16", "cuda")
+    dl = torch.from_numpy(gi.dlast).cuda()
+    with chunk_len(128):
+        a = mamba_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["delta_bias"], d["Dskip"], d["z"], True,
+                           None, dl)
+        b = mamba_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["delta_bias"], d["Dskip"], d["z"], True,
+                           None, dl)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_chunking_does_not_change_the_gradients_beyond_rounding():
+    """The same problem cut into 1, 4 and 16 chunks (carries through the aggregates)."""
+    _need_gpu()
+    _announce("backward chunk-count invariance (2, 1024, 128, 16) fp32")
+    inp = W.generate(2, 1024, 128, 16, "f32", seed=91)
+    gi = W.grad_inputs(2, 1024, 128, 16, "f32", seed=91)
+    ref = oracle_bwd(inp, gi)
+    for k in (1024, 256, 64):
+        with chunk_len(k):
+            got = gpu_bwd(inp, gi)
+        compare(got, ref, "f32", f"chunk {k}")
+
+
+def test_mamba130m_layer_full():
+    """Whole workload on the GPU, every gradient against the full oracle."""
+    _need_gpu()
+    _announce("backward, mamba130m_layer (8, 2048, 1536, 16) bf16, full comparison")
+    inp = W.generate_workload("mamba130m_layer")
+    gi = W.grad_inputs(inp.batch, inp.seqlen, inp.dim, inp.dstate, inp.io, seed=W.WORKLOADS["mamba130m_layer"].seed)
+    got = gpu_bwd(inp, gi)
+    ref = oracle_bwd(inp, gi)
+    compare(got, ref, "bf16", "mamba130m_layer")
+
+
+def test_mamba3b_layer_sampled():
+    """Whole workload on the GPU.  Oracle: batch row 0 with all channels (every
+    per-token gradient of that row, its dB and dC, its dh0) and all batch rows
+    for 128 sampled channels (their dA, dDskip, dbias)."""
+    _need_gpu()
+    _announce("backward, mamba3b_layer (4, 4096, 5120, 16) bf16, sampled comparison")
+    inp = W.generate_workload("mamba3b_layer")
+    gi = W.grad_inputs(inp.batch, inp.seqlen, inp.dim, inp.dstate, inp.io, seed=W.WORKLOADS["mamba3b_layer"].seed)
+    got = gpu_bwd(inp, gi)
+    # batch row 0, all channels
+    row = W.channel_subset(inp, [0], np.arange(inp.dim))
+    gr = W.GradInputs(np.ascontiguousarray(gi.dout[:1]), np.ascontiguousarray(gi.dlast[:1]))
+    ref = oracle_bwd(row, gr)
+    sub = {k: got[k][:1] for k in ("du", "ddelta", "dz", "dB", "dC", "dh0")}
+    compare(sub, ref, "bf16", "mamba3b_layer row 0", keys=("du", "ddelta", "dz", "dB", "dC", "dh0"))
+    # all rows, sampled channels
+    ch = np.arange(0, inp.dim, 40)
+    part = W.channel_subset(inp, np.arange(inp.batch), ch)
+    gp = W.GradInputs(np.ascontiguousarray(gi.dout[:, :, ch]), np.ascontiguousarray(gi.dlast[:, ch]))
+    ref = oracle_bwd(part, gp)
+    sub = {"dA": got["dA"][ch], "dDskip": got["dDskip"][ch], "dbias": got["dbias"][ch]}
+    compare(sub, ref, "bf16", "mamba3b_layer 128 channels", keys=("dA", "dDskip", "dbias"))
+
+
+def test_long_sequence_with_resets_full():
+    """A long fp32 sequence with 1 % reset tokens (many chunks, carries across
+    resets), every gradient against the full oracle."""
+    _need_gpu()
+    _announce("backward, (1, 65536, 256, 16) fp32 with resets, full comparison")
+    inp = W.generate(1, 65536, 256, 16, "f32", seed=W.WORKLOADS["million_tokens"].seed, reset_frac=0.01)
+    gi = W.grad_inputs(1, 65536, 256, 16, "f32", seed=5)
+    got = gpu_bwd(inp, gi)
+    ref = oracle_bwd(inp, gi)
+    compare(got, ref, "f32", "65536 tokens with resets")
+
+
+def test_million_tokens_sampled():
+    """The million-token workload whole on the GPU; the oracle on 16 of its 256
+    channels (every gradient of those channels except dB and dC, which need all
+    channels and are covered by the 65536-token case above)."""
+    _need_gpu()
+    _announce("backward, million_tokens (1, 1048576, 256, 16) fp32, 16 sampled channels")
+    inp = W.generate_workload("million_tokens")
+    gi = W.grad_inputs(inp.batch, inp.seqlen, inp.dim, inp.dstate, inp.io, seed=W.WORKLOADS["million_tokens"].seed)
+    got = gpu_bwd(inp, gi)
+    ch = np.arange(3, inp.dim, 16)
+    part = W.channel_subset(inp, [0], ch)
+    gp = W.GradInputs(np.ascontiguousarray(gi.dout[:, :, ch]), np.ascontiguousarray(gi.dlast[:, ch]))
+    ref = oracle_bwd(part, gp)
+    sub = {"du": got["du"][:, :, ch], "ddelta": got["ddelta"][:, :, ch], "dz": got["dz"][:, :, ch],
+           "dh0": got["dh0"][:, ch], "dA": got["dA"][ch], "dDskip": got["dDskip"][ch], "dbias": got["dbias"][ch]}
+    compare(sub, ref, "f32", "million_tokens 16 channels", keys=tuple(sub))
