@@ -26,6 +26,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 VALU_FP32_PEAK_TFLOPS = 78.6    # 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz, non-packed fp32
 VALU_FP32_PACKED_TFLOPS = 157.3  # published fp32 vector peak (packed fp32, not used by this code)
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak, published
+MFMA_F32_PEAK_TFLOPS = 157.3     # dense fp32 matrix peak, published
 # Algorithmic fp32 operations (FMA = 2, other ops and transcendentals = 1):
 FLOPS_PER_ELEMENT = 9.0          # per (b, l, d, n): dt*A, exp, input weight, *B, *x, h FMA, readout FMA
 FLOPS_PER_TOKEN_CHANNEL = 15.0   # per (b, l, d): bias add, softplus (6), skip FMA, SiLU (5), gate mul
@@ -145,8 +147,10 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="fwd: mamba_scan_fwd (the headline); bwd: mamba_scan_bwd on the same workload")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "sel", "ssm"], default="fwd",
+                    help="fwd: mamba_scan_fwd (the headline); bwd: mamba_scan_bwd on the same workload; "
+                         "sel: the selection projections (mamba_selection_fwd, dt rank d_model/16); "
+                         "ssm: selection then scan (mamba_ssm_fwd)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -171,8 +175,8 @@ def main():
         calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
         return
     w = W.WORKLOADS[args.workload]
-    if args.which == "bwd" and w.decode_steps > 0:
-        print("bench.py: --pass bwd applies to the full-sequence workloads, not decode", file=sys.stderr)
+    if args.which != "fwd" and w.decode_steps > 0:
+        print("bench.py: --pass bwd/sel/ssm apply to the full-sequence workloads, not decode", file=sys.stderr)
         sys.exit(2)
     inp = W.generate_workload(args.workload)
     tdt = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -228,6 +232,37 @@ def main():
         bytes_per_step = (4 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
                           + 3 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
                           + 8 * w.dim * w.dstate + 16 * w.dim + 8 * w.batch * w.dim * w.dstate)
+    elif args.which in ("sel", "ssm"):
+        R = W.dt_rank_for(w.dim)
+        sw = W.selection_weights(w.dim, w.dstate, R, w.io, seed=w.seed)
+        wx, wdt = t(sw.W_x), t(sw.W_dt)
+        M = w.batch * w.seqlen
+        if args.which == "sel":
+            sel_out = (torch.empty_like(u), torch.empty_like(B), torch.empty_like(C))
+            ws = torch.empty(max(binding.mamba_selection_fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, R,
+                                                                            1 if w.io == "bf16" else 0), 1),
+                             dtype=torch.uint8, device=dev)
+
+            def step():
+                binding.mamba_selection_fwd(u, wx, wdt, w.dstate, *sel_out, workspace=ws)
+
+            units = M * w.dim  # output elements of delta
+            bytes_per_step = io_bytes * (2 * M * w.dim + (R + 2 * w.dstate) * w.dim + w.dim * R + 2 * M * w.dstate)
+            sel_flops = 2.0 * M * w.dim * (R + 2 * w.dstate) + 2.0 * M * R * w.dim
+        else:
+            out = torch.empty_like(u)
+            last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(binding.mamba_ssm_fwd_workspace_size(w.batch, w.seqlen, w.dim, w.dstate, R,
+                                                                      1 if w.io == "bf16" else 0), 1),
+                             dtype=torch.uint8, device=dev)
+
+            def step():
+                binding.mamba_ssm_fwd(u, wx, wdt, A, z=z, dt_bias=bias, Dskip=dskip, out=out, last_state=last,
+                                      workspace=ws)
+
+            units = w.elements
+            bytes_per_step = (3 * io_bytes * M * w.dim + io_bytes * ((R + 2 * w.dstate) * w.dim + w.dim * R)
+                              + 8 * w.dim + 4 * w.dim * w.dstate + 4 * w.batch * w.dim * w.dstate)
     else:
         out = torch.empty_like(u)
         last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
@@ -289,7 +324,13 @@ def main():
         # per (b, l, d, n): forward recompute (9) as above plus the reverse step (~20 fp32 ops, FMA = 2)
         flops = units * (FLOPS_PER_ELEMENT + BWD_FLOPS_PER_ELEMENT) + (units / w.dstate) * 30.0
         tflops = flops / (ms * 1e-3) / 1e12
-    if decode:
+    if args.which == "sel":
+        peak = MFMA_BF16_PEAK_TFLOPS if w.io == "bf16" else MFMA_F32_PEAK_TFLOPS
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "mfma_tflops": round(sel_flops / (ms * 1e-3) / 1e12, 2), "mfma_peak": peak,
+                "note": "two GEMMs of arithmetic intensity below the MFMA/HBM ridge: HBM-bound"}
+    elif decode:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": bytes_per_step // L}
@@ -300,8 +341,10 @@ def main():
                 "note": "fp32 VALU without packed-fp32 instructions; frac vs the packed 157.3 TFLOP/s "
                         f"figure: {tflops / VALU_FP32_PACKED_TFLOPS:.4f}"}
     rec = {
-        "metric": metric_name() if args.which == "fwd" else
-        "selective-scan bwd elements(B*L*D*N)/s (all gradients, states recomputed)",
+        "metric": {"fwd": metric_name(),
+                   "bwd": "selective-scan bwd elements(B*L*D*N)/s (all gradients, states recomputed)",
+                   "sel": "selection projections: delta elements (B*L*D)/s (x_proj + dt_proj GEMMs)",
+                   "ssm": "selective SSM from x: elements(B*L*D*N)/s (selection GEMMs + scan)"}[args.which],
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,
@@ -322,7 +365,7 @@ def main():
         "algorithmic_bytes_per_step": bytes_per_step,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.which in ("fwd", "bwd"):
         rec["cpu_baseline"] = cpu_baseline(inp, args.workload, args.which)
     print(json.dumps(rec), flush=True)
 

@@ -162,6 +162,48 @@ int mamba_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    float* dDskip, void* dz, float* ddelta_bias, float* dh0,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Selection front end (section 3.2: B_t = Linear_N(x_t), C_t = Linear_N(x_t),
+ * and dt from a projection of x_t of size dt_rank expanded to the D channels;
+ * the page's form Broadcast_D(Linear_1(x)) is dt_rank = 1 with W_dt = ones).
+ * With M = batch * seqlen token rows:
+ *   xdbl  = x W_x^T                    (M, dt_rank + 2*dstate), kept in the workspace
+ *   B     = xdbl[:, dt_rank : dt_rank + dstate]
+ *   C     = xdbl[:, dt_rank + dstate :]
+ *   delta = xdbl[:, :dt_rank] W_dt^T   (raw: the scan adds delta_bias and the softplus)
+ *   x            : (batch, seqlen, dim)              I/O type
+ *   W_x          : (dt_rank + 2*dstate, dim)         I/O type (rows = output features)
+ *   W_dt         : (dim, dt_rank)                    I/O type
+ *   delta        : (batch, seqlen, dim)              I/O type, written
+ *   B, C         : (batch, seqlen, dstate)           I/O type, written
+ *   workspace    : at least mamba_selection_fwd_workspace_size() bytes (xdbl,
+ *                  in the I/O type, as a framework would keep it).
+ * Products accumulate in fp32 on the matrix cores (bf16 or fp32 MFMA); rows
+ * that are not 16-byte aligned take a slower vector path.  dt_rank >= 1.
+ */
+size_t mamba_selection_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                          int64_t dt_rank, int io_dtype);
+int mamba_selection_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank, int io_dtype,
+                        const void* x, const void* W_x, const void* W_dt, void* delta, void* B, void* C,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Selective SSM from the token features alone: mamba_selection_fwd followed
+ * by mamba_scan_fwd with u = x, delta/B/C from the selection (in the
+ * workspace), dt = softplus(delta + dt_bias) when delta_softplus is set.
+ *   x, z, out    : (batch, seqlen, dim) I/O type (z nullable: no gate)
+ *   W_x, W_dt    : as for mamba_selection_fwd
+ *   dt_bias, Dskip (dim), A (dim, dstate), h0 and last_state (batch, dim,
+ *   dstate): float, as for mamba_scan_fwd (dt_bias, Dskip, h0, last_state nullable)
+ *   workspace    : at least mamba_ssm_fwd_workspace_size() bytes.
+ */
+size_t mamba_ssm_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank,
+                                    int io_dtype);
+int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank, int io_dtype,
+                  const void* x, const void* z, const void* W_x, const void* W_dt, const float* dt_bias,
+                  const float* A, const float* Dskip, int delta_softplus, const float* h0,
+                  void* out, float* last_state, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,9 @@ Two independent implementations of the same definition live here:
   * ``scan_numpy``: a numpy fp64 twin vectorised over (batch, channel, state)
     with a Python loop over tokens, used to cross-check the C code;
   * ``scan_bwd``: the C oracle's backward, the derivative of the same
-    definition, pinned against central finite differences of ``scan``.
+    definition, pinned against central finite differences of ``scan``;
+  * ``selection``: the section 3.2 projections (B, C = Linear_N(x), dt from a
+    rank-R projection of x expanded to the D channels), fp64 matrix products.
 Both follow "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
 section 2.1 eq. (2) (ZOH), eq. (3a)/(3b) (recurrence and readout),
 section 3.2 (selection: per-token dt through softplus, B/C shared by channels)
@@ -179,3 +181,23 @@ def scan_numpy(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=
             y = y * (zt / (1.0 + np.exp(-zt)))
         out[:, t, :] = y
     return out, h
+
+
+def selection(x, W_x, W_dt, dstate, store=None):
+    """fp64 selection projections (section 3.2).  x (batch, L, D), W_x (R + 2N, D),
+    W_dt (D, R).  Returns (delta_raw (batch, L, D), B (batch, L, N), C (batch, L, N)):
+    xdbl = x W_x^T; B, C = its columns R..R+N and R+N..R+2N; delta = xdbl[:, :R] W_dt^T.
+
+    ``store`` (optional) maps an fp64 array to the values of the type the
+    projected tensors are kept in (xdbl before the dt projection, and the three
+    results); None keeps fp64 throughout."""
+    keep = store if store is not None else (lambda a: a)
+    x = np.asarray(x, np.float64)
+    W_x = np.asarray(W_x, np.float64)
+    W_dt = np.asarray(W_dt, np.float64)
+    R = W_dt.shape[1]
+    N = int(dstate)
+    assert W_x.shape == (R + 2 * N, x.shape[-1]) and W_dt.shape == (x.shape[-1], R)
+    xdbl = keep(x @ W_x.T)
+    delta = keep(xdbl[..., :R] @ W_dt.T)
+    return delta, np.ascontiguousarray(xdbl[..., R:R + N]), np.ascontiguousarray(xdbl[..., R + N:])

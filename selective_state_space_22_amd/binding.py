@@ -51,6 +51,14 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_scan_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mamba_scan_bwd.argtypes = [I64, I64, I64, I64, I] + [P] * 8 + [I, P, P, P] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.mamba_scan_bwd.restype = I
+    lib.mamba_selection_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.mamba_selection_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_selection_fwd.argtypes = [I64, I64, I64, I64, I64, I, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.mamba_selection_fwd.restype = I
+    lib.mamba_ssm_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.mamba_ssm_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_ssm_fwd.argtypes = [I64, I64, I64, I64, I64, I, P, P, P, P, P, P, P, I, P, P, P, P, ctypes.c_size_t, P]
+    lib.mamba_ssm_fwd.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -213,3 +221,70 @@ def mamba_scan_bwd(u, delta, A, B, C, dout, delta_bias=None, Dskip=None, z=None,
     if st != 0:
         raise MambaError("mamba_scan_bwd", st)
     return {k: g[k] for k in need}
+
+
+def mamba_selection_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype) -> int:
+    return int(load_library().mamba_selection_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype))
+
+
+def mamba_selection_fwd(x, W_x, W_dt, dstate, delta=None, B=None, C=None, workspace=None):
+    """Selection projections: x (batch, L, D); W_x (R + 2N, D); W_dt (D, R).
+
+    Returns (delta (batch, L, D), B (batch, L, N), C (batch, L, N)) in x's dtype."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = x.shape
+    N = int(dstate)
+    R = W_dt.shape[1]
+    io = _io_dtype(x)
+    dev = x.device
+    delta = torch.empty_like(x) if delta is None else delta
+    B = torch.empty((batch, L, N), dtype=x.dtype, device=dev) if B is None else B
+    C = torch.empty((batch, L, N), dtype=x.dtype, device=dev) if C is None else C
+    ws_bytes = mamba_selection_fwd_workspace_size(batch, L, D, N, R, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.mamba_selection_fwd(
+        batch, L, D, N, R, io, _ptr(x, "x", x.dtype, (batch, L, D), dev), _ptr(W_x, "W_x", x.dtype, (R + 2 * N, D), dev),
+        _ptr(W_dt, "W_dt", x.dtype, (D, R), dev), _ptr(delta, "delta", x.dtype, (batch, L, D), dev),
+        _ptr(B, "B", x.dtype, (batch, L, N), dev), _ptr(C, "C", x.dtype, (batch, L, N), dev),
+        _ptr(workspace, "workspace", device=dev),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_selection_fwd", st)
+    return delta, B, C
+
+
+def mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype) -> int:
+    return int(load_library().mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype))
+
+
+def mamba_ssm_fwd(x, W_x, W_dt, A, z=None, dt_bias=None, Dskip=None, delta_softplus=True, h0=None, out=None,
+                  last_state=None, workspace=None, return_last_state=True):
+    """Selection projections followed by the scan (u = x).  Returns (out, last_state)."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = x.shape
+    N = A.shape[1]
+    R = W_dt.shape[1]
+    io = _io_dtype(x)
+    dev = x.device
+    f32 = torch.float32
+    out = torch.empty_like(x) if out is None else out
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, D, N), dtype=f32, device=dev)
+    ws_bytes = mamba_ssm_fwd_workspace_size(batch, L, D, N, R, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.mamba_ssm_fwd(
+        batch, L, D, N, R, io, _ptr(x, "x", x.dtype, (batch, L, D), dev), _ptr(z, "z", x.dtype, (batch, L, D), dev),
+        _ptr(W_x, "W_x", x.dtype, (R + 2 * N, D), dev), _ptr(W_dt, "W_dt", x.dtype, (D, R), dev),
+        _ptr(dt_bias, "dt_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev), _ptr(Dskip, "Dskip", f32, (D,), dev),
+        int(bool(delta_softplus)), _ptr(h0, "h0", f32, (batch, D, N), dev), _ptr(out, "out", x.dtype, (batch, L, D), dev),
+        _ptr(last_state, "last_state", f32, (batch, D, N), dev), _ptr(workspace, "workspace", device=dev),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_ssm_fwd", st)
+    return out, last_state

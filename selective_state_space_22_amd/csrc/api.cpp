@@ -262,4 +262,114 @@ int mamba_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   return MAMBA_OK;
 }
 
+size_t mamba_selection_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                          int64_t dt_rank, int io_dtype) {
+  if (check_shape("mamba_selection_fwd_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK) return 0;
+  if (dt_rank < 1 || dt_rank > kMaxDim) return 0;
+  return s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype);
+}
+
+int mamba_selection_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank, int io_dtype,
+                        const void* x, const void* W_x, const void* W_dt, void* delta, void* B, void* C,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "mamba_selection_fwd";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  if (dt_rank < 1 || dt_rank > kMaxDim) return fail(MAMBA_ERR_DIM, where, "dt_rank");
+  const bool tokens = batch > 0 && seqlen > 0;
+  PtrCheck pc{where};
+  pc.req(x, tokens && dim > 0, "x");
+  pc.req(W_x, tokens && dim > 0, "W_x");
+  pc.req(W_dt, tokens && dim > 0, "W_dt");
+  pc.req(delta, tokens && dim > 0, "delta");
+  pc.req(B, tokens, "B");
+  pc.req(C, tokens, "C");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (!tokens) return MAMBA_OK;
+  const size_t need = s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype);
+  if (!workspace || workspace_bytes < need) return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  s6::SelArgs a{x, W_x, W_dt, delta, B, C, workspace, batch, seqlen, dim, dstate, dt_rank,
+                s6::selection_ld(dt_rank, dstate)};
+  hipError_t e = s6::launch_selection(a, io_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
+size_t mamba_ssm_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank,
+                                    int io_dtype) {
+  if (check_shape("mamba_ssm_fwd_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK) return 0;
+  if (dt_rank < 1 || dt_rank > kMaxDim) return 0;
+  const size_t e = io_dtype == MAMBA_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)batch * seqlen;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return al(tok * dim * e) + 2 * al(tok * dstate * e) + s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype) +
+         al(s6::plan_scan(batch, seqlen, dim, dstate).ws_bytes);
+}
+
+int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank, int io_dtype,
+                  const void* x, const void* z, const void* W_x, const void* W_dt, const float* dt_bias,
+                  const float* A, const float* Dskip, int delta_softplus, const float* h0,
+                  void* out, float* last_state, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "mamba_ssm_fwd";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  if (dt_rank < 1 || dt_rank > kMaxDim) return fail(MAMBA_ERR_DIM, where, "dt_rank");
+  const bool tokens = batch > 0 && seqlen > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(x, tokens, "x");
+  pc.req(W_x, tokens, "W_x");
+  pc.req(W_dt, tokens, "W_dt");
+  pc.req(A, tokens, "A");
+  pc.req(out, tokens, "out");
+  pc.opt(z, "z");
+  pc.opt(dt_bias, "dt_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(h0, "h0");
+  pc.opt(last_state, "last_state");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (batch == 0 || dim == 0) return MAMBA_OK;
+  const size_t need = mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype);
+  if (tokens && (!workspace || workspace_bytes < need)) return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  const size_t e = io_dtype == MAMBA_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)batch * seqlen;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  void* delta = w;
+  void* Bm = w + al(tok * dim * e);
+  void* Cm = w + al(tok * dim * e) + al(tok * dstate * e);
+  void* xdbl = w + al(tok * dim * e) + 2 * al(tok * dstate * e);
+  void* scan_ws = static_cast<uint8_t*>(xdbl) + s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (tokens) {
+    s6::SelArgs sa{x, W_x, W_dt, delta, Bm, Cm, xdbl, batch, seqlen, dim, dstate, dt_rank,
+                   s6::selection_ld(dt_rank, dstate)};
+    hipError_t e1 = s6::launch_selection(sa, io_dtype, hs);
+    if (e1 != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e1));
+  }
+  const s6::ScanPlan plan = s6::plan_scan(batch, seqlen, dim, dstate);
+  s6::ScanArgs a{};
+  a.u = x;
+  a.delta = delta;
+  a.bias = dt_bias;
+  a.A = A;
+  a.B = Bm;
+  a.C = Cm;
+  a.dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.out = out;
+  a.last = last_state;
+  a.batch = batch;
+  a.L = seqlen;
+  a.D = dim;
+  a.chunk_len = plan.chunk_len;
+  a.nchunks = plan.nchunks;
+  a.softplus = delta_softplus != 0;
+  hipError_t e2 = s6::launch_scan(a, plan, io_dtype, (int)dstate, tokens ? scan_ws : nullptr, hs);
+  if (e2 != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e2));
+  return MAMBA_OK;
+}
+
 }  // extern "C"

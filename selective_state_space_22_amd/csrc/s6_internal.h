@@ -145,6 +145,26 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N);
 hipError_t launch_bwd(const BwdArgs& a, int io, int N, hipStream_t stream);
 
+// ---------------------------------------------------------------- selection projections (selection.hip)
+
+// xdbl = x W_x^T (M x (R+2N), row stride ldx), B/C = its last 2N columns, delta = xdbl[:, :R] W_dt^T.
+struct SelArgs {
+  const void* x;    // (M, D)
+  const void* Wx;   // (R + 2N, D)
+  const void* Wdt;  // (D, R)
+  void* delta;      // (M, D)
+  void* Bout;       // (M, N)
+  void* Cout;       // (M, N)
+  void* xdbl;       // workspace (M, ldx)
+  int64_t batch, L, D, N, R, ldx;
+};
+
+int64_t selection_ld(int64_t R, int64_t N);
+size_t selection_ws_bytes(int64_t batch, int64_t L, int64_t R, int64_t N, int io);
+hipError_t launch_selection(const SelArgs& s, int io, hipStream_t stream);
+hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                          int64_t ldb, int64_t ldc, int io, hipStream_t stream);
+
 // Enqueue the kernels of one scan / one decode step on `stream`.
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
 // Carry pass over (batch, chunk, D, N) chunk aggregates (both engines' split modes).

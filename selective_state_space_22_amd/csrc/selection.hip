@@ -1,0 +1,340 @@
+// selection.hip -- the selection front end of the selective scan on gfx950:
+// the per-token B_t, C_t and the raw dt are linear functions of the token
+// ("Mamba 状态空间模型原理与 Transformer 对比", kb.agiseed.tech, section 3.2:
+// s_B(x) = Linear_N(x), s_C(x) = Linear_N(x), s_dt(x) = a projection of x of a
+// small size, broadcast to the D channels; the dt projection size is the
+// subject of the page's Δ-projection ablation table).  With rank R:
+//     xdbl  = x W_x^T                (M x (R + 2N)),  M = batch * L
+//     B, C  = columns R.. and R+N.. of xdbl
+//     delta = xdbl[:, :R] W_dt^T     (M x D)          (bias and softplus follow in the scan)
+// Both products are dense contractions, so they run on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 for bf16 I/O, v_mfma_f32_16x16x4_f32 for fp32 I/O,
+// fp32 accumulation in both cases.
+//
+// GEMM kernel (C = A B^T, A: M x K, B: N x K, both K-contiguous, 16-byte
+// aligned rows): 128 x 128 output blocks, operands staged through LDS with
+// coalesced loads, fp32 accumulation, results leaving through LDS as 16-byte
+// row segments; every global access is bounds-checked by a buffer resource
+// (rows past M or N and K past the end read as zero, stores past the edges are
+// dropped).  A long K with few output columns (x W_x^T) is split over
+// workgroups into fp32 parts, summed in a fixed order by the kernel that also
+// rounds and splits xdbl.  Shapes whose rows are not 16-byte aligned take a
+// plain VALU kernel instead.
+#include <cstdlib>
+
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int32_t kBufferDword3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, float v);
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store_elem<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// One K slice of 64 bytes per row: 32 bf16 (one MFMA) or 16 fp32 (four MFMAs).
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<uint16_t> {
+  static constexpr int kSlice = 32;  // elements per 64-byte slice
+  static __device__ __forceinline__ f32x4 step(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+};
+template <>
+struct Mfma<float> {
+  static constexpr int kSlice = 16;
+  static __device__ __forceinline__ f32x4 step(u32x4 a, u32x4 b, f32x4 c) {
+    // lanes 16q..16q+15 hold K offsets 4q..4q+3 of the slice; MFMA e takes element e
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+struct GemmArgs {
+  const void* A;  // M x K, row stride lda (elements)
+  const void* B;  // N x K, row stride ldb
+  void* C;        // M x N, row stride ldc
+  int64_t M, N, K, lda, ldb, ldc;
+  int64_t split_stride = 0;  // split K (gridDim.z > 1): part z covers slices [z*sps, (z+1)*sps), output at C + z*split_stride
+  int32_t sps = 0;
+};
+
+// 128 x 128 output block per workgroup of 2 x 2 waves (4 x 4 tiles of 16 x 16
+// each).  K advances in stages of 128 bytes per row (64 bf16 / 32 fp32): the
+// A and B stage tiles (128 rows x 128 bytes each) are read with coalesced
+// 16-byte loads (8 adjacent lanes per row), stored to LDS (double buffered,
+// rows padded by 16 bytes against bank conflicts), and each wave reads its
+// MFMA operands from LDS (lane l: row l % 16, bytes 16 (l / 16) of a 64-byte
+// half-stage).  The next stage's global loads are in flight while the current
+// stage is multiplied.
+constexpr int kGemmBM = 128;
+constexpr int kStageBytes = 128;                  // K bytes per row per stage
+constexpr int kRowPitch = kStageBytes + 16;       // LDS row pitch in bytes
+
+template <typename IN, typename OUT>
+__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
+  constexpr int TM = 4, TN = 4;
+  constexpr uint32_t E = sizeof(IN);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t bm0 = (int64_t)blockIdx.y * kGemmBM;
+  const int64_t bn0 = (int64_t)blockIdx.x * kGemmBM;
+  const int64_t mrows = g.M - bm0 < kGemmBM ? g.M - bm0 : kGemmBM;
+  const int64_t nrows = g.N - bn0 < kGemmBM ? g.N - bn0 : kGemmBM;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda,
+                                              (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb,
+                                              (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kGemmBM * kRowPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kGemmBM * kRowPitch];
+
+  // global -> register share of one stage: 4 loads per operand per thread
+  const int t = threadIdx.x;
+  const int lrow = t >> 3;             // 0..31, + 32 v
+  const uint32_t lbyte = (t & 7) * 16u;
+  const uint32_t kbytes = (uint32_t)(g.K * E);
+  u32x4 ga[4], gb[4];
+  const int all = (int)((kbytes + kStageBytes - 1) / kStageBytes);
+  const int first = gridDim.z > 1 ? (int)blockIdx.z * g.sps : 0;
+  const int nst = gridDim.z > 1 ? (all - first < g.sps ? all - first : g.sps) : all;
+  auto gload = [&](int stage) {
+    const uint32_t kb = (uint32_t)stage * kStageBytes + lbyte;
+    const bool in = stage < first + nst && kb < kbytes;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t row = lrow + 32 * v;
+      ga[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? (uint32_t)(row * g.lda * E) + kb : kOutOfRange, 0, 0);
+      gb[v] = __builtin_amdgcn_raw_buffer_load_b128(rb, in ? (uint32_t)(row * g.ldb * E) + kb : kOutOfRange, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t o = (lrow + 32 * v) * kRowPitch + lbyte;
+      *reinterpret_cast<u32x4*>(&lds_a[buf][o]) = ga[v];
+      *reinterpret_cast<u32x4*>(&lds_b[buf][o]) = gb[v];
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int r16 = lane & 15, q = lane >> 4;
+  gload(first);
+  lstore(0);
+  gload(first + 1);
+  __syncthreads();
+  for (int k = 0; k < nst; ++k) {
+    const int buf = k & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // two 64-byte halves of the stage
+      u32x4 a[TM], b[TN];
+      const uint32_t col = h * 64u + 16u * q;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][(wm * 64 + 16 * i + r16) * kRowPitch + col]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][(wn * 64 + 16 * j + r16) * kRowPitch + col]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<IN>::step(a[i], b[j], acc[i][j]);
+    }
+    if (k + 1 < nst) lstore(buf ^ 1);
+    gload(first + k + 2);
+    __syncthreads();
+  }
+
+  // Output: each 16-row strip of a wave's 64 x 64 tile goes through LDS (fp32,
+  // reusing the stage buffers after the last barrier), then every lane writes
+  // 16 contiguous bytes of one row.
+  OUT* cbase = static_cast<OUT*>(g.C) + (gridDim.z > 1 ? (int64_t)blockIdx.z * g.split_stride : 0);
+  const int64_t m0 = bm0 + wm * 64, n0 = bn0 + wn * 64;
+  const int64_t wrows = g.M - m0 < 64 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 64;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(cbase + m0 * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
+  const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15u) == 0;
+  float(*st)[68] = reinterpret_cast<float(*)[68]>(&lds_a[0][0] + w * 16 * 68 * 4);
+  constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
+  constexpr int LPR = 64 / EPV;          // lanes per row
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[4 * q + r][16 * j + r16] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave execute in order
+#pragma unroll
+    for (int e0 = 0; e0 < 16 * LPR; e0 += 64) {
+      const int e = e0 + lane;
+      const int row = e / LPR, c0 = (e % LPR) * EPV;
+      const int64_t grow = 16 * i + row;  // relative to m0
+      const int64_t gcol = n0 + c0;
+      float v[EPV];
+#pragma unroll
+      for (int kk = 0; kk < EPV; ++kk) v[kk] = st[row][c0 + kk];
+      if (vec_ok && gcol + EPV <= g.N) {
+        const uint32_t off = (uint32_t)((grow * g.ldc + gcol) * sizeof(OUT));
+        u32x4 pk;
+        if constexpr (sizeof(OUT) == 2) {
+          pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+          pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        } else {
+          pk = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(pk, rc, grow < wrows ? off : kOutOfRange, 0, 0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < EPV; ++kk) {
+          const uint32_t off =
+              gcol + kk < g.N ? (uint32_t)((grow * g.ldc + gcol + kk) * sizeof(OUT)) : kOutOfRange;
+          store_elem<OUT>(rc, grow < wrows ? off : kOutOfRange, v[kk]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Any alignment: one thread per output element, K FMAs.
+template <typename IN, typename OUT>
+__global__ void gemm_nt_valu_kernel(GemmArgs g) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.M * g.N) return;
+  const int64_t m = i / g.N, n = i % g.N;
+  const IN* a = static_cast<const IN*>(g.A) + m * g.lda;
+  const IN* b = static_cast<const IN*>(g.B) + n * g.ldb;
+  float acc = 0.0f;
+  for (int64_t k = 0; k < g.K; ++k) acc = __builtin_fmaf(load_io(a, k), load_io(b, k), acc);
+  store_io(static_cast<OUT*>(g.C), (size_t)(m * g.ldc + n), acc);
+}
+
+// Sum of the split-K parts of x W_x^T, rounded once to the I/O type: the
+// first R columns to xdbl (input of the dt projection), the next N to B, the
+// last N to C.
+template <typename IO>
+__global__ void xproj_reduce_kernel(const float* part, int64_t parts, int64_t M, int64_t R, int64_t N, IO* xdbl,
+                                    int64_t ldx, IO* B, IO* C) {
+  const int64_t W = R + 2 * N;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (m, c)
+  if (i >= M * W) return;
+  const int64_t m = i / W, c = i % W;
+  float v = 0.0f;
+  for (int64_t z = 0; z < parts; ++z) v += part[z * M * W + i];
+  if (c < R) store_io(xdbl, (size_t)(m * ldx + c), v);
+  else if (c < R + N) store_io(B, (size_t)(m * N + c - R), v);
+  else store_io(C, (size_t)(m * N + c - R - N), v);
+}
+
+size_t xdbl_bytes(int64_t batch, int64_t L, int64_t R, int64_t N, size_t e) {
+  (void)N;
+  return ((size_t)batch * L * ((R + 7) / 8 * 8) * e + 255) / 256 * 256;
+}
+
+template <typename IN>
+bool mfma_ok(const GemmArgs& g) {
+  constexpr int64_t VEC = 16 / sizeof(IN);
+  return g.K % VEC == 0 && g.lda % VEC == 0 && g.ldb % VEC == 0 && (reinterpret_cast<uintptr_t>(g.A) & 15u) == 0 &&
+         (reinterpret_cast<uintptr_t>(g.B) & 15u) == 0;
+}
+
+// C (OUT) = A B^T.  128 x 128 per workgroup of 2 x 2 waves of 4 x 4 tiles, two
+// K slices in flight; with parts > 1, K is split over gridDim.z and part z is
+// written (fp32) at C + z * split_stride.
+template <typename IN, typename OUT>
+hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (mfma_ok<IN>(g)) {
+    const int all = (int)((g.K * (int64_t)sizeof(IN) + kStageBytes - 1) / kStageBytes);
+    g.sps = (all + parts - 1) / parts;
+    dim3 grid((unsigned)((g.N + kGemmBM - 1) / kGemmBM), (unsigned)((g.M + kGemmBM - 1) / kGemmBM), (unsigned)parts);
+    hipLaunchKernelGGL((gemm_nt_mfma_kernel<IN, OUT>), grid, dim3(256), 0, st, g);
+  } else {
+    // the vector path never splits: part 0 holds the whole sum (callers pass parts = 1 then)
+    const int64_t n = g.M * g.N;
+    hipLaunchKernelGGL((gemm_nt_valu_kernel<IN, OUT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g);
+  }
+  return hipGetLastError();
+}
+
+// Split of K for x W_x^T: enough workgroups to fill the chip several times over
+// (the product has few output columns and a long K).
+int xproj_parts(int64_t M, int64_t W, int64_t K, int esize) {
+  const int64_t tiles = ((M + 127) / 128) * ((W + 127) / 128);
+  const int64_t stages = (K * esize + kStageBytes - 1) / kStageBytes;
+  int parts = 1;
+  while (parts < 8 && tiles * parts < 1024 && stages / (parts * 2) >= 8) parts *= 2;
+  return parts;
+}
+
+template <typename IO>
+hipError_t launch_selection_t(const SelArgs& s, hipStream_t st) {
+  const int64_t M = s.batch * s.L;
+  const int64_t W = s.R + 2 * s.N;
+  IO* xdbl = static_cast<IO*>(s.xdbl);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(s.xdbl) + xdbl_bytes(s.batch, s.L, s.R, s.N, sizeof(IO)));
+  GemmArgs g1{s.x, s.Wx, part, M, W, s.D, s.D, s.D, W};
+  g1.split_stride = M * W;
+  const int parts = mfma_ok<IO>(g1) ? xproj_parts(M, W, s.D, sizeof(IO)) : 1;
+  hipError_t e = gemm_nt<IO, float>(g1, st, parts);
+  if (e != hipSuccess) return e;
+  const int64_t n = M * W;
+  hipLaunchKernelGGL((xproj_reduce_kernel<IO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
+                     (int64_t)parts, M, s.R, s.N, xdbl, s.ldx, static_cast<IO*>(s.Bout), static_cast<IO*>(s.Cout));
+  GemmArgs g2{xdbl, s.Wdt, s.delta, M, s.D, s.R, s.ldx, s.R, s.D};
+  return gemm_nt<IO, IO>(g2, st);
+}
+
+}  // namespace
+
+int64_t selection_ld(int64_t R, int64_t N) { return (R + 7) / 8 * 8; }
+
+size_t selection_ws_bytes(int64_t batch, int64_t L, int64_t R, int64_t N, int io) {
+  const size_t e = io == kIoBF16 ? 2 : 4;
+  const int64_t M = batch * L, W = R + 2 * N;
+  // xdbl (first R columns, padded rows), then up to 8 fp32 split-K parts of x W_x^T
+  return xdbl_bytes(batch, L, R, N, e) + ((size_t)8 * M * W * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_selection(const SelArgs& s, int io, hipStream_t st) {
+  return io == kIoBF16 ? launch_selection_t<uint16_t>(s, st) : launch_selection_t<float>(s, st);
+}
+
+hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
+                          int64_t ldb, int64_t ldc, int io, hipStream_t st) {
+  GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc};
+  return io == kIoBF16 ? gemm_nt<uint16_t, uint16_t>(g, st) : gemm_nt<float, float>(g, st);
+}
+
+}  // namespace s6

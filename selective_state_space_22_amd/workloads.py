@@ -239,6 +239,35 @@ def grad_inputs(batch: int, seqlen: int, dim: int, dstate: int, io: str = "f32",
     return GradInputs(dout, dlast)
 
 
+def dt_rank_for(dim: int) -> int:
+    """Size of the dt projection for a layer of D = dim channels: d_model / 16 with
+    d_model = D / 2 (expand factor 2), at least 1.  The page's dt-projection
+    ablation has its default model (the 371.5 M-parameter row shared with the
+    state-size table) at size 64, i.e. d_model 1024 / 16."""
+    return max(1, -(-(dim // 2) // 16))
+
+
+@dataclasses.dataclass
+class SelectionWeights:
+    W_x: np.ndarray   # (R + 2N, D)
+    W_dt: np.ndarray  # (D, R)
+
+
+def selection_weights(dim: int, dstate: int, dt_rank: int, io: str = "f32", seed: int = SEED_BASE) -> SelectionWeights:
+    """Random-init projection weights in the usual linear-layer ranges:
+    W_x ~ U(-1/sqrt(D), 1/sqrt(D)), W_dt ~ U(-1/sqrt(R), 1/sqrt(R)) (own streams of
+    SeedSequence(seed + 700000)); bf16 rounds once (RNE)."""
+    seqs = np.random.SeedSequence(seed + 700_000).spawn(2)
+    bx = 1.0 / math.sqrt(dim)
+    bd = 1.0 / math.sqrt(dt_rank)
+    W_x = _fill(seqs[0], (dt_rank + 2 * dstate, dim), "uniform", -bx, bx)
+    W_dt = _fill(seqs[1], (dim, dt_rank), "uniform", -bd, bd)
+    if io == "bf16":
+        W_x = bf16_round(W_x)[1].reshape(W_x.shape)
+        W_dt = bf16_round(W_dt)[1].reshape(W_dt.shape)
+    return SelectionWeights(W_x, W_dt)
+
+
 def generate_workload(name: str) -> ScanInputs:
     """The seeded inputs of a named workload (decode: the 64 tokens as one (B, 64, D) block)."""
     w = WORKLOADS[name]

@@ -32,7 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
-                                    "mamba_scan_fwd_workspace_size", "mamba_state_update", "mamba_status_string",
+                                    "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
+                                    "mamba_selection_fwd_workspace_size", "mamba_ssm_fwd",
+                                    "mamba_ssm_fwd_workspace_size", "mamba_state_update", "mamba_status_string",
                                     "mamba_version"]
 
 
@@ -178,3 +180,32 @@ def test_bwd_rejects_misaligned_pointers_and_small_workspace(lib):
 def test_bwd_empty_channel_dimension_is_a_no_op(lib):
     assert bwd_call(lib, D=0, u=None, delta=None, A=None, B=None, C=None, dout=None, du=None, ddelta=None, dA=None,
                     dB=None, dC=None) == OK
+
+
+def test_selection_and_ssm_validation(lib):
+    sel = lib.mamba_selection_fwd
+    need = binding.mamba_selection_fwd_workspace_size(1, 8, 64, 16, 4, 0)
+    assert need >= 8 * 40 * 4
+    ok = dict(x=FAKE, wx=FAKE, wdt=FAKE, d=FAKE, b=FAKE, c=FAKE)
+
+    def call(R=4, io=0, ws=FAKE, ws_bytes=need, **kw):
+        p = {**ok, **kw}
+        return sel(1, 8, 64, 16, R, io, p["x"], p["wx"], p["wdt"], p["d"], p["b"], p["c"], ws, ws_bytes, None)
+
+    assert call(R=0) == ERR_DIM
+    assert call(io=4) == ERR_DTYPE
+    for k in ok:
+        assert call(**{k: None}) == ERR_NULL, k
+        assert call(**{k: FAKE + 2}) == ERR_ALIGN, k
+    assert call(ws=None) == ERR_WORKSPACE and call(ws_bytes=need - 1) == ERR_WORKSPACE
+    assert binding.mamba_selection_fwd_workspace_size(1, 8, 64, 16, 0, 0) == 0
+    # the fused call checks the same way before touching the device
+    ssm = lib.mamba_ssm_fwd
+    nss = binding.mamba_ssm_fwd_workspace_size(1, 8, 64, 16, 4, 0)
+    assert nss > need
+    assert ssm(1, 8, 64, 16, 4, 0, FAKE, None, FAKE, FAKE, None, FAKE, None, 1, None, FAKE, None, FAKE, nss - 1,
+               None) == ERR_WORKSPACE
+    assert ssm(1, 8, 64, 16, 4, 0, None, None, FAKE, FAKE, None, FAKE, None, 1, None, FAKE, None, FAKE, nss,
+               None) == ERR_NULL
+    assert ssm(1, 8, 64, 16, 0, 0, FAKE, None, FAKE, FAKE, None, FAKE, None, 1, None, FAKE, None, FAKE, nss,
+               None) == ERR_DIM
