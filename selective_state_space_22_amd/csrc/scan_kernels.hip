@@ -181,7 +181,11 @@ int64_t env_int(const char* name, int64_t dflt) {
 
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
-constexpr int64_t kGridMax = 256;           // persistent workgroups: one per CU of an MI355X
+#ifndef S6_WG_PER_CU
+#define S6_WG_PER_CU 1
+#endif
+constexpr int64_t kCus = 256;                          // compute units of an MI355X
+constexpr int64_t kGridMax = kCus * S6_WG_PER_CU;      // persistent workgroups
 constexpr int64_t kChainedMinChains = 128;  // below this many channel blocks, long sequences use two passes
 
 ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N) {
@@ -223,7 +227,7 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
     // about 1024 tokens let the persistent grid balance the blocks.
     p.split = 0;
     int64_t chunk = L;
-    if (chains > kGridMax) chunk = env_int("MAMBA_MI355X_CHUNK", 1024);
+    if (chains > kCus) chunk = env_int("MAMBA_MI355X_CHUNK", 1024);
     chunk = ((chunk + T - 1) / T) * T;
     if (chunk > cap) chunk = cap;
     if (chunk >= L) chunk = L;

@@ -39,6 +39,20 @@ namespace s6 {
 namespace {
 
 constexpr uint32_t kSpinLimit = 1u << 24;
+#ifndef S6_SCAN_AHEAD
+#define S6_SCAN_AHEAD 1
+#endif
+#ifndef S6_WG_TILE
+#define S6_WG_TILE 16
+#endif
+#ifndef S6_WG_PER_CU
+#define S6_WG_PER_CU 1
+#endif
+#ifndef S6_WG_SLOTS
+#define S6_WG_SLOTS 2
+#endif
+constexpr int kSlots = S6_WG_SLOTS;  // LDS slots of front-end data (2 or 3)
+constexpr int kScanAhead = S6_SCAN_AHEAD;  // tokens of LDS operands read ahead in the scan loop
 constexpr int32_t kBufferDword3 = 0x00020000;  // raw (untyped) buffer access on the gfx9 family
 constexpr uint32_t kOutOfRange = 0x80000000u;  // offset beyond every buffer: loads 0, stores dropped
 
@@ -79,24 +93,29 @@ struct WgScan {
   static constexpr int S = N / W;                 // states per wave
   static constexpr int TW = T / W;                // front-end / epilogue tokens per wave per tile
   static constexpr int NT = 64 * W;               // threads
-  static constexpr int BCV = 2 * T * N / NT;      // B/C elements staged per thread per tile
-  static_assert(N % W == 0 && T % W == 0 && W % 2 == 0 && (2 * T * N) % NT == 0 && BCV >= 1 && N % BCV == 0,
-                "tile shape");
+  // B/C of a tile: 2TN elements.  With at least one per thread, the first half
+  // of the waves stage B and the second half C, BCV consecutive elements per
+  // thread; with fewer (short tiles), the first 2TN/64 waves stage one each.
+  static constexpr bool kBcSparse = 2 * T * N < NT;
+  static constexpr int BCV = kBcSparse ? 1 : 2 * T * N / NT;  // B/C elements staged per thread per tile
+  static_assert(N % W == 0 && T % W == 0 && W % 2 == 0, "tile shape");
+  static_assert(kBcSparse ? (T * N) % 64 == 0 : ((2 * T * N) % NT == 0 && N % BCV == 0), "B/C staging");
   static constexpr bool kOut = MODE != kModeAgg;
   static constexpr uint32_t kIo = sizeof(IO);
 
-  // Buffers of tile k: fr and bc in slot k % 3, yp in slot k % 2.  Iteration
-  // k runs front(k+1), epilogue(k-1), scan(k), then the tile's one barrier.
-  // Race-free: front(k+1) overwrites the fr/bc slot of tile k-2, whose last
-  // readers (scan(k-2), epilogue(k-2)) finished before the barrier of
-  // iteration k-1; scan(k) overwrites the yp slot of tile k-2, last read by
-  // epilogue(k-2) before that same barrier; epilogue(k-1) reads what scan(k-1)
-  // wrote before the barrier of iteration k-1.
+  // Buffers of tile k: fr and bc in slot k % kSlots, yp in slot k % 2.  With
+  // three slots, iteration k runs front(k+1), epilogue(k-1), scan(k), then the
+  // tile's one barrier.  Race-free: front(k+1) overwrites the fr/bc slot of
+  // tile k-2, whose last readers (scan(k-2), epilogue(k-2)) finished before the
+  // barrier of iteration k-1; scan(k) overwrites the yp slot of tile k-2, last
+  // read by epilogue(k-2) before that same barrier; epilogue(k-1) reads what
+  // scan(k-1) wrote before the barrier of iteration k-1.  With two slots the
+  // epilogue of k-1 runs first (see run_item).
   static constexpr int BCW = (2 * S + 3) / 4 * 4;  // bc row per (token, wave), padded to float4
 
   struct Lds {
-    float4 fr[3][T][64];                         // (dt, dt^2, x, z) per (token, channel)
-    __attribute__((aligned(16))) float bc[3][T][W][BCW];  // per token and wave: B of its states, then C
+    float4 fr[kSlots][T][64];                    // (dt, dt^2, x, z) per (token, channel)
+    __attribute__((aligned(16))) float bc[kSlots][T][W][BCW];  // per token and wave: B of its states, then C
     float yp[kOut ? 2 : 1][T][W][64];            // partial readouts
     float sdt[W][64];                            // split mode: partial sums of dt
     int item[2];
@@ -142,12 +161,19 @@ struct WgScan {
       r.uu[i] = BufIo<IO>::load(r_u, off);
       if (kOut) r.zz[i] = BufIo<IO>::load(r_z, off);
     }
-    // The first half of the waves stage B, the second half C (uniform per wave).
-    const __amdgpu_buffer_rsrc_t rbc = w < W / 2 ? r_B : r_C;
+    if (kBcSparse) {
+      const int q = (w * 64) / (T * N);  // 0: B, 1: C, >= 2: nothing (uniform per wave)
+      const __amdgpu_buffer_rsrc_t rbc = q == 0 ? r_B : r_C;
+      const int e = w * 64 + lane - q * (T * N);
+      r.bcv[0] = BufIo<IO>::load(rbc, q < 2 ? (uint32_t)(k * T * N + e) * kIo : kOutOfRange);
+    } else {
+      // The first half of the waves stage B, the second half C (uniform per wave).
+      const __amdgpu_buffer_rsrc_t rbc = w < W / 2 ? r_B : r_C;
 #pragma unroll
-    for (int v = 0; v < BCV; ++v) {
-      const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;  // element of the tile's B (or C) block
-      r.bcv[v] = BufIo<IO>::load(rbc, (uint32_t)(k * T * N + e) * kIo);
+      for (int v = 0; v < BCV; ++v) {
+        const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;  // element of the tile's B (or C) block
+        r.bcv[v] = BufIo<IO>::load(rbc, (uint32_t)(k * T * N + e) * kIo);
+      }
     }
   }
 
@@ -168,12 +194,21 @@ struct WgScan {
         dsum = tk;
       }
     }
-    const int c = w < W / 2 ? 0 : 1;
+    if (kBcSparse) {
+      const int q = (w * 64) / (T * N);
+      if (q < 2) {
+        const int e = w * 64 + lane - q * (T * N);
+        const int j = e / N, n = e % N;
+        sm.bc[f3][j][n / S][q * S + n % S] = BufIo<IO>::widen(r.bcv[0]);
+      }
+    } else {
+      const int c = w < W / 2 ? 0 : 1;
 #pragma unroll
-    for (int v = 0; v < BCV; ++v) {
-      const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;
-      const int j = e / N, n = e % N;
-      sm.bc[f3][j][n / S][c * S + n % S] = BufIo<IO>::widen(r.bcv[v]);
+      for (int v = 0; v < BCV; ++v) {
+        const int e = ((w % (W / 2)) * 64 + lane) * BCV + v;
+        const int j = e / N, n = e % N;
+        sm.bc[f3][j][n / S][c * S + n % S] = BufIo<IO>::widen(r.bcv[v]);
+      }
     }
   }
 
@@ -215,12 +250,15 @@ struct WgScan {
   __device__ __forceinline__ void scan(int k, int f3, int y2) {
     const int nv = tile_valid(k);
     if (nv == T) {
-      Tok t[2];
-      read_tok(t[0], f3, 0);
+      // operands of the next kScanAhead tokens are in flight while a token is computed
+      constexpr int P = kScanAhead < T ? kScanAhead : T;
+      Tok t[P + 1];
+#pragma unroll
+      for (int j = 0; j < P; ++j) read_tok(t[j], f3, j);
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        if (j + 1 < T) read_tok(t[(j + 1) & 1], f3, j + 1);
-        step(t[j & 1], y2, j);
+        if (j + P < T) read_tok(t[(j + P) % (P + 1)], f3, j + P);
+        step(t[j % (P + 1)], y2, j);
       }
     } else {
       for (int j = 0; j < nv; ++j) {
@@ -330,19 +368,36 @@ struct WgScan {
     // of tile k: it reads the yp slot of k-1 (next written by the scan of k+1,
     // after this interval's barrier) and the fr slot of k-1 (next written by
     // the front end of k+2, also after it).
-    int f3 = 0;   // slot of tile k
-    int f3p = 2;  // slot of tile k - 1
-    for (int k = 0; k < ntiles; ++k) {
-      const int f3n = f3 == 2 ? 0 : f3 + 1;
-      front(r, k + 1, f3n);
-      load(r, k + 2);
-      if (k > 0) epilogue(k - 1, f3p, (k - 1) & 1);
-      scan(k, f3, k & 1);
-      __syncthreads();
-      f3p = f3;
-      f3 = f3n;
+    if (kSlots == 3) {
+      int f3 = 0;   // slot of tile k
+      int f3p = 2;  // slot of tile k - 1
+      for (int k = 0; k < ntiles; ++k) {
+        const int f3n = f3 == 2 ? 0 : f3 + 1;
+        front(r, k + 1, f3n);
+        load(r, k + 2);
+        if (k > 0) epilogue(k - 1, f3p, (k - 1) & 1);
+        scan(k, f3, k & 1);
+        __syncthreads();
+        f3p = f3;
+        f3 = f3n;
+      }
+      if (ntiles > 0) epilogue(ntiles - 1, f3p, (ntiles - 1) & 1);
+    } else {
+      // Two slots: the epilogue of tile k-1 reads its fr entries before the
+      // front end of tile k+1 overwrites that slot.  Both touch only the
+      // entries of this wave's own tokens (token j belongs to wave j % W), so
+      // program order within the wave is enough; the scans read all entries
+      // of a slot only in the interval after its front end, past a barrier.
+      for (int k = 0; k < ntiles; ++k) {
+        const int f2 = k & 1;
+        if (k > 0) epilogue(k - 1, f2 ^ 1, f2 ^ 1);
+        front(r, k + 1, f2 ^ 1);
+        load(r, k + 2);
+        scan(k, f2, f2);
+        __syncthreads();
+      }
+      if (ntiles > 0) epilogue(ntiles - 1, (ntiles - 1) & 1, (ntiles - 1) & 1);
     }
-    if (ntiles > 0) epilogue(ntiles - 1, f3p, (ntiles - 1) & 1);
 
     // publish the chunk's end
     if (MODE == kModeChained) {
@@ -385,7 +440,7 @@ struct WgScan {
 };
 
 template <typename IO, int N, int W, int T, int MODE>
-__global__ __launch_bounds__(64 * W, 1) void scan_wg_kernel(WgArgs a) {
+__global__ __launch_bounds__(64 * W, S6_WG_PER_CU) void scan_wg_kernel(WgArgs a) {
   using K = WgScan<IO, N, W, T, MODE>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
@@ -430,7 +485,8 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.nitems = a.chains * (p.nchunks - 1);
     const unsigned g1 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
     hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg>), dim3(g1), block, 0, st, a);
-    launch_chunk_carry(a.s, N, st);
+    const hipError_t ce = launch_chunk_carry(a.s, N, st);
+    if (ce != hipSuccess) return ce;
     a.ticket = ctrl + 1;
     a.nitems = a.chains * p.nchunks;
     const unsigned g2 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
@@ -447,16 +503,19 @@ int wg_waves(int64_t N) {
   if (N == 16 && v && v[0] == '4') return 4;
   return N == 16 ? 8 : 4;
 }
-int wg_tile(int64_t) { return 16; }
+int wg_tile(int64_t) { return S6_WG_TILE; }
 
 hipError_t launch_scan_wg(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
   const bool bf = io == kIoBF16;
   if (N == 16 && p.waves == 8)
-    return bf ? launch_wg_t<uint16_t, 16, 8, 16>(s, p, ws, st) : launch_wg_t<float, 16, 8, 16>(s, p, ws, st);
+    return bf ? launch_wg_t<uint16_t, 16, 8, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_t<float, 16, 8, S6_WG_TILE>(s, p, ws, st);
   if (N == 16 && p.waves == 4)
-    return bf ? launch_wg_t<uint16_t, 16, 4, 16>(s, p, ws, st) : launch_wg_t<float, 16, 4, 16>(s, p, ws, st);
+    return bf ? launch_wg_t<uint16_t, 16, 4, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_t<float, 16, 4, S6_WG_TILE>(s, p, ws, st);
   if (N == 8)
-    return bf ? launch_wg_t<uint16_t, 8, 4, 16>(s, p, ws, st) : launch_wg_t<float, 8, 4, 16>(s, p, ws, st);
+    return bf ? launch_wg_t<uint16_t, 8, 4, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_t<float, 8, 4, S6_WG_TILE>(s, p, ws, st);
   return hipErrorInvalidValue;
 }
 
