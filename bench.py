@@ -72,6 +72,17 @@ def cpu_baseline(inp, name, which="fwd"):
     args = [np.ascontiguousarray(x, np.float64) if x is not None else None
             for x in (sub.u, sub.delta, sub.A, sub.B, sub.C, sub.delta_bias, sub.Dskip, sub.z)]
     threads = oracle.max_threads()
+    min_s, max_calls = 10.0, 64  # repeat the sample until about 10 s of CPU work has run
+
+    def timed(fn):
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= min_s or calls >= max_calls:
+                return el / calls, calls
+
     if which == "bwd":
         if name != "million_tokens":  # one batch row: the backward oracle is ~3x the forward's work
             sub = W.channel_subset(inp, [0], np.arange(inp.dim))
@@ -79,18 +90,15 @@ def cpu_baseline(inp, name, which="fwd"):
             args = [np.ascontiguousarray(x, np.float64) if x is not None else None
                     for x in (sub.u, sub.delta, sub.A, sub.B, sub.C, sub.delta_bias, sub.Dskip, sub.z)]
         gi = W.grad_inputs(sub.batch, sub.seqlen, sub.dim, sub.dstate, "f32", seed=1)
-        t0 = time.perf_counter()
-        oracle.scan_bwd(args[0], args[1], args[2], args[3], args[4], gi.dout, args[5], args[6], args[7],
-                        softplus=True, dlast=gi.dlast, nthreads=threads)
-        dt = time.perf_counter() - t0
+        dt, calls = timed(lambda: oracle.scan_bwd(args[0], args[1], args[2], args[3], args[4], gi.dout, args[5],
+                                                  args[6], args[7], softplus=True, dlast=gi.dlast, nthreads=threads))
         what += " (backward)"
     else:
-        t0 = time.perf_counter()
-        oracle.scan(*args, softplus=True, nthreads=threads)
-        dt = time.perf_counter() - t0
+        dt, calls = timed(lambda: oracle.scan(*args, softplus=True, nthreads=threads))
     elems = sub.batch * sub.seqlen * sub.dim * sub.dstate
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what}; {elems} elements in {dt:.2f} s wall (fp64, OpenMP over (batch, channel))"}
+            "sample": f"{what}; {elems} elements per call, {calls} calls, {dt:.3f} s wall per call "
+                      "(fp64, OpenMP over (batch, channel))"}
 
 
 def source_sha256():
@@ -106,7 +114,7 @@ def source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, which="fwd"):
     """HBM bytes per launch of the dominant kernel from the committed PMC readings, or None."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
@@ -115,7 +123,7 @@ def measured_traffic(workload):
         return None
     if rec.get("source_sha256") != source_sha256():
         return None
-    w = rec.get("workloads", {}).get(workload)
+    w = rec.get("workloads", {}).get(workload if which == "fwd" else f"{workload}:{which}")
     return None if w is None else int(w["bytes"])
 
 
@@ -319,7 +327,7 @@ def main():
     gbps = bytes_per_step / (ms * 1e-3) / 1e9
     flops = units * FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
     tflops = flops / (ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload) if args.which == "fwd" else None
+    traffic = measured_traffic(args.workload, args.which)
     if args.which == "bwd":
         # per (b, l, d, n): forward recompute (9) as above plus the reverse step (~20 fp32 ops, FMA = 2)
         flops = units * (FLOPS_PER_ELEMENT + BWD_FLOPS_PER_ELEMENT) + (units / w.dstate) * 30.0
@@ -327,7 +335,7 @@ def main():
     if args.which == "sel":
         peak = MFMA_BF16_PEAK_TFLOPS if w.io == "bf16" else MFMA_F32_PEAK_TFLOPS
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "mfma_tflops": round(sel_flops / (ms * 1e-3) / 1e12, 2), "mfma_peak": peak,
                 "note": "two GEMMs of arithmetic intensity below the MFMA/HBM ridge: HBM-bound"}
     elif decode:

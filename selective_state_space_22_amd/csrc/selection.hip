@@ -79,8 +79,9 @@ struct GemmArgs {
   const void* B;  // N x K, row stride ldb
   void* C;        // M x N, row stride ldc
   int64_t M, N, K, lda, ldb, ldc;
-  int64_t split_stride = 0;  // split K (gridDim.z > 1): part z covers slices [z*sps, (z+1)*sps), output at C + z*split_stride
+  int64_t split_stride = 0;  // split K (parts > 1): part z covers stages [z*sps, (z+1)*sps), output at C + z*split_stride
   int32_t sps = 0;
+  int32_t parts = 1;
 };
 
 // 128 x 128 output block per workgroup of 2 x 2 waves (4 x 4 tiles of 16 x 16
@@ -102,8 +103,21 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int64_t bm0 = (int64_t)blockIdx.y * kGemmBM;
-  const int64_t bn0 = (int64_t)blockIdx.x * kGemmBM;
+  // XCD-aware block order.  Consecutive workgroup ids go to the 8 XCDs in turn,
+  // each with its own L2.  The column blocks of one (row block, K part) group,
+  // which all read the same rows of A, get ids congruent mod 8 and 8 apart:
+  // they run on one XCD at about the same time and read A once into its L2.
+  const int nbn = (int)((g.N + kGemmBM - 1) / kGemmBM);
+  const int64_t groups = ((g.M + kGemmBM - 1) / kGemmBM) * g.parts;
+  const int64_t id = blockIdx.x;
+  const int64_t round = id / (8 * nbn), rem = id % (8 * nbn);
+  const int64_t grp = round * 8 + rem % 8;
+  if (grp >= groups) return;
+  const int col_blk = (int)(rem / 8);
+  const int64_t row_blk = grp % ((g.M + kGemmBM - 1) / kGemmBM);
+  const int part = (int)(grp / ((g.M + kGemmBM - 1) / kGemmBM));
+  const int64_t bm0 = row_blk * kGemmBM;
+  const int64_t bn0 = (int64_t)col_blk * kGemmBM;
   const int64_t mrows = g.M - bm0 < kGemmBM ? g.M - bm0 : kGemmBM;
   const int64_t nrows = g.N - bn0 < kGemmBM ? g.N - bn0 : kGemmBM;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda,
@@ -120,8 +134,8 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
   const uint32_t kbytes = (uint32_t)(g.K * E);
   u32x4 ga[4], gb[4];
   const int all = (int)((kbytes + kStageBytes - 1) / kStageBytes);
-  const int first = gridDim.z > 1 ? (int)blockIdx.z * g.sps : 0;
-  const int nst = gridDim.z > 1 ? (all - first < g.sps ? all - first : g.sps) : all;
+  const int first = g.parts > 1 ? part * g.sps : 0;
+  const int nst = g.parts > 1 ? (all - first < g.sps ? all - first : g.sps) : all;
   auto gload = [&](int stage) {
     const uint32_t kb = (uint32_t)stage * kStageBytes + lbyte;
     const bool in = stage < first + nst && kb < kbytes;
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
   // Output: each 16-row strip of a wave's 64 x 64 tile goes through LDS (fp32,
   // reusing the stage buffers after the last barrier), then every lane writes
   // 16 contiguous bytes of one row.
-  OUT* cbase = static_cast<OUT*>(g.C) + (gridDim.z > 1 ? (int64_t)blockIdx.z * g.split_stride : 0);
+  OUT* cbase = static_cast<OUT*>(g.C) + (g.parts > 1 ? (int64_t)part * g.split_stride : 0);
   const int64_t m0 = bm0 + wm * 64, n0 = bn0 + wn * 64;
   const int64_t wrows = g.M - m0 < 64 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 64;
   const __amdgpu_buffer_rsrc_t rc =
@@ -270,7 +284,7 @@ bool mfma_ok(const GemmArgs& g) {
 }
 
 // C (OUT) = A B^T.  128 x 128 per workgroup of 2 x 2 waves of 4 x 4 tiles, two
-// K slices in flight; with parts > 1, K is split over gridDim.z and part z is
+// K slices in flight; with parts > 1, K is split into parts and part z is
 // written (fp32) at C + z * split_stride.
 template <typename IN, typename OUT>
 hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
@@ -278,8 +292,11 @@ hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
   if (mfma_ok<IN>(g)) {
     const int all = (int)((g.K * (int64_t)sizeof(IN) + kStageBytes - 1) / kStageBytes);
     g.sps = (all + parts - 1) / parts;
-    dim3 grid((unsigned)((g.N + kGemmBM - 1) / kGemmBM), (unsigned)((g.M + kGemmBM - 1) / kGemmBM), (unsigned)parts);
-    hipLaunchKernelGGL((gemm_nt_mfma_kernel<IN, OUT>), grid, dim3(256), 0, st, g);
+    g.parts = parts;
+    const int64_t nbn = (g.N + kGemmBM - 1) / kGemmBM;
+    const int64_t groups = ((g.M + kGemmBM - 1) / kGemmBM) * parts;
+    const int64_t blocks = (groups + 7) / 8 * 8 * nbn;  // whole groups of 8 (ids past the last group exit)
+    hipLaunchKernelGGL((gemm_nt_mfma_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st, g);
   } else {
     // the vector path never splits: part 0 holds the whole sum (callers pass parts = 1 then)
     const int64_t n = g.M * g.N;
