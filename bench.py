@@ -101,30 +101,30 @@ def cpu_baseline(inp, name, which="fwd"):
                       "(fp64, OpenMP over (batch, channel))"}
 
 
-def source_sha256():
-    """Hash of the HIP sources: counter readings taken on other sources do not apply."""
-    import glob
+def source_sha256(files):
+    """Hash of the named HIP source files (csrc/): counter readings taken on other sources do not apply."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "selective_state_space_22_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in sorted(files):
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "selective_state_space_22_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload, which="fwd"):
-    """HBM bytes per launch of the dominant kernel from the committed PMC readings, or None."""
+    """HBM bytes per launch of the dominant kernel from the committed PMC readings, or None
+    when there is no reading or the kernel's sources changed since it was taken."""
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f)
-    except (OSError, ValueError):
+        w = rec["workloads"].get(workload if which == "fwd" else f"{workload}:{which}")
+        if w is None or source_sha256(w["sources"]) != w["source_sha256"]:
+            return None
+        return int(w["bytes"])
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("source_sha256") != source_sha256():
-        return None
-    w = rec.get("workloads", {}).get(workload if which == "fwd" else f"{workload}:{which}")
-    return None if w is None else int(w["bytes"])
 
 
 def calibrate_copy(torch, dev, mib, steps):
