@@ -101,3 +101,72 @@ def test_decode_graph_replays_match_eager():
         assert all(torch.equal(a, b) for a, b in zip(outs, ref_outs)), f"replay {rep}: outputs differ"
         assert torch.equal(state, ref_state), f"replay {rep}: state differs"
         _ = float(np.asarray(state[0, 0].cpu()).sum())
+
+
+def _replay_matches(call, outputs, reps=3):
+    """Capture call() in a graph; every replay (with eager work in between) reproduces the eager outputs."""
+    call()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(reps):
+        for o in outputs:
+            o.fill_(float("nan") if o.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outputs, ref)):
+            assert torch.equal(o, r), f"replay {rep}: output {i} differs"
+        _ = float(outputs[0].float().sum().item())  # unrelated eager work between replays
+
+
+def test_backward_graph_replays_match_eager():
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+
+    print("\n[gpu-test] graph replay of mamba_scan_bwd (2, 700, 200, 16) bf16", flush=True)
+    inp = W.generate(2, 700, 200, 16, "bf16", seed=55)
+    gi = W.grad_inputs(2, 700, 200, 16, "bf16", seed=55)
+    d = to_device(inp)
+    dout = torch.from_numpy(gi.dout).cuda().to(torch.bfloat16)
+    dl = torch.from_numpy(gi.dlast).cuda()
+    grads = {"du": torch.empty_like(d["u"]), "ddelta": torch.empty_like(d["u"]), "dz": torch.empty_like(d["u"]),
+             "dB": torch.empty_like(d["B"]), "dC": torch.empty_like(d["C"]),
+             "dA": torch.empty((200, 16), device="cuda"), "dDskip": torch.empty(200, device="cuda"),
+             "ddelta_bias": torch.empty(200, device="cuda"), "dh0": torch.empty((2, 200, 16), device="cuda")}
+    ws = torch.empty(binding.mamba_scan_bwd_workspace_size(2, 700, 200, 16, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.mamba_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dout, d["delta_bias"], d["Dskip"], d["z"],
+                               True, None, dl, grads=grads, workspace=ws)
+
+    _replay_matches(call, list(grads.values()))
+
+
+def test_ssm_graph_replays_match_eager():
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+
+    print("\n[gpu-test] graph replay of mamba_ssm_fwd (2, 600, 256, 16) bf16", flush=True)
+    inp = W.generate(2, 600, 256, 16, "bf16", seed=66)
+    sw = W.selection_weights(256, 16, 8, "bf16", seed=66)
+    d = to_device(inp)
+    wx = torch.from_numpy(sw.W_x).cuda().to(torch.bfloat16)
+    wdt = torch.from_numpy(sw.W_dt).cuda().to(torch.bfloat16)
+    out = torch.empty_like(d["u"])
+    last = torch.empty((2, 256, 16), device="cuda")
+    ws = torch.empty(binding.mamba_ssm_fwd_workspace_size(2, 600, 256, 16, 8, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.mamba_ssm_fwd(d["u"], wx, wdt, d["A"], z=d["z"], dt_bias=d["delta_bias"], Dskip=d["Dskip"], out=out,
+                              last_state=last, workspace=ws)
+
+    _replay_matches(call, [out, last])

@@ -330,3 +330,33 @@ def test_linearity():
     o3, h3 = _run(inp)
     assert parity_error(o3, 0.5 * o1.astype(np.float64) - 1.25 * o2) <= 1e-4
     assert parity_error(h3, 0.5 * h1.astype(np.float64) - 1.25 * h2) <= 1e-4
+
+
+@pytest.mark.parametrize("case", [(3, 12, 70, 1, "f32"), (2, 9, 64, 2, "bf16"), (4, 10, 100, 4, "f32"),
+                                  (2, 8, 130, 8, "bf16"), (1, 5, 33, 16, "f32")], ids=str)
+def test_decode_small_dstate(case):
+    """Decode steps for every supported N against the oracle's step (and the GPU scan)."""
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_state_update
+
+    batch, L, D, N, io = case
+    _announce(f"decode {case}")
+    inp = W.generate(batch, L, D, N, io, seed=900 + N)
+    d = to_device(inp)
+    h0 = np.random.default_rng(N).standard_normal((batch, D, N)).astype(np.float32)
+    state = torch.from_numpy(h0.copy()).cuda()
+    st_ref = h0.astype(np.float64)
+    outs = []
+    for t in range(L):
+        # fresh copies: a slice of a batch-1 tensor is already contiguous and keeps its (unaligned) offset
+        o = mamba_state_update(state, d["u"][:, t].clone(), d["delta"][:, t].clone(), d["A"],
+                               d["B"][:, t].clone(), d["C"][:, t].clone(), d["delta_bias"], d["Dskip"],
+                               d["z"][:, t].clone(), True)
+        outs.append(to_host(o))
+        ro, st_ref = oracle.step(st_ref, inp.u[:, t], inp.delta[:, t], inp.A, inp.B[:, t], inp.C[:, t],
+                                 inp.delta_bias, inp.Dskip, inp.z[:, t], True)
+        assert parity_error(outs[-1], ro) <= TOL[io], f"step {t}"
+    torch.cuda.synchronize()
+    assert parity_error(to_host(state), st_ref) <= TOL[io]
+    so, sl = gpu_scan(inp, h0=h0)
+    assert parity_error(np.stack(outs, 1), so) <= TOL[io] and parity_error(to_host(state), sl) <= 1e-5
