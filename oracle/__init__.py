@@ -183,14 +183,15 @@ def scan_numpy(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=
     return out, h
 
 
-def selection(x, W_x, W_dt, dstate, store=None):
+def selection(x, W_x, W_dt, dstate, store=None, store_delta=True):
     """fp64 selection projections (section 3.2).  x (batch, L, D), W_x (R + 2N, D),
     W_dt (D, R).  Returns (delta_raw (batch, L, D), B (batch, L, N), C (batch, L, N)):
     xdbl = x W_x^T; B, C = its columns R..R+N and R+N..R+2N; delta = xdbl[:, :R] W_dt^T.
 
     ``store`` (optional) maps an fp64 array to the values of the type the
     projected tensors are kept in (xdbl before the dt projection, and the three
-    results); None keeps fp64 throughout."""
+    results); None keeps fp64 throughout.  ``store_delta=False`` leaves delta
+    unrounded (a consumer that projects dt itself never stores it)."""
     keep = store if store is not None else (lambda a: a)
     x = np.asarray(x, np.float64)
     W_x = np.asarray(W_x, np.float64)
@@ -199,5 +200,7 @@ def selection(x, W_x, W_dt, dstate, store=None):
     N = int(dstate)
     assert W_x.shape == (R + 2 * N, x.shape[-1]) and W_dt.shape == (x.shape[-1], R)
     xdbl = keep(x @ W_x.T)
-    delta = keep(xdbl[..., :R] @ W_dt.T)
+    delta = xdbl[..., :R] @ W_dt.T
+    if store_delta:
+        delta = keep(delta)
     return delta, np.ascontiguousarray(xdbl[..., R:R + N]), np.ascontiguousarray(xdbl[..., R + N:])

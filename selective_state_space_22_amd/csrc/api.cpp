@@ -342,13 +342,20 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
   void* xdbl = w + al(tok * dim * e) + 2 * al(tok * dstate * e);
   void* scan_ws = static_cast<uint8_t*>(xdbl) + s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  const s6::ScanPlan plan = s6::plan_scan(batch, seqlen, dim, dstate);
+  // Opt-in (MAMBA_MI355X_FUSED_DT=1): the workgroup engine projects dt itself
+  // on the matrix cores (no delta tensor).  Off by default: the scan is
+  // VALU-bound and the extra per-tile work there costs about what the separate
+  // dt projection GEMM does.
+  const char* fenv = std::getenv("MAMBA_MI355X_FUSED_DT");
+  const bool fused = tokens && plan.engine == s6::kEngineWg && s6::fused_dt_supported(dstate, dt_rank, io_dtype) &&
+                     aligned16(W_dt) && fenv && fenv[0] == '1';
   if (tokens) {
-    s6::SelArgs sa{x, W_x, W_dt, delta, Bm, Cm, xdbl, batch, seqlen, dim, dstate, dt_rank,
+    s6::SelArgs sa{x, W_x, W_dt, fused ? nullptr : delta, Bm, Cm, xdbl, batch, seqlen, dim, dstate, dt_rank,
                    s6::selection_ld(dt_rank, dstate)};
     hipError_t e1 = s6::launch_selection(sa, io_dtype, hs);
     if (e1 != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e1));
   }
-  const s6::ScanPlan plan = s6::plan_scan(batch, seqlen, dim, dstate);
   s6::ScanArgs a{};
   a.u = x;
   a.delta = delta;
@@ -367,6 +374,13 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
   a.chunk_len = plan.chunk_len;
   a.nchunks = plan.nchunks;
   a.softplus = delta_softplus != 0;
+  if (fused) {
+    a.delta = nullptr;
+    a.dtlow = xdbl;
+    a.Wdt = W_dt;
+    a.R = dt_rank;
+    a.ldr = s6::selection_ld(dt_rank, dstate);
+  }
   hipError_t e2 = s6::launch_scan(a, plan, io_dtype, (int)dstate, tokens ? scan_ws : nullptr, hs);
   if (e2 != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e2));
   return MAMBA_OK;

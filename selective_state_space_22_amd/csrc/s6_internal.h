@@ -29,7 +29,16 @@ struct ScanArgs {
   int64_t chunk_len;
   int32_t nchunks;
   int32_t softplus;
+  // Fused dt projection (workgroup engine only): when dtlow is set, the raw dt
+  // is dtlow[token, :R] . Wdt[channel, :R] computed on the matrix cores and
+  // `delta` is not read.  dtlow: (batch*L, ldr), Wdt: (D, R), both I/O type.
+  const void* dtlow = nullptr;
+  const void* Wdt = nullptr;
+  int64_t R = 0, ldr = 0;
 };
+
+// Largest dt rank the fused projection keeps in registers (eight 64-byte K slices).
+bool fused_dt_supported(int64_t N, int64_t R, int io);
 
 struct StepArgs {
   float* state;
@@ -152,7 +161,7 @@ struct SelArgs {
   const void* x;    // (M, D)
   const void* Wx;   // (R + 2N, D)
   const void* Wdt;  // (D, R)
-  void* delta;      // (M, D)
+  void* delta;      // (M, D); null: only xdbl, B and C (the scan projects dt itself)
   void* Bout;       // (M, N)
   void* Cout;       // (M, N)
   void* xdbl;       // workspace (M, ldx)

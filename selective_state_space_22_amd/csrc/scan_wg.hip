@@ -88,7 +88,30 @@ struct BufIo<float> {
 // initial state), so that later waits only have to cover the tile prefetches.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <typename IO, int N, int W, int T, int MODE>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDtSlices = 8;  // 64-byte K slices of the fused dt projection kept in registers
+
+// One 64-byte K slice of the dt projection on the matrix cores (16 x 16 output tile).
+template <typename IO>
+__device__ __forceinline__ f32x4 dt_mfma(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 dt_mfma<uint16_t>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 dt_mfma<float>(u32x4 a, u32x4 b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+template <typename IO, int N, int W, int T, int MODE, bool FDT>
 struct WgScan {
   static constexpr int S = N / W;                 // states per wave
   static constexpr int TW = T / W;                // front-end / epilogue tokens per wave per tile
@@ -118,6 +141,7 @@ struct WgScan {
     __attribute__((aligned(16))) float bc[kSlots][T][W][BCW];  // per token and wave: B of its states, then C
     float yp[kOut ? 2 : 1][T][W][64];            // partial readouts
     float sdt[W][64];                            // split mode: partial sums of dt
+    float raw[FDT ? 2 : 1][T][64];               // fused dt projection: raw dt per (token, channel)
     int item[2];
   };
 
@@ -134,6 +158,11 @@ struct WgScan {
   bool dvalid;
   uint32_t chan_off;  // byte offset of this lane's channel in a token row (out of range if d >= D)
   __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_out, r_B, r_C;
+  // fused dt projection: waves 0..3 own channels 16w..16w+15 of the block
+  static_assert(!FDT || T == 16, "fused dt projection works on 16-token tiles");
+  __amdgpu_buffer_rsrc_t r_dtl, r_wdt;
+  u32x4 wdt[kDtSlices], dta[kDtSlices];
+  int nks;
   float a2[S], ka[S], ah[S], h[S];
   float bias, dskip;
   float dsum, dcomp;  // compensated sum of dt (split mode, first pass)
@@ -157,7 +186,7 @@ struct WgScan {
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
       const uint32_t off = base + (uint32_t)(W * i) * row;
-      r.dl[i] = BufIo<IO>::load(r_dl, off);
+      if (!FDT) r.dl[i] = BufIo<IO>::load(r_dl, off);
       r.uu[i] = BufIo<IO>::load(r_u, off);
       if (kOut) r.zz[i] = BufIo<IO>::load(r_z, off);
     }
@@ -177,6 +206,39 @@ struct WgScan {
     }
   }
 
+  // Fused dt projection.  Operands straight from global memory in the MFMA
+  // layout (lane l: row l % 16, the 16 bytes at offset 16 (l / 16) of each
+  // 64-byte K slice); K slices past R and rows past the chunk or D read zero.
+  // Waves 0..3 project dt for every tile.  (Alternating tiles between the two
+  // groups of four waves measured slower: the extra registers cost more than
+  // the balance gains.)
+  __device__ __forceinline__ bool dt_group(int) const { return w < 4; }
+  __device__ __forceinline__ void load_dt(int k) {
+    if (!FDT || !dt_group(k)) return;
+    const uint32_t ldb = (uint32_t)(A.s.ldr * kIo);
+    const uint32_t rbytes = (uint32_t)(A.s.R * kIo);
+    const uint32_t row = (uint32_t)(k * T + (lane & 15));
+#pragma unroll
+    for (int ks = 0; ks < kDtSlices; ++ks) {
+      const uint32_t kb = (uint32_t)ks * 64u + 16u * (lane >> 4);
+      dta[ks] = __builtin_amdgcn_raw_buffer_load_b128(r_dtl, ks < nks && kb < rbytes ? row * ldb + kb : kOutOfRange,
+                                                      0, 0);
+    }
+  }
+  // raw dt of tile k's 16 tokens for channels 16w..16w+15 into raw slot k & 1
+  __device__ __forceinline__ f32x4 mfma_dt() const {
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kDtSlices; ++ks)
+      if (ks < nks) acc = dt_mfma<IO>(dta[ks], wdt[ks], acc);
+    return acc;
+  }
+  __device__ __forceinline__ void store_dt(const f32x4& acc, int k) {
+    if (!FDT || !dt_group(k)) return;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sm.raw[k & 1][4 * (lane >> 4) + rr][16 * (w & 3) + (lane & 15)] = acc[rr];
+  }
+
   // Front end of tile k into slot f3 of fr and bc.
   __device__ __forceinline__ void front(const Regs& r, int k, int f3) {
     const int nv = tile_valid(k);
@@ -185,7 +247,8 @@ struct WgScan {
     for (int i = 0; i < TW; ++i) {
       const int j = w + W * i;
       const float x = BufIo<IO>::widen(r.uu[i]);
-      TokenFront f = make_front(BufIo<IO>::widen(r.dl[i]), bias, sp);
+      const float raw = FDT ? sm.raw[k & 1][j][lane] : BufIo<IO>::widen(r.dl[i]);
+      TokenFront f = make_front(raw, bias, sp);
       sm.fr[f3][j][lane] = make_float4(f.dt, f.dt2, x, kOut ? BufIo<IO>::widen(r.zz[i]) : 0.0f);
       if (MODE == kModeAgg) {  // Kahan sum of dt over this wave's valid tokens
         const float yk = (j < nv ? f.dt : 0.0f) - dcomp;
@@ -307,6 +370,22 @@ struct WgScan {
       r_out = make_rsrc(static_cast<const IO*>(A.s.out) + row0 * A.s.D, kOut ? span : 0u);
       r_B = make_rsrc(static_cast<const IO*>(A.s.B) + row0 * N, bspan);
       r_C = make_rsrc(static_cast<const IO*>(A.s.C) + row0 * N, bspan);
+      if (FDT) {
+        r_dtl = make_rsrc(static_cast<const IO*>(A.s.dtlow) + row0 * A.s.ldr, (uint32_t)((t1 - t0) * A.s.ldr * kIo));
+        const int64_t c0 = (d - lane) + 16 * (w & 3);  // first channel of this wave's group
+        const int64_t rows = A.s.D - c0 < 16 ? (A.s.D - c0 > 0 ? A.s.D - c0 : 0) : 16;
+        r_wdt = make_rsrc(static_cast<const IO*>(A.s.Wdt) + c0 * A.s.R, (uint32_t)(rows * A.s.R * kIo));
+        nks = (int)((A.s.R * kIo + 63) / 64);
+        if (w < 4) {
+          const uint32_t rbytes = (uint32_t)(A.s.R * kIo);
+#pragma unroll
+          for (int ks = 0; ks < kDtSlices; ++ks) {
+            const uint32_t kb = (uint32_t)ks * 64u + 16u * (lane >> 4);
+            wdt[ks] = __builtin_amdgcn_raw_buffer_load_b128(
+                r_wdt, ks < nks && kb < rbytes ? (uint32_t)((lane & 15) * A.s.R * kIo) + kb : kOutOfRange, 0, 0);
+          }
+        }
+      }
     }
     const int nstate0 = w * S;
 #pragma unroll
@@ -360,7 +439,15 @@ struct WgScan {
     // tile pipeline: global loads one tile ahead, LDS slots rotating
     const int ntiles = (int)((t1 - t0 + T - 1) / T);
     Regs r;
+    if (FDT) {  // raw dt of tiles 0 and 1, operands of tile 2 in flight
+      load_dt(0);
+      if (dt_group(0)) store_dt(mfma_dt(), 0);
+      load_dt(1);
+      if (dt_group(1)) store_dt(mfma_dt(), 1);
+      load_dt(2);
+    }
     load(r, 0);
+    if (FDT) __syncthreads();
     front(r, 0, 0);
     load(r, 1);
     __syncthreads();
@@ -368,6 +455,7 @@ struct WgScan {
     // of tile k: it reads the yp slot of k-1 (next written by the scan of k+1,
     // after this interval's barrier) and the fr slot of k-1 (next written by
     // the front end of k+2, also after it).
+    static_assert(!FDT || kSlots == 2, "fused dt projection uses the two-slot pipeline");
     if (kSlots == 3) {
       int f3 = 0;   // slot of tile k
       int f3p = 2;  // slot of tile k - 1
@@ -392,8 +480,15 @@ struct WgScan {
         const int f2 = k & 1;
         if (k > 0) epilogue(k - 1, f2 ^ 1, f2 ^ 1);
         front(r, k + 1, f2 ^ 1);
+        // fused dt projection of tile k+2: issued before the scan, its result
+        // (raw slot k & 1, last read by front(k) before the previous barrier)
+        // stored after it, so the matrix cores run while the VALU scans
+        f32x4 acc;
+        if (FDT && dt_group(k + 2)) acc = mfma_dt();
         load(r, k + 2);
+        load_dt(k + 3);
         scan(k, f2, f2);
+        if (FDT) store_dt(acc, k + 2);
         __syncthreads();
       }
       if (ntiles > 0) epilogue(ntiles - 1, (ntiles - 1) & 1, (ntiles - 1) & 1);
@@ -439,9 +534,9 @@ struct WgScan {
   }
 };
 
-template <typename IO, int N, int W, int T, int MODE>
+template <typename IO, int N, int W, int T, int MODE, bool FDT>
 __global__ __launch_bounds__(64 * W, S6_WG_PER_CU) void scan_wg_kernel(WgArgs a) {
-  using K = WgScan<IO, N, W, T, MODE>;
+  using K = WgScan<IO, N, W, T, MODE, FDT>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
   for (int round = 0;; ++round) {
@@ -458,7 +553,7 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-template <typename IO, int N, int W, int T>
+template <typename IO, int N, int W, int T, bool FDT>
 hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
   uint8_t* base = static_cast<uint8_t*>(ws);
   WgArgs a;
@@ -476,7 +571,7 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.ticket = ctrl;
     a.carry = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.nitems = a.chains * p.nchunks;
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained>), dim3(p.grid), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained, FDT>), dim3(p.grid), block, 0, st, a);
   } else {
     a.s.agg_h = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N;
@@ -484,15 +579,21 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.ticket = ctrl;
     a.nitems = a.chains * (p.nchunks - 1);
     const unsigned g1 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg>), dim3(g1), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg, FDT>), dim3(g1), block, 0, st, a);
     const hipError_t ce = launch_chunk_carry(a.s, N, st);
     if (ce != hipSuccess) return ce;
     a.ticket = ctrl + 1;
     a.nitems = a.chains * p.nchunks;
     const unsigned g2 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut>), dim3(g2), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut, FDT>), dim3(g2), block, 0, st, a);
   }
   return hipGetLastError();
+}
+
+template <typename IO, int N, int W, int T>
+hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
+  if (s.dtlow) return launch_wg_t<IO, N, W, T, true>(s, p, ws, st);
+  return launch_wg_t<IO, N, W, T, false>(s, p, ws, st);
 }
 
 }  // namespace
@@ -505,17 +606,22 @@ int wg_waves(int64_t N) {
 }
 int wg_tile(int64_t) { return S6_WG_TILE; }
 
+bool fused_dt_supported(int64_t N, int64_t R, int io) {
+  const int64_t e = io == kIoBF16 ? 2 : 4;
+  return wg_supported(N) && S6_WG_TILE == 16 && R >= 1 && (R * e) % 16 == 0 && R * e <= 64 * kDtSlices;
+}
+
 hipError_t launch_scan_wg(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
   const bool bf = io == kIoBF16;
   if (N == 16 && p.waves == 8)
-    return bf ? launch_wg_t<uint16_t, 16, 8, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_t<float, 16, 8, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 16, 8, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_fdt<float, 16, 8, S6_WG_TILE>(s, p, ws, st);
   if (N == 16 && p.waves == 4)
-    return bf ? launch_wg_t<uint16_t, 16, 4, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_t<float, 16, 4, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 16, 4, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_fdt<float, 16, 4, S6_WG_TILE>(s, p, ws, st);
   if (N == 8)
-    return bf ? launch_wg_t<uint16_t, 8, 4, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_t<float, 8, 4, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 8, 4, S6_WG_TILE>(s, p, ws, st)
+              : launch_wg_fdt<float, 8, 4, S6_WG_TILE>(s, p, ws, st);
   return hipErrorInvalidValue;
 }
 

@@ -329,6 +329,7 @@ hipError_t launch_selection_t(const SelArgs& s, hipStream_t st) {
   const int64_t n = M * W;
   hipLaunchKernelGGL((xproj_reduce_kernel<IO>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part,
                      (int64_t)parts, M, s.R, s.N, xdbl, s.ldx, static_cast<IO*>(s.Bout), static_cast<IO*>(s.Cout));
+  if (!s.delta) return hipGetLastError();  // dt projection fused into the scan
   GemmArgs g2{xdbl, s.Wdt, s.delta, M, s.D, s.R, s.ldx, s.R, s.D};
   return gemm_nt<IO, IO>(g2, st);
 }

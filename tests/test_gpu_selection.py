@@ -87,21 +87,40 @@ def test_selection_mamba3b_layer_sampled_rows():
     assert max(errs) <= TOL["bf16"], errs
 
 
-@pytest.mark.parametrize("case", [(1, 256, 64, 16, "f32"), (2, 300, 130, 16, "f32"), (2, 1000, 1536, 16, "bf16")],
-                         ids=str)
-def test_ssm_matches_selection_then_scan_oracle(case):
+SSM_CASES = [
+    # batch, L, D, N, io, dt rank (None: d_model/16).  With the fused projection switched on, the
+    # workgroup engine projects dt on the matrix cores when the rank's rows are 16-byte
+    # multiples; otherwise (and by default) a GEMM writes delta
+    (1, 256, 64, 16, "f32", None),       # R 2: unfused
+    (2, 300, 130, 16, "f32", None),      # R 5: unfused
+    (2, 1000, 1536, 16, "bf16", None),   # R 48: fused, chained chunks
+    (2, 300, 256, 16, "f32", 8),         # fused fp32 (four MFMAs per K slice), ragged tail
+    (1, 777, 5120, 16, "bf16", 160),     # fused, Mamba-3B width and rank
+    (2, 400, 128, 8, "bf16", 16),        # fused, N = 8 (four waves)
+    (1, 8192, 64, 16, "f32", 8),         # fused, one channel block: two-pass chunked mode
+    (2, 129, 200, 16, "bf16", 256),      # fused at the largest rank kept in registers
+]
+
+
+@pytest.mark.parametrize("fused", ["on", "off"])
+@pytest.mark.parametrize("case", SSM_CASES, ids=str)
+def test_ssm_matches_selection_then_scan_oracle(case, fused, monkeypatch):
     _need_gpu()
     from selective_state_space_22_amd import mamba_ssm_fwd
 
-    batch, L, D, N, io = case
-    R = W.dt_rank_for(D)
-    _announce(f"ssm (selection + scan) {case} R {R}")
+    batch, L, D, N, io, R = case
+    R = R or W.dt_rank_for(D)
+    monkeypatch.setenv("MAMBA_MI355X_FUSED_DT", "1" if fused == "on" else "0")
+    _announce(f"ssm (selection + scan) {case} R {R} fused={fused}")
     inp, sw = _inputs(batch, L, D, N, R, io, seed=400 + L)
     d = to_device(inp)
     out, last = mamba_ssm_fwd(d["u"], torch_io(sw.W_x, io, "cuda"), torch_io(sw.W_dt, io, "cuda"), d["A"], z=d["z"],
                               dt_bias=d["delta_bias"], Dskip=d["Dskip"])
     torch.cuda.synchronize()
-    delta, B, C = oracle.selection(inp.u, sw.W_x, sw.W_dt, N, store=_store(io))
+    # the fused path keeps the projected dt in fp32 (no delta tensor is stored)
+    e = 2 if io == "bf16" else 4
+    fused_path = fused == "on" and N in (8, 16) and (R * e) % 16 == 0 and R * e <= 512
+    delta, B, C = oracle.selection(inp.u, sw.W_x, sw.W_dt, N, store=_store(io), store_delta=not fused_path)
     ro, rl = oracle.scan(inp.u, delta, inp.A, B, C, inp.delta_bias, inp.Dskip, inp.z, True)
     eo, el = parity_error(to_host(out), ro), parity_error(to_host(last), rl)
     print(f"{case}: out {eo:.2e} last_state {el:.2e}")

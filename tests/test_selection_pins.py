@@ -95,3 +95,13 @@ def test_store_applies_to_xdbl_and_results_only():
     xdbl = q(x @ W_x.T)
     assert np.array_equal(B, xdbl[..., R:R + N]) and np.array_equal(C, xdbl[..., R + N:])
     assert np.array_equal(delta, q(xdbl[..., :R] @ W_dt.T))
+
+
+def test_store_delta_false_keeps_the_dt_projection_unrounded():
+    rng = np.random.default_rng(7)
+    D, N, R = 8, 2, 3
+    x = _rand(rng, 1, 5, D)
+    W_x, W_dt = _rand(rng, R + 2 * N, D), _rand(rng, D, R)
+    q = lambda a: np.round(np.asarray(a) * 64.0) / 64.0
+    delta, _, _ = oracle.selection(x, W_x, W_dt, N, store=q, store_delta=False)
+    assert np.array_equal(delta, q(x @ W_x.T)[..., :R] @ W_dt.T)
