@@ -11,6 +11,8 @@ Two independent implementations of the same definition live here:
     with a Python loop over tokens, used to cross-check the C code;
   * ``scan_bwd``: the C oracle's backward, the derivative of the same
     definition, pinned against central finite differences of ``scan``;
+  * ``scan_complex``: the forward with complex diagonal A (the page's
+    -1/2 + ni initialisation), real x, B, C and output Re(C . h);
   * ``selection``: the section 3.2 projections (B, C = Linear_N(x), dt from a
     rank-R projection of x expanded to the D channels), fp64 matrix products.
 Both follow "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
@@ -59,6 +61,9 @@ def _load():
         lib.s6_oracle_step.restype = ctypes.c_int
         lib.s6_oracle_scan_bwd.argtypes = [I64, I64, I64, I64] + [P] * 8 + [ctypes.c_int] + [P] * 12 + [ctypes.c_int]
         lib.s6_oracle_scan_bwd.restype = ctypes.c_int
+        lib.s6_oracle_scan_complex.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
+                                               ctypes.c_int]
+        lib.s6_oracle_scan_complex.restype = ctypes.c_int
         lib.s6_oracle_max_threads.argtypes = []
         lib.s6_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -115,6 +120,27 @@ def step(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus
     if rc != 0:
         raise RuntimeError(f"s6_oracle_step failed with {rc}")
     return out, st
+
+
+def scan_complex(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, softplus=True, h0=None,
+                 nthreads: int | None = None):
+    """fp64 forward scan with complex diagonal A (D, N) (a numpy complex array).
+    Returns (out (batch, L, D) real, last_state (batch, D, N) complex); h0 complex or None."""
+    u, delta, B, C = (_f64(x) for x in (u, delta, B, C))
+    delta_bias, Dskip, z = (_f64(x) for x in (delta_bias, Dskip, z))
+    Ac = np.ascontiguousarray(np.stack([np.real(A), np.imag(A)], axis=-1), dtype=np.float64)
+    h0c = None if h0 is None else np.ascontiguousarray(np.stack([np.real(h0), np.imag(h0)], axis=-1), np.float64)
+    batch, L, D = u.shape
+    N = Ac.shape[1]
+    out = np.empty((batch, L, D))
+    last = np.empty((batch, D, N, 2))
+    nt = nthreads if nthreads else max_threads()
+    rc = _load().s6_oracle_scan_complex(batch, L, D, N, _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(Ac), _ptr(B),
+                                        _ptr(C), _ptr(Dskip), _ptr(z), int(bool(softplus)), _ptr(h0c), _ptr(out),
+                                        _ptr(last), nt)
+    if rc != 0:
+        raise RuntimeError(f"s6_oracle_scan_complex failed with {rc}")
+    return out, last[..., 0] + 1j * last[..., 1]
 
 
 def scan_bwd(u, delta, A, B, C, dout, delta_bias=None, Dskip=None, z=None, softplus=True, h0=None, dlast=None,

@@ -262,3 +262,64 @@ int s6_oracle_scan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N,
     }
     return bad ? 2 : 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Complex diagonal A (the -1/2 + ni row of the A-initialisation table of the
+ * same page).  The page gives only the values of A; the reading taken here is
+ * the plainest one the rest supports: delta, x, B and C stay real, A_n is
+ * complex, so the state is complex with
+ *     Abar_n = exp(dt A_n),   Bbar_n = (exp(dt A_n) - 1)/(dt A_n) * dt * B_n
+ *     h_t = Abar h_{t-1} + Bbar x_t,   y_t = Re(sum_n C_n h_t[n])
+ * (eq. (2), (3a), (3b) with complex A), then the same skip and gate.
+ * A is given as (D, N, 2) = (re, im); h0 and last_state as (batch, D, N, 2).
+ * ------------------------------------------------------------------------ */
+#include <complex.h>
+
+static double complex phi1c(double complex a) {
+    /* (e^a - 1)/a, limit 1 at a = 0.  Below |a| = 1e-2 its Taylor series
+     * 1 + a/2 + a^2/6 + a^3/24 + a^4/120 (next term |a|^5/720 < 1.4e-13);
+     * above, the quotient, whose cancellation costs at most ~2e-14. */
+    if (cabs(a) < 1e-2) return 1.0 + a * (1.0 / 2.0 + a * (1.0 / 6.0 + a * (1.0 / 24.0 + a / 120.0)));
+    return (cexp(a) - 1.0) / a;
+}
+
+int s6_oracle_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N,
+                           const double* u, const double* delta, const double* delta_bias,
+                           const double* A, const double* B, const double* C,
+                           const double* Dskip, const double* z, int softplus_flag,
+                           const double* h0, double* out, double* last_state, int nthreads) {
+    if (batch < 0 || L < 0 || D < 0 || N <= 0 || !A || !out) return 1;
+    if (L > 0 && (!u || !delta || !B || !C)) return 1;
+    if (nthreads <= 0) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads) reduction(| : bad)
+    for (int64_t unit = 0; unit < batch * D; ++unit) {
+        int64_t b = unit / D, d = unit % D;
+        double complex* h = (double complex*)malloc((size_t)N * sizeof(double complex));
+        if (!h) { bad |= 1; continue; }
+        for (int64_t n = 0; n < N; ++n)
+            h[n] = h0 ? h0[((b * D + d) * N + n) * 2] + I * h0[((b * D + d) * N + n) * 2 + 1] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t i = (b * L + t) * D + d;
+            double dt = token_dt(delta[i], delta_bias, d, softplus_flag);
+            double x = u[i];
+            double y = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double complex An = A[(d * N + n) * 2] + I * A[(d * N + n) * 2 + 1];
+                double complex a = dt * An;                     /* dt*A_n             */
+                double complex abar = cexp(a);                  /* eq. (2), Abar      */
+                double complex bbar = phi1c(a) * dt * B[(b * L + t) * N + n];
+                h[n] = abar * h[n] + bbar * x;                  /* eq. (3a)           */
+                y += C[(b * L + t) * N + n] * creal(h[n]);     /* eq. (3b), real part */
+            }
+            out[i] = finish(y, x, Dskip, d, z ? z + i : NULL);
+        }
+        if (last_state)
+            for (int64_t n = 0; n < N; ++n) {
+                last_state[((b * D + d) * N + n) * 2] = creal(h[n]);
+                last_state[((b * D + d) * N + n) * 2 + 1] = cimag(h[n]);
+            }
+        free(h);
+    }
+    return bad ? 2 : 0;
+}
