@@ -34,6 +34,9 @@ FLOPS_PER_TOKEN_CHANNEL = 15.0   # per (b, l, d): bias add, softplus (6), skip F
 # Backward, per (b, l, d, n) on top of the recomputed forward: gradient recurrence FMA, dC and dB products,
 # du FMA, d(beta) and d(Abar) products, ddt FMAs, d beta/d A (series or difference), two dA FMAs, state-gradient decay
 BWD_FLOPS_PER_ELEMENT = 22.0
+# Complex A, per (b, l, d, n): dt*A (2), |Abar| exp and the sin/cos pair (3), Abar (2), (Abar-1)/A (7),
+# B*x (1), beta*Bx (2), complex h update (8), readout FMA on Re h (2)
+COMPLEX_FLOPS_PER_ELEMENT = 27.0
 
 
 def algorithmic_bytes(batch, L, D, N, io_bytes, decode=False):
@@ -83,7 +86,12 @@ def cpu_baseline(inp, name, which="fwd"):
             if el >= min_s or calls >= max_calls:
                 return el / calls, calls
 
-    if which == "bwd":
+    if which == "complex":
+        Ac = W.a_init_complex(sub.dim, sub.dstate).astype(np.complex128)
+        dt, calls = timed(lambda: oracle.scan_complex(args[0], args[1], Ac, args[3], args[4], args[5], args[6],
+                                                      args[7], softplus=True, nthreads=threads))
+        what += " (complex A)"
+    elif which == "bwd":
         if name != "million_tokens":  # one batch row: the backward oracle is ~3x the forward's work
             sub = W.channel_subset(inp, [0], np.arange(inp.dim))
             what = f"batch row 0 of {inp.batch}, all channels and tokens"
@@ -155,8 +163,9 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "sel", "ssm"], default="fwd",
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "sel", "ssm", "complex"], default="fwd",
                     help="fwd: mamba_scan_fwd (the headline); bwd: mamba_scan_bwd on the same workload; "
+                         "complex: mamba_scan_fwd_complex with A_n = -1/2 + n i; "
                          "sel: the selection projections (mamba_selection_fwd, dt rank d_model/16); "
                          "ssm: selection then scan (mamba_ssm_fwd)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -184,7 +193,8 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     if args.which != "fwd" and w.decode_steps > 0:
-        print("bench.py: --pass bwd/sel/ssm apply to the full-sequence workloads, not decode", file=sys.stderr)
+        print("bench.py: --pass bwd/sel/ssm/complex apply to the full-sequence workloads, not decode",
+              file=sys.stderr)
         sys.exit(2)
     inp = W.generate_workload(args.workload)
     tdt = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -271,6 +281,22 @@ def main():
             units = w.elements
             bytes_per_step = (3 * io_bytes * M * w.dim + io_bytes * ((R + 2 * w.dstate) * w.dim + w.dim * R)
                               + 8 * w.dim + 4 * w.dim * w.dstate + 4 * w.batch * w.dim * w.dstate)
+    elif args.which == "complex":
+        Ac = torch.from_numpy(W.a_init_complex(w.dim, w.dstate)).to(dev)
+        out = torch.empty_like(u)
+        last = torch.empty((w.batch, w.dim, w.dstate, 2), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(binding.mamba_scan_fwd_complex_workspace_size(w.batch, w.seqlen, w.dim, w.dstate,
+                                                                          1 if w.io == "bf16" else 0), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.mamba_scan_fwd_complex(u, delta, Ac, B, C, bias, dskip, z, True, None, out=out, last_state=last,
+                                           workspace=ws)
+
+        units = w.elements
+        # as the real scan, with A (D, N) and last_state (batch, D, N) complex
+        bytes_per_step = (algorithmic_bytes(w.batch, w.seqlen, w.dim, w.dstate, io_bytes)
+                          + 4 * w.dim * w.dstate + 4 * w.batch * w.dim * w.dstate)
     else:
         out = torch.empty_like(u)
         last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
@@ -328,6 +354,9 @@ def main():
     flops = units * FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
     tflops = flops / (ms * 1e-3) / 1e12
     traffic = measured_traffic(args.workload, args.which)
+    if args.which == "complex":
+        flops = units * COMPLEX_FLOPS_PER_ELEMENT + (units / w.dstate) * FLOPS_PER_TOKEN_CHANNEL
+        tflops = flops / (ms * 1e-3) / 1e12
     if args.which == "bwd":
         # per (b, l, d, n): forward recompute (9) as above plus the reverse step (~20 fp32 ops, FMA = 2)
         flops = units * (FLOPS_PER_ELEMENT + BWD_FLOPS_PER_ELEMENT) + (units / w.dstate) * 30.0
@@ -352,7 +381,8 @@ def main():
         "metric": {"fwd": metric_name(),
                    "bwd": "selective-scan bwd elements(B*L*D*N)/s (all gradients, states recomputed)",
                    "sel": "selection projections: delta elements (B*L*D)/s (x_proj + dt_proj GEMMs)",
-                   "ssm": "selective SSM from x: elements(B*L*D*N)/s (selection GEMMs + scan)"}[args.which],
+                   "ssm": "selective SSM from x: elements(B*L*D*N)/s (selection GEMMs + scan)",
+                   "complex": "selective-scan fwd with complex A: elements(B*L*D*N)/s"}[args.which],
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,
@@ -373,7 +403,7 @@ def main():
         "algorithmic_bytes_per_step": bytes_per_step,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and args.which in ("fwd", "bwd"):
+    if not args.no_cpu_baseline and args.which in ("fwd", "bwd", "complex"):
         rec["cpu_baseline"] = cpu_baseline(inp, args.workload, args.which)
     print(json.dumps(rec), flush=True)
 

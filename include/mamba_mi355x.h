@@ -100,6 +100,30 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward selective scan with a complex diagonal A: the complex row
+ * A_n = -1/2 + n i of the A-initialisation ablation (section 6.5).  dt, u,
+ * B, C, z and out stay real; eq. (2) and (3a) are taken over the complex
+ * numbers and the output reads the real part:
+ *     Abar = exp(dt*A_n),   h_t = Abar*h_{t-1} + (Abar - 1)/A_n * B_t,n * x_t,
+ *     y_t  = sum_n C_t,n * Re(h_t,n),   out = (y + Dskip*x) * SiLU(z).
+ *   A                : (dim, dstate, 2)          float, re/im pairs
+ *   h0, last_state   : (batch, dim, dstate, 2)   float, re/im pairs, nullable
+ *   every other argument as for mamba_scan_fwd.  A_n = 0 is allowed (the
+ *   input weight is then dt).  With every Im A_n = 0 the result equals
+ *   mamba_scan_fwd's on the real parts.
+ * Limits as for mamba_scan_fwd.  Workspace: about 8*N bytes per (batch row,
+ * channel) and sequence chunk.
+ */
+size_t mamba_scan_fwd_complex_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                             int io_dtype);
+int mamba_scan_fwd_complex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                           const void* u, const void* delta, const float* delta_bias, const float* A,
+                           const void* B, const void* C, const float* Dskip, const void* z,
+                           int delta_softplus, const float* h0,
+                           void* out, float* last_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step (section 5: constant time per token, the state is
  * the whole memory): every (batch row, channel) advances by one token.
  *   state            : (batch, dim, dstate) float, read and overwritten in place

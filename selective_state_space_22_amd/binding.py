@@ -59,6 +59,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_ssm_fwd_workspace_size.restype = ctypes.c_size_t
     lib.mamba_ssm_fwd.argtypes = [I64, I64, I64, I64, I64, I, P, P, P, P, P, P, P, I, P, P, P, P, ctypes.c_size_t, P]
     lib.mamba_ssm_fwd.restype = I
+    lib.mamba_scan_fwd_complex_workspace_size.argtypes = [I64, I64, I64, I64, I]
+    lib.mamba_scan_fwd_complex_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd_complex.argtypes = lib.mamba_scan_fwd.argtypes
+    lib.mamba_scan_fwd_complex.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -142,6 +146,65 @@ def mamba_scan_fwd(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta
     if st != 0:
         raise MambaError("mamba_scan_fwd", st)
     return out, last_state
+
+
+def mamba_scan_fwd_complex_workspace_size(batch: int, seqlen: int, dim: int, dstate: int, io_dtype: int) -> int:
+    return int(load_library().mamba_scan_fwd_complex_workspace_size(batch, seqlen, dim, dstate, io_dtype))
+
+
+def _re_im(t, name):
+    """A complex64 tensor as its float32 (..., 2) re/im view; float32 (..., 2) tensors pass through."""
+    import torch
+
+    if t is None:
+        return None
+    if t.is_complex():
+        if t.dtype != torch.complex64:
+            raise TypeError(f"{name} must be complex64, got {t.dtype}")
+        return torch.view_as_real(t.resolve_conj())
+    return t
+
+
+def mamba_scan_fwd_complex(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
+                           out=None, last_state=None, workspace=None, return_last_state=True):
+    """Forward selective scan with a complex diagonal A; x, dt, B, C and out are real, y = Re(C . h).
+
+    A: (D, N) complex64 or (D, N, 2) float32 re/im; h0 likewise (batch, D, N).  Other
+    arguments as for mamba_scan_fwd.  Returns (out, last_state) with last_state
+    complex64 (batch, D, N)."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = u.shape
+    N = A.shape[1]
+    A = _re_im(A, "A")
+    h0 = _re_im(h0, "h0")
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty_like(u)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, D, N, 2), dtype=f32, device=dev)
+    else:
+        last_state = _re_im(last_state, "last_state")
+    ws_bytes = mamba_scan_fwd_complex_workspace_size(batch, L, D, N, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_ptr = _ptr(workspace, "workspace", device=dev)
+    st = lib.mamba_scan_fwd_complex(
+        batch, L, D, N, io,
+        _ptr(u, "u", u.dtype, (batch, L, D), dev), _ptr(delta, "delta", u.dtype, (batch, L, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N, 2), dev),
+        _ptr(B, "B", u.dtype, (batch, L, N), dev), _ptr(C, "C", u.dtype, (batch, L, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, L, D), dev),
+        int(bool(delta_softplus)), _ptr(h0, "h0", f32, (batch, D, N, 2), dev),
+        _ptr(out, "out", u.dtype, (batch, L, D), dev),
+        _ptr(last_state, "last_state", f32, (batch, D, N, 2), dev),
+        ws_ptr, workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_scan_fwd_complex", st)
+    return out, (torch.view_as_complex(last_state) if last_state is not None else None)
 
 
 def mamba_state_update(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True,

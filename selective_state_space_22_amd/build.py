@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba_mi355x.so")
-SOURCES = ["api.cpp", "scan_kernels.hip", "scan_wg.hip", "scan_bwd.hip", "selection.hip"]
+SOURCES = ["api.cpp", "scan_kernels.hip", "scan_wg.hip", "scan_bwd.hip", "selection.hip", "scan_complex.hip"]
 ARCH = os.environ.get("MAMBA_MI355X_ARCH", "gfx950")
 
 

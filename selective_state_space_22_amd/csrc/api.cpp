@@ -132,6 +132,68 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
   return MAMBA_OK;
 }
 
+size_t mamba_scan_fwd_complex_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                                             int io_dtype) {
+  if (check_shape("mamba_scan_fwd_complex_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK)
+    return 0;
+  return s6::plan_scan_complex(batch, seqlen, dim, dstate).ws_bytes;
+}
+
+int mamba_scan_fwd_complex(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                           const void* u, const void* delta, const float* delta_bias, const float* A,
+                           const void* B, const void* C, const float* Dskip, const void* z,
+                           int delta_softplus, const float* h0,
+                           void* out, float* last_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* where = "mamba_scan_fwd_complex";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  const bool tokens = batch > 0 && seqlen > 0 && dim > 0;
+  const bool chans = batch > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(u, tokens, "u");
+  pc.req(delta, tokens, "delta");
+  pc.req(A, tokens, "A");
+  pc.req(B, tokens, "B");
+  pc.req(C, tokens, "C");
+  pc.req(out, tokens, "out");
+  pc.opt(delta_bias, "delta_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(z, "z");
+  pc.opt(h0, "h0");
+  pc.opt(last_state, "last_state");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (!chans) return MAMBA_OK;
+  const s6::ScanPlan plan = s6::plan_scan_complex(batch, seqlen, dim, dstate);
+  if (tokens && plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  s6::ScanArgs a;
+  a.u = u;
+  a.delta = delta;
+  a.bias = delta_bias;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.dskip = Dskip;
+  a.z = z;
+  a.h0 = h0;
+  a.out = out;
+  a.last = last_state;
+  a.agg_h = nullptr;
+  a.agg_s = nullptr;
+  a.batch = batch;
+  a.L = seqlen;
+  a.D = dim;
+  a.chunk_len = plan.chunk_len;
+  a.nchunks = plan.nchunks;
+  a.softplus = delta_softplus != 0;
+  hipError_t e =
+      s6::launch_scan_complex(a, plan, io_dtype, (int)dstate, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
 int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
                        const void* u, const void* delta, const float* delta_bias, const float* A,
                        const void* B, const void* C, const float* Dskip, const void* z,

@@ -103,6 +103,12 @@ int wg_tile(int64_t N);
 
 bool dstate_supported(int64_t N);
 
+// Complex diagonal A (scan_complex.hip): A, h0 and last are (.., N, 2) re/im
+// float; agg_h is (batch, nchunks, D, N, 2).  The plan is the lane engine's.
+ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N);
+hipError_t launch_scan_complex(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace,
+                               hipStream_t stream);
+
 // ---------------------------------------------------------------- backward (scan_bwd.hip)
 
 constexpr int kBwdTile = 8;  // tokens per tile of the backward passes

@@ -1,0 +1,274 @@
+// scan_complex.hip -- forward selective scan with a complex diagonal A on gfx950.
+//
+// The A-initialisation ablation of "Mamba 状态空间模型原理与 Transformer 对比"
+// (kb.agiseed.tech) lists a complex initialisation A_n = -1/2 + n i.  With a
+// complex A and everything else as in the real scan (real dt, x, B, C), eq. (2)
+// and (3a) make the state complex:
+//     Abar_n = e^{dt A_n} = e^{dt Re A_n} (cos(dt Im A_n) + i sin(dt Im A_n))
+//     beta_n = (Abar_n - 1) / A_n        (the ZOH input weight, dt + dt^2 A_n/2 near 0)
+//     h_t    = Abar h_{t-1} + beta B_t x_t,     y_t = Re(C_t . h_t)   (eq. (3b), real part)
+// followed by the same skip and SiLU gate.
+//
+// Mapping: the lane engine's -- one lane per (batch row, channel), its N
+// complex states in VGPRs, B_t and C_t wave-uniform -- with the same split of
+// long sequences into chunks: chunk end states from zero and the chunk sum of
+// dt, a carry pass composing them with h_in(g+1) = e^{A sum dt} h_in(g) + b_g,
+// then every chunk from its carry-in.  v_sin_f32 / v_cos_f32 take their
+// argument in revolutions; it is reduced to [0, 1) with v_fract_f32 first.
+#include <cstdlib>
+
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+namespace {
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+__device__ __forceinline__ float sin_rev(float r) { return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r)); }
+__device__ __forceinline__ float cos_rev(float r) { return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r)); }
+
+// Per (channel, state) constants.
+template <int N>
+struct CplxConst {
+  float re[N], im[N];  // A_n
+  float inv[N];        // 1 / |A_n|^2
+  float ar2[N];        // Re A_n * log2 e
+  float ai_rev[N];     // Im A_n / 2 pi
+  __device__ __forceinline__ void load(const float* A_row) {  // (N, 2) re, im
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      re[n] = A_row[2 * n];
+      im[n] = A_row[2 * n + 1];
+      inv[n] = rcp(__builtin_fmaf(re[n], re[n], im[n] * im[n]));
+      ar2[n] = re[n] * kLog2e;
+      ai_rev[n] = im[n] * kInv2Pi;
+    }
+  }
+};
+
+// Below |dt A_n| = 0.1 the input weight comes from the Taylor series of
+// (e^x - 1)/x to x^4 (truncation <= |x|^5/720 < 2e-8); above it from
+// (Abar - 1)/A_n, whose cancellation costs at most err(Abar)/0.1.
+constexpr float kCplxSeriesX2 = 0.01f;
+
+// One token for all N complex states; returns Re(C . h) when READ.
+template <int N, bool READ>
+__device__ __forceinline__ float ctoken(const CplxConst<N>& c, float dt, float x, const float* Bt, const float* Ct,
+                                        float (&hr)[N], float (&hi)[N]) {
+  float y = 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const float mag = ex2(dt * c.ar2[n]);
+    const float ang = dt * c.ai_rev[n];
+    const float abr = mag * cos_rev(ang), abi = mag * sin_rev(ang);
+    // (Abar - 1) conj(A) / |A|^2
+    const float er = abr - 1.0f;
+    const float gr = __builtin_fmaf(er, c.re[n], abi * c.im[n]) * c.inv[n];
+    const float gi = __builtin_fmaf(abi, c.re[n], -er * c.im[n]) * c.inv[n];
+    // dt (1 + x/2 + x^2/6 + x^3/24 + x^4/120), x = dt A_n
+    const float xr = dt * c.re[n], xi = dt * c.im[n];
+    float qr = __builtin_fmaf(xr, 1.0f / 120.0f, 1.0f / 24.0f), qi = xi * (1.0f / 120.0f);
+    float tr = __builtin_fmaf(xr, qr, __builtin_fmaf(-xi, qi, 1.0f / 6.0f));
+    float ti = __builtin_fmaf(xr, qi, xi * qr);
+    qr = __builtin_fmaf(xr, tr, __builtin_fmaf(-xi, ti, 0.5f));
+    qi = __builtin_fmaf(xr, ti, xi * tr);
+    tr = __builtin_fmaf(xr, qr, __builtin_fmaf(-xi, qi, 1.0f));
+    ti = __builtin_fmaf(xr, qi, xi * qr);
+    const bool small = __builtin_fmaf(xr, xr, xi * xi) < kCplxSeriesX2;
+    const float br = small ? dt * tr : gr;
+    const float bi = small ? dt * ti : gi;
+    const float bx = Bt[n] * x;
+    const float nr = __builtin_fmaf(abr, hr[n], __builtin_fmaf(-abi, hi[n], br * bx));
+    const float ni = __builtin_fmaf(abr, hi[n], __builtin_fmaf(abi, hr[n], bi * bx));
+    hr[n] = nr;
+    hi[n] = ni;
+    if (READ) y = __builtin_fmaf(Ct[n], nr, y);
+  }
+  return y;
+}
+
+template <typename IO, int N>
+__device__ __forceinline__ void load_bc(const IO* p, float (&v)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) v[n] = load_io(p, n);
+}
+
+struct CplxArgs {
+  ScanArgs s;   // A, h0 and last are (.., N, 2) float; agg_h is (batch, G, D, N, 2)
+};
+
+// Chunk end states from a zero start and chunk sums of dt (all chunks but the last).
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void cplx_chunk_state_kernel(CplxArgs c) {
+  const ScanArgs& a = c.s;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y, g = blockIdx.z;
+  if (d >= a.D) return;
+  const int64_t L = a.L, D = a.D;
+  const IO* u = static_cast<const IO*>(a.u);
+  const IO* dl = static_cast<const IO*>(a.delta);
+  const IO* Bp = static_cast<const IO*>(a.B);
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  CplxConst<N> cc;
+  cc.load(a.A + d * N * 2);
+  float hr[N], hi[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) hr[n] = hi[n] = 0.0f;
+  float s = 0.0f, sc = 0.0f;
+  const int64_t t0 = g * a.chunk_len;
+  const int64_t t1 = t0 + a.chunk_len < L ? t0 + a.chunk_len : L;
+  const bool sp = a.softplus != 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    const size_t i = ((size_t)b * L + t) * D + d;
+    float Bt[N];
+    load_bc<IO, N>(Bp + ((size_t)b * L + t) * N, Bt);
+    const TokenFront f = make_front(load_io(dl, i), bias, sp);
+    ctoken<N, false>(cc, f.dt, load_io(u, i), Bt, Bt, hr, hi);
+    const float yk = f.dt - sc;
+    const float tk = s + yk;
+    sc = (tk - s) - yk;
+    s = tk;
+  }
+  const size_t base = ((size_t)b * a.nchunks + g) * D + d;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    a.agg_h[(base * N + n) * 2] = hr[n];
+    a.agg_h[(base * N + n) * 2 + 1] = hi[n];
+  }
+  a.agg_s[base] = s;
+}
+
+// Carry pass: one lane per (batch, channel, state); agg_h then holds the state entering each chunk.
+template <int N>
+__global__ __launch_bounds__(256) void cplx_carry_kernel(CplxArgs c) {
+  const ScanArgs& a = c.s;
+  const int64_t lane = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t D = a.D;
+  if (lane >= a.batch * D * N) return;
+  const int64_t n = lane % N, d = (lane / N) % D, b = lane / (N * D);
+  const float ar2 = a.A[(d * N + n) * 2] * kLog2e;
+  const float ai_rev = a.A[(d * N + n) * 2 + 1] * kInv2Pi;
+  float cr = a.h0 ? a.h0[lane * 2] : 0.0f, ci = a.h0 ? a.h0[lane * 2 + 1] : 0.0f;
+  const int G = a.nchunks;
+  for (int g = 0; g < G - 1; ++g) {
+    const size_t base = ((size_t)b * G + g) * D + d;
+    const float sdt = a.agg_s[base];
+    const float mag = ex2(ar2 * sdt);
+    const float pr = mag * cos_rev(ai_rev * sdt), pi = mag * sin_rev(ai_rev * sdt);
+    const size_t k = (base * N + n) * 2;
+    const float br = a.agg_h[k], bi = a.agg_h[k + 1];
+    a.agg_h[k] = cr;
+    a.agg_h[k + 1] = ci;
+    const float nr = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, br));
+    const float ni = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, bi));
+    cr = nr;
+    ci = ni;
+  }
+  const size_t k = ((((size_t)b * G + (G - 1)) * D + d) * N + n) * 2;
+  a.agg_h[k] = cr;
+  a.agg_h[k + 1] = ci;
+}
+
+// Output pass: every chunk from its carry-in (or h0 / zero when unchunked).
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void cplx_output_kernel(CplxArgs c) {
+  const ScanArgs& a = c.s;
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y, g = blockIdx.z;
+  if (d >= a.D) return;
+  const int64_t L = a.L, D = a.D;
+  const IO* u = static_cast<const IO*>(a.u);
+  const IO* dl = static_cast<const IO*>(a.delta);
+  const IO* zp = static_cast<const IO*>(a.z);
+  const IO* Bp = static_cast<const IO*>(a.B);
+  const IO* Cp = static_cast<const IO*>(a.C);
+  IO* out = static_cast<IO*>(a.out);
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float dskip = a.dskip ? a.dskip[d] : 0.0f;
+  CplxConst<N> cc;
+  cc.load(a.A + d * N * 2);
+  float hr[N], hi[N];
+  const float* src = a.nchunks > 1 ? a.agg_h + (((size_t)b * a.nchunks + g) * D + d) * N * 2
+                                   : (a.h0 ? a.h0 + ((size_t)b * D + d) * N * 2 : nullptr);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    hr[n] = src ? src[2 * n] : 0.0f;
+    hi[n] = src ? src[2 * n + 1] : 0.0f;
+  }
+  const int64_t t0 = g * a.chunk_len;
+  const int64_t t1 = t0 + a.chunk_len < L ? t0 + a.chunk_len : L;
+  const bool sp = a.softplus != 0;
+  const bool has_z = zp != nullptr;
+  for (int64_t t = t0; t < t1; ++t) {
+    const size_t i = ((size_t)b * L + t) * D + d;
+    float Bt[N], Ct[N];
+    load_bc<IO, N>(Bp + ((size_t)b * L + t) * N, Bt);
+    load_bc<IO, N>(Cp + ((size_t)b * L + t) * N, Ct);
+    const float x = load_io(u, i);
+    const TokenFront f = make_front(load_io(dl, i), bias, sp);
+    const float y = ctoken<N, true>(cc, f.dt, x, Bt, Ct, hr, hi);
+    const float zv = has_z ? load_io(zp, i) : 0.0f;
+    store_io(out, i, epilogue(y, x, dskip, has_z, zv));
+  }
+  if (a.last && g == a.nchunks - 1) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      a.last[(((size_t)b * D + d) * N + n) * 2] = hr[n];
+      a.last[(((size_t)b * D + d) * N + n) * 2 + 1] = hi[n];
+    }
+  }
+}
+
+__global__ void cplx_empty_kernel(float* last, const float* h0, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) last[i] = h0 ? h0[i] : 0.0f;
+}
+
+template <typename IO, int N>
+hipError_t launch_cplx_t(const CplxArgs& c, int bs, hipStream_t st) {
+  const ScanArgs& a = c.s;
+  const dim3 block(bs);
+  const dim3 grid((unsigned)((a.D + bs - 1) / bs), (unsigned)a.batch, (unsigned)a.nchunks);
+  if (a.nchunks > 1) {
+    const dim3 g1((unsigned)((a.D + bs - 1) / bs), (unsigned)a.batch, (unsigned)(a.nchunks - 1));
+    hipLaunchKernelGGL((cplx_chunk_state_kernel<IO, N>), g1, block, 0, st, c);
+    const int64_t lanes = a.batch * a.D * N;
+    hipLaunchKernelGGL((cplx_carry_kernel<N>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, c);
+  }
+  hipLaunchKernelGGL((cplx_output_kernel<IO, N>), grid, block, 0, st, c);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_cplx_io(const CplxArgs& c, int N, int bs, hipStream_t st) {
+  switch (N) {
+    case 1: return launch_cplx_t<IO, 1>(c, bs, st);
+    case 2: return launch_cplx_t<IO, 2>(c, bs, st);
+    case 4: return launch_cplx_t<IO, 4>(c, bs, st);
+    case 8: return launch_cplx_t<IO, 8>(c, bs, st);
+    case 16: return launch_cplx_t<IO, 16>(c, bs, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan_complex(const ScanArgs& in, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
+  if (in.batch == 0 || in.D == 0) return hipSuccess;
+  if (in.L == 0) {
+    if (!in.last) return hipSuccess;
+    const int64_t count = in.batch * in.D * N * 2;
+    hipLaunchKernelGGL(cplx_empty_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, in.last, in.h0,
+                       count);
+    return hipGetLastError();
+  }
+  CplxArgs c{in};
+  c.s.chunk_len = p.chunk_len;
+  c.s.nchunks = p.nchunks;
+  c.s.agg_h = static_cast<float*>(ws);
+  c.s.agg_s = p.nchunks > 1 ? c.s.agg_h + (size_t)in.batch * p.nchunks * in.D * N * 2 : nullptr;
+  return io == kIoBF16 ? launch_cplx_io<uint16_t>(c, N, p.block, st) : launch_cplx_io<float>(c, N, p.block, st);
+}
+
+}  // namespace s6

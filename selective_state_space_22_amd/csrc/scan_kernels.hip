@@ -262,6 +262,13 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
   return plan_lane(batch, L, D, N);
 }
 
+ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  // The lane engine's chunking; each chunk aggregate holds N complex states.
+  ScanPlan p = plan_lane(batch, L, D, N);
+  p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (2 * N + 1) * sizeof(float) : 0;
+  return p;
+}
+
 template <typename IO, int N>
 static hipError_t launch_scan_t(const ScanArgs& a, const ScanPlan& p, hipStream_t s) {
   const int block = p.block;

@@ -114,6 +114,14 @@ def a_init(dim: int, dstate: int, kind: str = "s4d_real", rng: np.random.Generat
     raise ValueError(kind)
 
 
+def a_init_complex(dim: int, dstate: int) -> np.ndarray:
+    """Complex diagonal A of shape (D, N), complex64: A_n = -1/2 + n i, the complex
+    row of the A-initialisation ablation (same for every channel)."""
+    n = np.arange(dstate, dtype=np.float32)
+    row = (-0.5 + 1j * n).astype(np.complex64)
+    return np.ascontiguousarray(np.broadcast_to(row, (dim, dstate)))
+
+
 def softplus_inverse(y: np.ndarray) -> np.ndarray:
     """x such that log(1 + e^x) = y (input recipe for delta_bias), in float64."""
     y = np.asarray(y, dtype=np.float64)

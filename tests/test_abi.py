@@ -32,6 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
+                                    "mamba_scan_fwd_complex", "mamba_scan_fwd_complex_workspace_size",
                                     "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
                                     "mamba_selection_fwd_workspace_size", "mamba_ssm_fwd",
                                     "mamba_ssm_fwd_workspace_size", "mamba_state_update", "mamba_status_string",
@@ -209,3 +210,25 @@ def test_selection_and_ssm_validation(lib):
                None) == ERR_NULL
     assert ssm(1, 8, 64, 16, 0, 0, FAKE, None, FAKE, FAKE, None, FAKE, None, 1, None, FAKE, None, FAKE, nss,
                None) == ERR_DIM
+
+
+def test_complex_scan_validation_and_workspace(lib):
+    ws = binding.mamba_scan_fwd_complex_workspace_size
+    # short rows: one chunk, no workspace; long rows over few channels: (batch, chunks, D, 2N+1) floats
+    assert ws(1, 256, 64, 16, 0) == 0
+    w = ws(1, 1 << 20, 256, 16, 0)
+    assert w > 0 and w % (256 * 33 * 4) == 0
+    assert ws(1, 16, 64, 3, 0) == 0 and ws(1, 16, 64, 16, 9) == 0
+
+    def call(batch=1, L=8, D=64, N=16, io=0, u=FAKE, A=FAKE, out=FAKE, h0=None, ws_ptr=None, ws_bytes=0):
+        return lib.mamba_scan_fwd_complex(batch, L, D, N, io, u, FAKE, None, A, FAKE, FAKE, None, None, 1, h0, out,
+                                          None, ws_ptr, ws_bytes, None)
+
+    assert call(io=3) == ERR_DTYPE
+    assert call(N=5) == ERR_UNSUPPORTED
+    assert call(L=-1) == ERR_DIM
+    assert call(u=None) == ERR_NULL and call(A=None) == ERR_NULL and call(out=None) == ERR_NULL
+    assert call(A=FAKE + 8) == ERR_ALIGN and call(h0=FAKE + 4) == ERR_ALIGN
+    assert call(L=1 << 20, D=256) == ERR_WORKSPACE
+    assert call(L=1 << 20, D=256, ws_ptr=FAKE, ws_bytes=w - 1) == ERR_WORKSPACE
+    assert call(batch=0, u=None, A=None, out=None) == OK
