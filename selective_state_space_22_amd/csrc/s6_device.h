@@ -130,6 +130,113 @@ __device__ __forceinline__ void token_step_state(const ChanConst<N>& cc, const T
   }
 }
 
+// ---------------------------------------------------------------- complex A
+//
+// The complex row A_n = -1/2 + n i of the page's A-initialisation ablation
+// (section 6.5), with dt, x, B and C real: eq. (2) over the complex numbers,
+//     Abar = e^{dt Re A} (cos(dt Im A) + i sin(dt Im A)),  beta = (Abar - 1)/A_n,
+// and the output reads Re(C . h).
+//
+// A state with slow decay multiplies by nearly the same Abar for thousands of
+// tokens, so any bias in Abar grows linearly in the state.  The hardware
+// v_sin_f32 / v_cos_f32 (errors up to ~3e-7, ~5 ulp) measured four times the
+// error budget of an fp32 scan this way; sin and cos are therefore evaluated
+// here from their Taylor series (about 1 ulp).  Below |dt A_n| = 0.02 the input
+// weight is the series dt (1 + x/2 + x^2/6) (truncation <= |x|^3/24 < 4e-7);
+// above it the quotient, whose cancellation costs err(Abar)/|x| < 1e-5.
+constexpr float kCplxSeriesX2 = 0.02f * 0.02f;
+constexpr float kQuarterPi = 0.78539816339744831f;
+constexpr float k2OverPi = 0.63661977236758134f;
+constexpr float kHalfPiHi = 1.57079637050628662f;    // float(pi/2)
+constexpr float kHalfPiLo = -4.37113900018624e-8f;   // pi/2 - kHalfPiHi
+
+// sin r and cos r for |r| <= pi/4: Taylor series through r^9 and r^10
+// (truncation below 2e-9 and 6e-11).
+__device__ __forceinline__ void sincos_small(float r, float& s, float& c) {
+  const float r2 = r * r;
+  float ps = __builtin_fmaf(r2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+  ps = __builtin_fmaf(r2, ps, 1.0f / 120.0f);
+  ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
+  s = __builtin_fmaf(r * r2, ps, r);
+  float pc = __builtin_fmaf(r2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+  pc = __builtin_fmaf(r2, pc, -1.0f / 720.0f);
+  pc = __builtin_fmaf(r2, pc, 1.0f / 24.0f);
+  pc = __builtin_fmaf(r2, pc, -0.5f);
+  c = __builtin_fmaf(r2, pc, 1.0f);
+}
+
+// sin a and cos a: a = k pi/2 + r with |r| <= pi/4 (pi/2 in two parts, each
+// product exact inside the FMA), then the quadrant k mod 4 swaps and negates.
+// Accurate while k pi/2 stays far inside fp32's range of exact products
+// (|a| up to about 1e5 radians).
+__device__ __forceinline__ void sincos_any(float a, float& s, float& c) {
+  const float k = __builtin_rintf(a * k2OverPi);
+  float r = __builtin_fmaf(-k, kHalfPiHi, a);
+  r = __builtin_fmaf(-k, kHalfPiLo, r);
+  float sr, cr;
+  sincos_small(r, sr, cr);
+  const int q = (int)k;
+  const float ss = (q & 1) ? cr : sr;
+  const float cc = (q & 1) ? sr : cr;
+  s = (q & 2) ? -ss : ss;
+  c = ((q + 1) & 2) ? -cc : cc;
+}
+
+// Per-state constants of a complex A_n.
+struct CplxA {
+  float re, im;  // A_n
+  float kr, ki;  // 1 / A_n = conj(A_n) / |A_n|^2 (inf/NaN for A_n = 0: never selected)
+  float m2;      // |A_n|^2
+  __device__ __forceinline__ void load(float r, float i) {
+    re = r;
+    im = i;
+    m2 = __builtin_fmaf(r, r, i * i);
+    const float inv = rcp(m2);
+    kr = r * inv;
+    ki = -i * inv;
+  }
+};
+
+// One token of eq. (3a) for one complex state: h = Abar h + beta * bx, bx = B_t,n x_t.
+// SMALL: the caller has checked |dt Im A_n| <= pi/4 (no angle reduction needed).
+template <bool SMALL>
+__device__ __forceinline__ void cplx_update(const CplxA& a, float dt, float dt2, float bx, float& hr, float& hi) {
+  const float xr = dt * a.re, xi = dt * a.im;
+  const float mag = ex2(xr * kLog2e);
+  float sn, cs;
+  if (SMALL) sincos_small(xi, sn, cs);
+  else sincos_any(xi, sn, cs);
+  const float abr = mag * cs, abi = mag * sn;
+  // (Abar - 1) / A
+  const float er = abr - 1.0f;
+  const float gr = __builtin_fmaf(er, a.kr, -abi * a.ki);
+  const float gi = __builtin_fmaf(er, a.ki, abi * a.kr);
+  // dt (1 + x (1/2 + x/6))
+  const float qr = __builtin_fmaf(xr, 1.0f / 6.0f, 0.5f), qi = xi * (1.0f / 6.0f);
+  const float tr = __builtin_fmaf(xr, qr, __builtin_fmaf(-xi, qi, 1.0f));
+  const float ti = __builtin_fmaf(xr, qi, xi * qr);
+  const bool small = dt2 * a.m2 < kCplxSeriesX2;
+  const float br = small ? dt * tr : gr;
+  const float bi = small ? dt * ti : gi;
+  const float nr = __builtin_fmaf(abr, hr, __builtin_fmaf(-abi, hi, br * bx));
+  const float ni = __builtin_fmaf(abr, hi, __builtin_fmaf(abi, hr, bi * bx));
+  hr = nr;
+  hi = ni;
+}
+
+// True when every active lane's angles dt |Im A_n| are at most pi/4 (maxim:
+// the lane's largest |Im A_n|), so that all of them can skip the reduction.
+__device__ __forceinline__ bool wave_small_angles(float dt, float maxim) { return __all(dt * maxim <= kQuarterPi); }
+
+// e^{A_n s} for a sum s of dt (chunk carries).
+__device__ __forceinline__ void cplx_decay(const CplxA& a, float s, float& pr, float& pi) {
+  const float mag = ex2(s * a.re * kLog2e);
+  float sn, cs;
+  sincos_any(s * a.im, sn, cs);
+  pr = mag * cs;
+  pi = mag * sn;
+}
+
 // Epilogue of one (token, channel): skip term, then the SiLU gate.
 __device__ __forceinline__ float epilogue(float y, float x, float dskip, bool has_z, float zv) {
   y = __builtin_fmaf(dskip, x, y);

@@ -96,7 +96,9 @@ struct ScanPlan {
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N);
 
 // Workgroup engine (scan_wg.hip).
-hipError_t launch_scan_wg(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
+// cplx: complex A (A, h0, last and the carries hold (re, im) pairs), no fused dt projection.
+hipError_t launch_scan_wg(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream,
+                          bool cplx = false);
 bool wg_supported(int64_t N);
 int wg_waves(int64_t N);
 int wg_tile(int64_t N);
@@ -104,10 +106,13 @@ int wg_tile(int64_t N);
 bool dstate_supported(int64_t N);
 
 // Complex diagonal A (scan_complex.hip): A, h0 and last are (.., N, 2) re/im
-// float; agg_h is (batch, nchunks, D, N, 2).  The plan is the lane engine's.
+// float; agg_h is (batch, nchunks, D, N, 2).  The plans are those of the real
+// scan with two floats per state.
 ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N);
 hipError_t launch_scan_complex(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace,
                                hipStream_t stream);
+// Carry pass over complex (batch, chunk, D, N, 2) chunk aggregates.
+hipError_t launch_cplx_carry(const ScanArgs& a, int N, hipStream_t stream);
 
 // ---------------------------------------------------------------- backward (scan_bwd.hip)
 

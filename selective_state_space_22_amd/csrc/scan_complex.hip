@@ -13,8 +13,8 @@
 // complex states in VGPRs, B_t and C_t wave-uniform -- with the same split of
 // long sequences into chunks: chunk end states from zero and the chunk sum of
 // dt, a carry pass composing them with h_in(g+1) = e^{A sum dt} h_in(g) + b_g,
-// then every chunk from its carry-in.  v_sin_f32 / v_cos_f32 take their
-// argument in revolutions; it is reduced to [0, 1) with v_fract_f32 first.
+// then every chunk from its carry-in.  The per-state arithmetic (cplx_update,
+// cplx_decay) is shared with the workgroup engine.
 #include <cstdlib>
 
 #include "s6_device.h"
@@ -23,69 +23,38 @@
 namespace s6 {
 namespace {
 
-constexpr float kInv2Pi = 0.15915494309189535f;
-
-__device__ __forceinline__ float sin_rev(float r) { return __builtin_amdgcn_sinf(__builtin_amdgcn_fractf(r)); }
-__device__ __forceinline__ float cos_rev(float r) { return __builtin_amdgcn_cosf(__builtin_amdgcn_fractf(r)); }
-
-// Per (channel, state) constants.
-template <int N>
-struct CplxConst {
-  float re[N], im[N];  // A_n
-  float inv[N];        // 1 / |A_n|^2
-  float ar2[N];        // Re A_n * log2 e
-  float ai_rev[N];     // Im A_n / 2 pi
-  __device__ __forceinline__ void load(const float* A_row) {  // (N, 2) re, im
+// One token for all N complex states; returns Re(C . h) when READ.  maxim: the
+// lane's largest |Im A_n| (small angles take the shorter sin/cos).
+template <int N, bool READ>
+__device__ __forceinline__ float ctoken(const CplxA (&c)[N], float maxim, const TokenFront& f, float x,
+                                        const float* Bt, const float* Ct, float (&hr)[N], float (&hi)[N]) {
+  float y = 0.0f;
+  if (wave_small_angles(f.dt, maxim)) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      re[n] = A_row[2 * n];
-      im[n] = A_row[2 * n + 1];
-      inv[n] = rcp(__builtin_fmaf(re[n], re[n], im[n] * im[n]));
-      ar2[n] = re[n] * kLog2e;
-      ai_rev[n] = im[n] * kInv2Pi;
+      cplx_update<true>(c[n], f.dt, f.dt2, Bt[n] * x, hr[n], hi[n]);
+      if (READ) y = __builtin_fmaf(Ct[n], hr[n], y);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      cplx_update<false>(c[n], f.dt, f.dt2, Bt[n] * x, hr[n], hi[n]);
+      if (READ) y = __builtin_fmaf(Ct[n], hr[n], y);
     }
   }
-};
+  return y;
+}
 
-// Below |dt A_n| = 0.1 the input weight comes from the Taylor series of
-// (e^x - 1)/x to x^4 (truncation <= |x|^5/720 < 2e-8); above it from
-// (Abar - 1)/A_n, whose cancellation costs at most err(Abar)/0.1.
-constexpr float kCplxSeriesX2 = 0.01f;
-
-// One token for all N complex states; returns Re(C . h) when READ.
-template <int N, bool READ>
-__device__ __forceinline__ float ctoken(const CplxConst<N>& c, float dt, float x, const float* Bt, const float* Ct,
-                                        float (&hr)[N], float (&hi)[N]) {
-  float y = 0.0f;
+// The channel's A (N (re, im) pairs); returns the largest |Im A_n|.
+template <int N>
+__device__ __forceinline__ float load_a(const float* A_row, CplxA (&c)[N]) {
+  float m = 0.0f;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const float mag = ex2(dt * c.ar2[n]);
-    const float ang = dt * c.ai_rev[n];
-    const float abr = mag * cos_rev(ang), abi = mag * sin_rev(ang);
-    // (Abar - 1) conj(A) / |A|^2
-    const float er = abr - 1.0f;
-    const float gr = __builtin_fmaf(er, c.re[n], abi * c.im[n]) * c.inv[n];
-    const float gi = __builtin_fmaf(abi, c.re[n], -er * c.im[n]) * c.inv[n];
-    // dt (1 + x/2 + x^2/6 + x^3/24 + x^4/120), x = dt A_n
-    const float xr = dt * c.re[n], xi = dt * c.im[n];
-    float qr = __builtin_fmaf(xr, 1.0f / 120.0f, 1.0f / 24.0f), qi = xi * (1.0f / 120.0f);
-    float tr = __builtin_fmaf(xr, qr, __builtin_fmaf(-xi, qi, 1.0f / 6.0f));
-    float ti = __builtin_fmaf(xr, qi, xi * qr);
-    qr = __builtin_fmaf(xr, tr, __builtin_fmaf(-xi, ti, 0.5f));
-    qi = __builtin_fmaf(xr, ti, xi * tr);
-    tr = __builtin_fmaf(xr, qr, __builtin_fmaf(-xi, qi, 1.0f));
-    ti = __builtin_fmaf(xr, qi, xi * qr);
-    const bool small = __builtin_fmaf(xr, xr, xi * xi) < kCplxSeriesX2;
-    const float br = small ? dt * tr : gr;
-    const float bi = small ? dt * ti : gi;
-    const float bx = Bt[n] * x;
-    const float nr = __builtin_fmaf(abr, hr[n], __builtin_fmaf(-abi, hi[n], br * bx));
-    const float ni = __builtin_fmaf(abr, hi[n], __builtin_fmaf(abi, hr[n], bi * bx));
-    hr[n] = nr;
-    hi[n] = ni;
-    if (READ) y = __builtin_fmaf(Ct[n], nr, y);
+    c[n].load(A_row[2 * n], A_row[2 * n + 1]);
+    m = fmaxf(m, fabsf(c[n].im));
   }
-  return y;
+  return m;
 }
 
 template <typename IO, int N>
@@ -110,8 +79,8 @@ __global__ __launch_bounds__(256) void cplx_chunk_state_kernel(CplxArgs c) {
   const IO* dl = static_cast<const IO*>(a.delta);
   const IO* Bp = static_cast<const IO*>(a.B);
   const float bias = a.bias ? a.bias[d] : 0.0f;
-  CplxConst<N> cc;
-  cc.load(a.A + d * N * 2);
+  CplxA cc[N];
+  const float maxim = load_a<N>(a.A + d * N * 2, cc);
   float hr[N], hi[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) hr[n] = hi[n] = 0.0f;
@@ -124,7 +93,7 @@ __global__ __launch_bounds__(256) void cplx_chunk_state_kernel(CplxArgs c) {
     float Bt[N];
     load_bc<IO, N>(Bp + ((size_t)b * L + t) * N, Bt);
     const TokenFront f = make_front(load_io(dl, i), bias, sp);
-    ctoken<N, false>(cc, f.dt, load_io(u, i), Bt, Bt, hr, hi);
+    ctoken<N, false>(cc, maxim, f, load_io(u, i), Bt, Bt, hr, hi);
     const float yk = f.dt - sc;
     const float tk = s + yk;
     sc = (tk - s) - yk;
@@ -147,15 +116,14 @@ __global__ __launch_bounds__(256) void cplx_carry_kernel(CplxArgs c) {
   const int64_t D = a.D;
   if (lane >= a.batch * D * N) return;
   const int64_t n = lane % N, d = (lane / N) % D, b = lane / (N * D);
-  const float ar2 = a.A[(d * N + n) * 2] * kLog2e;
-  const float ai_rev = a.A[(d * N + n) * 2 + 1] * kInv2Pi;
+  CplxA an;
+  an.load(a.A[(d * N + n) * 2], a.A[(d * N + n) * 2 + 1]);
   float cr = a.h0 ? a.h0[lane * 2] : 0.0f, ci = a.h0 ? a.h0[lane * 2 + 1] : 0.0f;
   const int G = a.nchunks;
   for (int g = 0; g < G - 1; ++g) {
     const size_t base = ((size_t)b * G + g) * D + d;
-    const float sdt = a.agg_s[base];
-    const float mag = ex2(ar2 * sdt);
-    const float pr = mag * cos_rev(ai_rev * sdt), pi = mag * sin_rev(ai_rev * sdt);
+    float pr, pi;
+    cplx_decay(an, a.agg_s[base], pr, pi);
     const size_t k = (base * N + n) * 2;
     const float br = a.agg_h[k], bi = a.agg_h[k + 1];
     a.agg_h[k] = cr;
@@ -186,8 +154,8 @@ __global__ __launch_bounds__(256) void cplx_output_kernel(CplxArgs c) {
   IO* out = static_cast<IO*>(a.out);
   const float bias = a.bias ? a.bias[d] : 0.0f;
   const float dskip = a.dskip ? a.dskip[d] : 0.0f;
-  CplxConst<N> cc;
-  cc.load(a.A + d * N * 2);
+  CplxA cc[N];
+  const float maxim = load_a<N>(a.A + d * N * 2, cc);
   float hr[N], hi[N];
   const float* src = a.nchunks > 1 ? a.agg_h + (((size_t)b * a.nchunks + g) * D + d) * N * 2
                                    : (a.h0 ? a.h0 + ((size_t)b * D + d) * N * 2 : nullptr);
@@ -207,7 +175,7 @@ __global__ __launch_bounds__(256) void cplx_output_kernel(CplxArgs c) {
     load_bc<IO, N>(Cp + ((size_t)b * L + t) * N, Ct);
     const float x = load_io(u, i);
     const TokenFront f = make_front(load_io(dl, i), bias, sp);
-    const float y = ctoken<N, true>(cc, f.dt, x, Bt, Ct, hr, hi);
+    const float y = ctoken<N, true>(cc, maxim, f, x, Bt, Ct, hr, hi);
     const float zv = has_z ? load_io(zp, i) : 0.0f;
     store_io(out, i, epilogue(y, x, dskip, has_z, zv));
   }
@@ -254,6 +222,21 @@ hipError_t launch_cplx_io(const CplxArgs& c, int N, int bs, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_cplx_carry(const ScanArgs& a, int N, hipStream_t st) {
+  const CplxArgs c{a};
+  const int64_t lanes = a.batch * a.D * N;
+  const dim3 grid((unsigned)((lanes + 255) / 256));
+  switch (N) {
+    case 1: hipLaunchKernelGGL((cplx_carry_kernel<1>), grid, dim3(256), 0, st, c); break;
+    case 2: hipLaunchKernelGGL((cplx_carry_kernel<2>), grid, dim3(256), 0, st, c); break;
+    case 4: hipLaunchKernelGGL((cplx_carry_kernel<4>), grid, dim3(256), 0, st, c); break;
+    case 8: hipLaunchKernelGGL((cplx_carry_kernel<8>), grid, dim3(256), 0, st, c); break;
+    case 16: hipLaunchKernelGGL((cplx_carry_kernel<16>), grid, dim3(256), 0, st, c); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_scan_complex(const ScanArgs& in, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
   if (in.batch == 0 || in.D == 0) return hipSuccess;
   if (in.L == 0) {
@@ -262,6 +245,12 @@ hipError_t launch_scan_complex(const ScanArgs& in, const ScanPlan& p, int io, in
     hipLaunchKernelGGL(cplx_empty_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, in.last, in.h0,
                        count);
     return hipGetLastError();
+  }
+  if (p.engine == kEngineWg) {
+    ScanArgs a = in;
+    a.chunk_len = p.chunk_len;
+    a.nchunks = p.nchunks;
+    return launch_scan_wg(a, p, io, N, ws, st, true);
   }
   CplxArgs c{in};
   c.s.chunk_len = p.chunk_len;

@@ -188,7 +188,8 @@ constexpr int64_t kCus = 256;                          // compute units of an MI
 constexpr int64_t kGridMax = kCus * S6_WG_PER_CU;      // persistent workgroups
 constexpr int64_t kChainedMinChains = 128;  // below this many channel blocks, long sequences use two passes
 
-ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N) {
+// cf: floats per state (1 real, 2 complex), for the workspace size.
+ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
   ScanPlan p{};
   p.engine = kEngineLane;
   p.block = D >= 256 ? 256 : (int32_t)(((D + 63) / 64) * 64);
@@ -206,11 +207,11 @@ ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N) {
   p.nchunks = (int32_t)(p.chunk_len > 0 ? (L + p.chunk_len - 1) / p.chunk_len : 1);
   if (p.nchunks < 1) p.nchunks = 1;
   p.ws_ctrl = 0;
-  p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) : 0;
+  p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (N * cf + 1) * sizeof(float) : 0;
   return p;
 }
 
-ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
+ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
   ScanPlan p{};
   p.engine = kEngineWg;
   p.waves = wg_waves(N);
@@ -235,7 +236,7 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
     p.nchunks = (int32_t)((L + chunk - 1) / chunk);
     p.grid = (int32_t)(chains < kGridMax ? chains : kGridMax);
     p.ws_ctrl = round_up(256 + 4 * (size_t)chains, 256);
-    p.ws_bytes = p.ws_ctrl + (size_t)chains * 64 * N * sizeof(float);
+    p.ws_bytes = p.ws_ctrl + (size_t)chains * 64 * N * cf * sizeof(float);
   } else {
     // Two passes over independent chunks: about 1024 work items.
     p.split = 1;
@@ -249,7 +250,7 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N) {
     p.nchunks = (int32_t)((L + chunk - 1) / chunk);
     p.grid = (int32_t)kGridMax;
     p.ws_ctrl = 256;
-    p.ws_bytes = p.ws_ctrl + (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float);
+    p.ws_bytes = p.ws_ctrl + (size_t)batch * p.nchunks * D * (N * cf + 1) * sizeof(float);
   }
   return p;
 }
@@ -263,10 +264,10 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
 }
 
 ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N) {
-  // The lane engine's chunking; each chunk aggregate holds N complex states.
-  ScanPlan p = plan_lane(batch, L, D, N);
-  p.ws_bytes = p.nchunks > 1 ? (size_t)batch * p.nchunks * D * (2 * N + 1) * sizeof(float) : 0;
-  return p;
+  // The real scan's plans; carries and chunk aggregates hold N complex states.
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0)
+    return plan_wg(batch, L, D, N, 2);
+  return plan_lane(batch, L, D, N, 2);
 }
 
 template <typename IO, int N>

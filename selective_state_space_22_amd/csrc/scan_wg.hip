@@ -111,9 +111,11 @@ __device__ __forceinline__ f32x4 dt_mfma<float>(u32x4 a, u32x4 b, f32x4 c) {
   return c;
 }
 
-template <typename IO, int N, int W, int T, int MODE, bool FDT>
+template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
 struct WgScan {
   static constexpr int S = N / W;                 // states per wave
+  static constexpr int CF = CPLX ? 2 : 1;         // floats per state (complex A: re, im)
+  static constexpr int CS = CPLX ? S : 1;         // sizes of the complex-only register arrays
   static constexpr int TW = T / W;                // front-end / epilogue tokens per wave per tile
   static constexpr int NT = 64 * W;               // threads
   // B/C of a tile: 2TN elements.  With at least one per thread, the first half
@@ -164,6 +166,9 @@ struct WgScan {
   u32x4 wdt[kDtSlices], dta[kDtSlices];
   int nks;
   float a2[S], ka[S], ah[S], h[S];
+  CplxA ca[CS];  // complex A: per-state constants; h holds Re h, hq Im h
+  float hq[CS];
+  float maxim;   // complex A: largest |Im A_n| of this wave's states
   float bias, dskip;
   float dsum, dcomp;  // compensated sum of dt (split mode, first pass)
 
@@ -296,6 +301,23 @@ struct WgScan {
   // its partial readout sum_s C_t[s] h_t[s] (eq. (3b)).
   __device__ __forceinline__ void step(const Tok& t, int y2, int j) {
     float y = 0.0f;
+    if constexpr (CPLX) {
+      if (wave_small_angles(t.fv.x, maxim)) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          cplx_update<true>(ca[s], t.fv.x, t.fv.y, t.bc[s] * t.fv.z, h[s], hq[s]);
+          if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          cplx_update<false>(ca[s], t.fv.x, t.fv.y, t.bc[s] * t.fv.z, h[s], hq[s]);
+          if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
+        }
+      }
+      if (kOut) sm.yp[y2][j][w][lane] = y;
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const float x2 = t.fv.x * a2[s];
@@ -351,6 +373,23 @@ struct WgScan {
     }
   }
 
+  // This wave's S states from / to p, the address of the first of them in a
+  // state array (N floats, or N (re, im) pairs, per channel).
+  __device__ __forceinline__ void get_state(const float* p) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      h[s] = p[s * CF];
+      if constexpr (CPLX) hq[s] = p[s * CF + 1];
+    }
+  }
+  __device__ __forceinline__ void put_state(float* p) const {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      p[s * CF] = h[s];
+      if constexpr (CPLX) p[s * CF + 1] = hq[s];
+    }
+  }
+
   __device__ void run_item(int chain, int g) {
     const int G = A.s.nchunks;
     b = chain / A.blocks_per_row;
@@ -388,12 +427,22 @@ struct WgScan {
       }
     }
     const int nstate0 = w * S;
+    if constexpr (CPLX) {
+      maxim = 0.0f;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const float a = dvalid ? A.s.A[d * N + nstate0 + s] : -1.0f;
-      a2[s] = a * kLog2e;
-      ka[s] = rcp(a);
-      ah[s] = 0.5f * a;
+      for (int s = 0; s < S; ++s) {
+        const size_t k = ((size_t)d * N + nstate0 + s) * 2;
+        ca[s].load(dvalid ? A.s.A[k] : -1.0f, dvalid ? A.s.A[k + 1] : 0.0f);
+        maxim = fmaxf(maxim, fabsf(ca[s].im));
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float a = dvalid ? A.s.A[d * N + nstate0 + s] : -1.0f;
+        a2[s] = a * kLog2e;
+        ka[s] = rcp(a);
+        ah[s] = 0.5f * a;
+      }
     }
     bias = (dvalid && A.s.bias) ? A.s.bias[d] : 0.0f;
     dskip = (dvalid && A.s.dskip) ? A.s.dskip[d] : 0.0f;
@@ -403,12 +452,11 @@ struct WgScan {
     // state entering the chunk
 #pragma unroll
     for (int s = 0; s < S; ++s) h[s] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < CS; ++s) hq[s] = 0.0f;
     if (MODE == kModeChained) {
       if (g == 0) {
-        if (A.s.h0 && dvalid) {
-#pragma unroll
-          for (int s = 0; s < S; ++s) h[s] = A.s.h0[((size_t)b * A.s.D + d) * N + nstate0 + s];
-        }
+        if (A.s.h0 && dvalid) get_state(A.s.h0 + (((size_t)b * A.s.D + d) * N + nstate0) * CF);
       } else {
         if (threadIdx.x == 0) {
           uint32_t spins = 0;
@@ -423,16 +471,10 @@ struct WgScan {
         // Thread 0's acquire load (which invalidates this CU's caches) is
         // ordered before the other waves' reads of the carry by the barrier.
         __syncthreads();
-        const float* src = A.carry + ((size_t)chain * 64 + lane) * N + nstate0;
-#pragma unroll
-        for (int s = 0; s < S; ++s) h[s] = src[s];
+        get_state(A.carry + (((size_t)chain * 64 + lane) * N + nstate0) * CF);
       }
     } else if (MODE == kModeOut) {
-      if (dvalid) {
-        const float* src = A.s.agg_h + (((size_t)b * G + g) * A.s.D + d) * N + nstate0;
-#pragma unroll
-        for (int s = 0; s < S; ++s) h[s] = src[s];
-      }
+      if (dvalid) get_state(A.s.agg_h + ((((size_t)b * G + g) * A.s.D + d) * N + nstate0) * CF);
     }
     wait_vmem();
 
@@ -497,9 +539,7 @@ struct WgScan {
     // publish the chunk's end
     if (MODE == kModeChained) {
       if (g < G - 1) {
-        float* dst = A.carry + ((size_t)chain * 64 + lane) * N + nstate0;
-#pragma unroll
-        for (int s = 0; s < S; ++s) dst[s] = h[s];
+        put_state(A.carry + (((size_t)chain * 64 + lane) * N + nstate0) * CF);
         // Every wave's carry stores complete (reach L2) before the barrier;
         // thread 0's release store then writes the L2 back once for all of
         // them before the flag becomes visible.
@@ -508,15 +548,11 @@ struct WgScan {
         if (threadIdx.x == 0)
           __hip_atomic_store(A.flags + chain, (uint32_t)(g + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       } else if (A.s.last && dvalid) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) A.s.last[((size_t)b * A.s.D + d) * N + nstate0 + s] = h[s];
+        put_state(A.s.last + (((size_t)b * A.s.D + d) * N + nstate0) * CF);
       }
     } else if (MODE == kModeAgg) {
       const size_t base = ((size_t)b * G + g) * A.s.D + d;
-      if (dvalid) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) A.s.agg_h[base * N + nstate0 + s] = h[s];
-      }
+      if (dvalid) put_state(A.s.agg_h + (base * N + nstate0) * CF);
       sm.sdt[w][lane] = dsum;
       __syncthreads();
       if (w == 0 && dvalid) {
@@ -526,17 +562,14 @@ struct WgScan {
         A.s.agg_s[base] = tot;
       }
     } else {  // kModeOut
-      if (g == G - 1 && A.s.last && dvalid) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) A.s.last[((size_t)b * A.s.D + d) * N + nstate0 + s] = h[s];
-      }
+      if (g == G - 1 && A.s.last && dvalid) put_state(A.s.last + (((size_t)b * A.s.D + d) * N + nstate0) * CF);
     }
   }
 };
 
-template <typename IO, int N, int W, int T, int MODE, bool FDT>
+template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
 __global__ __launch_bounds__(64 * W, S6_WG_PER_CU) void scan_wg_kernel(WgArgs a) {
-  using K = WgScan<IO, N, W, T, MODE, FDT>;
+  using K = WgScan<IO, N, W, T, MODE, FDT, CPLX>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
   for (int round = 0;; ++round) {
@@ -553,8 +586,9 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-template <typename IO, int N, int W, int T, bool FDT>
+template <typename IO, int N, int W, int T, bool FDT, bool CPLX>
 hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
+  constexpr int CF = CPLX ? 2 : 1;
   uint8_t* base = static_cast<uint8_t*>(ws);
   WgArgs a;
   a.s = s;
@@ -571,29 +605,30 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.ticket = ctrl;
     a.carry = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.nitems = a.chains * p.nchunks;
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained, FDT>), dim3(p.grid), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained, FDT, CPLX>), dim3(p.grid), block, 0, st, a);
   } else {
     a.s.agg_h = reinterpret_cast<float*>(base + p.ws_ctrl);
-    a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N;
+    a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N * CF;
     a.carry = nullptr;
     a.ticket = ctrl;
     a.nitems = a.chains * (p.nchunks - 1);
     const unsigned g1 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg, FDT>), dim3(g1), block, 0, st, a);
-    const hipError_t ce = launch_chunk_carry(a.s, N, st);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg, FDT, CPLX>), dim3(g1), block, 0, st, a);
+    const hipError_t ce = CPLX ? launch_cplx_carry(a.s, N, st) : launch_chunk_carry(a.s, N, st);
     if (ce != hipSuccess) return ce;
     a.ticket = ctrl + 1;
     a.nitems = a.chains * p.nchunks;
     const unsigned g2 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut, FDT>), dim3(g2), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut, FDT, CPLX>), dim3(g2), block, 0, st, a);
   }
   return hipGetLastError();
 }
 
 template <typename IO, int N, int W, int T>
-hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
-  if (s.dtlow) return launch_wg_t<IO, N, W, T, true>(s, p, ws, st);
-  return launch_wg_t<IO, N, W, T, false>(s, p, ws, st);
+hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, bool cplx, void* ws, hipStream_t st) {
+  if (cplx) return s.dtlow ? hipErrorInvalidValue : launch_wg_t<IO, N, W, T, false, true>(s, p, ws, st);
+  if (s.dtlow) return launch_wg_t<IO, N, W, T, true, false>(s, p, ws, st);
+  return launch_wg_t<IO, N, W, T, false, false>(s, p, ws, st);
 }
 
 }  // namespace
@@ -611,17 +646,17 @@ bool fused_dt_supported(int64_t N, int64_t R, int io) {
   return wg_supported(N) && S6_WG_TILE == 16 && R >= 1 && (R * e) % 16 == 0 && R * e <= 64 * kDtSlices;
 }
 
-hipError_t launch_scan_wg(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
+hipError_t launch_scan_wg(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st, bool cplx) {
   const bool bf = io == kIoBF16;
   if (N == 16 && p.waves == 8)
-    return bf ? launch_wg_fdt<uint16_t, 16, 8, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_fdt<float, 16, 8, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 16, 8, S6_WG_TILE>(s, p, cplx, ws, st)
+              : launch_wg_fdt<float, 16, 8, S6_WG_TILE>(s, p, cplx, ws, st);
   if (N == 16 && p.waves == 4)
-    return bf ? launch_wg_fdt<uint16_t, 16, 4, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_fdt<float, 16, 4, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 16, 4, S6_WG_TILE>(s, p, cplx, ws, st)
+              : launch_wg_fdt<float, 16, 4, S6_WG_TILE>(s, p, cplx, ws, st);
   if (N == 8)
-    return bf ? launch_wg_fdt<uint16_t, 8, 4, S6_WG_TILE>(s, p, ws, st)
-              : launch_wg_fdt<float, 8, 4, S6_WG_TILE>(s, p, ws, st);
+    return bf ? launch_wg_fdt<uint16_t, 8, 4, S6_WG_TILE>(s, p, cplx, ws, st)
+              : launch_wg_fdt<float, 8, 4, S6_WG_TILE>(s, p, cplx, ws, st);
   return hipErrorInvalidValue;
 }
 

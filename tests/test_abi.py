@@ -214,10 +214,16 @@ def test_selection_and_ssm_validation(lib):
 
 def test_complex_scan_validation_and_workspace(lib):
     ws = binding.mamba_scan_fwd_complex_workspace_size
-    # short rows: one chunk, no workspace; long rows over few channels: (batch, chunks, D, 2N+1) floats
-    assert ws(1, 256, 64, 16, 0) == 0
+    # the real scan's plans with two floats per state: N = 8, 16 hand (re, im) carries between
+    # chunks of a channel block (64 channels x N x 2 floats per block, after the work counters) ...
+    chains = 4 * 5120 // 64
+    w = ws(4, 4096, 5120, 16, 1)
+    assert chains * 64 * 16 * 8 <= w <= chains * 64 * 16 * 8 + 4096 + 4 * chains
+    # ... or keep (batch, chunks, D, 2N+1) chunk aggregates after a 256-byte header
     w = ws(1, 1 << 20, 256, 16, 0)
-    assert w > 0 and w % (256 * 33 * 4) == 0
+    assert w > 256 and (w - 256) % (256 * 33 * 4) == 0
+    # other N: the lane engine, no workspace for short rows
+    assert ws(1, 256, 64, 4, 0) == 0
     assert ws(1, 16, 64, 3, 0) == 0 and ws(1, 16, 64, 16, 9) == 0
 
     def call(batch=1, L=8, D=64, N=16, io=0, u=FAKE, A=FAKE, out=FAKE, h0=None, ws_ptr=None, ws_bytes=0):

@@ -73,14 +73,49 @@ def check(inp, Ac, h0=None, softplus=None, label=""):
     return eo, el
 
 
+def _engine(monkeypatch, engine):
+    """N = 8 and 16 run on the workgroup engine by default; MAMBA_MI355X_LANE_ENGINE=1
+    forces the lane-per-channel kernels so that both are covered."""
+    if engine == "lane":
+        monkeypatch.setenv("MAMBA_MI355X_LANE_ENGINE", "1")
+    else:
+        monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
+
+
+@pytest.mark.parametrize("engine", ["default", "lane"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
-def test_small_full(io, N):
+def test_small_full(io, N, engine, monkeypatch):
     _need_gpu()
-    _announce(f"complex A: (2, 300, 130, {N}) {io}, with h0")
+    _engine(monkeypatch, engine)
+    _announce(f"complex A: (2, 300, 130, {N}) {io}, with h0, engine={engine}")
     inp, Ac = _cinputs(2, 300, 130, N, io, seed=W.SEED_BASE + 41 + N)
-    eo, el = check(inp, Ac, h0=_h0(2, 130, N, 5), label=f"N={N} {io}")
-    print(f"N={N} {io}: out err {eo:.3e} last err {el:.3e}")
+    eo, el = check(inp, Ac, h0=_h0(2, 130, N, 5), label=f"N={N} {io} {engine}")
+    print(f"N={N} {io} {engine}: out err {eo:.3e} last err {el:.3e}")
+
+
+# Shapes that reach every mode of the workgroup engine with complex states:
+# chained with one chunk per channel block, chained with chunks handed between
+# workgroups (> 256 blocks), and the two-pass split (few blocks, long rows).
+WG_CASES = [
+    (3, 700, 4096, 16, "bf16"),    # 192 blocks, chained, one chunk
+    (5, 1100, 4096, 16, "bf16"),   # 320 blocks, chained, 3 chunks (last one ragged)
+    (1, 4096, 64, 16, "f32"),      # 1 block, split into 64 chunks
+    (2, 3000, 200, 16, "bf16"),    # 8 blocks with a ragged channel tail, split
+    (3, 900, 4096, 8, "f32"),      # N = 8, chained
+    (1, 5000, 128, 8, "bf16"),     # N = 8, split
+]
+
+
+@pytest.mark.parametrize("case", WG_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in WG_CASES])
+def test_workgroup_engine_modes(case, monkeypatch):
+    _need_gpu()
+    _engine(monkeypatch, "default")
+    batch, L, D, N, io = case
+    _announce(f"complex A, workgroup engine case {case}, with h0")
+    inp, Ac = _cinputs(batch, L, D, N, io, seed=W.SEED_BASE + 66 + L + N)
+    eo, el = check(inp, Ac, h0=_h0(batch, D, N, 9), label=str(case))
+    print(f"{case}: out err {eo:.3e} last err {el:.3e}")
 
 
 def test_scan_only_no_softplus():
@@ -91,10 +126,12 @@ def test_scan_only_no_softplus():
     check(inp, Ac, softplus=False, label="scan only")
 
 
-def test_long_sequence_is_chunked():
+@pytest.mark.parametrize("engine", ["default", "lane"])
+def test_long_sequence_is_chunked(engine, monkeypatch):
     """One row of 8192 tokens over 128 channels: the plan cuts it into chunks whose
     end states are composed through complex carries."""
     _need_gpu()
+    _engine(monkeypatch, engine)
     _announce("complex A: (1, 8192, 128, 16) f32, chunked, with h0")
     inp, Ac = _cinputs(1, 8192, 128, 16, "f32", seed=W.SEED_BASE + 62)
     eo, el = check(inp, Ac, h0=_h0(1, 128, 16, 6), label="long")
