@@ -21,6 +21,7 @@
 // rounds and splits xdbl.  Shapes whose rows are not 16-byte aligned take a
 // plain VALU kernel instead.
 #include <cstdlib>
+#include <type_traits>
 
 #include "s6_device.h"
 #include "s6_internal.h"
@@ -88,16 +89,23 @@ struct GemmArgs {
 // each).  K advances in stages of 128 bytes per row (64 bf16 / 32 fp32): the
 // A and B stage tiles (128 rows x 128 bytes each) are read with coalesced
 // 16-byte loads (8 adjacent lanes per row), stored to LDS (double buffered,
-// rows padded by 16 bytes against bank conflicts), and each wave reads its
-// MFMA operands from LDS (lane l: row l % 16, bytes 16 (l / 16) of a 64-byte
-// half-stage).  The next stage's global loads are in flight while the current
-// stage is multiplied.
+// chunks XOR-swizzled by row against bank conflicts, see stage_off), and each
+// wave reads its MFMA operands from LDS (lane l: row l % 16, bytes 16 (l / 16)
+// of a 64-byte half-stage).  Global loads run three stages ahead of the
+// multiplication, through a ring of registers: with two workgroups per CU that
+// keeps ~190 KB per CU in flight, enough to cover HBM latency at full bandwidth.
 constexpr int kGemmBM = 128;
 constexpr int kStageBytes = 128;                  // K bytes per row per stage
-constexpr int kRowPitch = kStageBytes + 16;       // LDS row pitch in bytes
+// LDS stage layout: 128-byte rows, the 16-byte chunk c of row r stored at chunk
+// c ^ ((r >> 1) & 7).  The 16 lanes of a quarter-wave then touch 64 distinct
+// banks both when they store two rows (8 chunks each) and when they read one
+// chunk of 16 consecutive rows as MFMA operands.
+__device__ __forceinline__ uint32_t stage_off(uint32_t row, uint32_t chunk) {
+  return row * kStageBytes + 16u * (chunk ^ ((row >> 1) & 7u));
+}
 
 template <typename IN, typename OUT>
-__global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, 2) void gemm_nt_mfma_kernel(GemmArgs g) {
   constexpr int TM = 4, TN = 4;
   constexpr uint32_t E = sizeof(IN);
   const int lane = threadIdx.x & 63;
@@ -124,36 +132,41 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
                                               (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb,
                                               (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kGemmBM * kRowPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kGemmBM * kRowPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kGemmBM * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kGemmBM * kStageBytes];
 
   // global -> register share of one stage: 4 loads per operand per thread
   const int t = threadIdx.x;
   const int lrow = t >> 3;             // 0..31, + 32 v
   const uint32_t lbyte = (t & 7) * 16u;
   const uint32_t kbytes = (uint32_t)(g.K * E);
-  u32x4 ga[4], gb[4];
+  u32x4 ga[3][4], gb[3][4];  // register ring: stage s lives in slot (s - first) % 3
   const int all = (int)((kbytes + kStageBytes - 1) / kStageBytes);
   const int first = g.parts > 1 ? part * g.sps : 0;
   const int nst = g.parts > 1 ? (all - first < g.sps ? all - first : g.sps) : all;
-  auto gload = [&](int stage) {
+  auto gload = [&](int stage, auto slot) {
+    constexpr int R = decltype(slot)::value;
     const uint32_t kb = (uint32_t)stage * kStageBytes + lbyte;
     const bool in = stage < first + nst && kb < kbytes;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const uint32_t row = lrow + 32 * v;
-      ga[v] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? (uint32_t)(row * g.lda * E) + kb : kOutOfRange, 0, 0);
-      gb[v] = __builtin_amdgcn_raw_buffer_load_b128(rb, in ? (uint32_t)(row * g.ldb * E) + kb : kOutOfRange, 0, 0);
+      ga[R][v] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? (uint32_t)(row * g.lda * E) + kb : kOutOfRange, 0, 0);
+      gb[R][v] = __builtin_amdgcn_raw_buffer_load_b128(rb, in ? (uint32_t)(row * g.ldb * E) + kb : kOutOfRange, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, auto slot) {
+    constexpr int R = decltype(slot)::value;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const uint32_t o = (lrow + 32 * v) * kRowPitch + lbyte;
-      *reinterpret_cast<u32x4*>(&lds_a[buf][o]) = ga[v];
-      *reinterpret_cast<u32x4*>(&lds_b[buf][o]) = gb[v];
+      const uint32_t o = stage_off(lrow + 32 * v, lbyte / 16);
+      *reinterpret_cast<u32x4*>(&lds_a[buf][o]) = ga[R][v];
+      *reinterpret_cast<u32x4*>(&lds_b[buf][o]) = gb[R][v];
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -162,30 +175,39 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int r16 = lane & 15, q = lane >> 4;
-  gload(first);
-  lstore(0);
-  gload(first + 1);
-  __syncthreads();
-  for (int k = 0; k < nst; ++k) {
+  // Stage k of this launch (global stage first + k): multiply it from LDS
+  // buffer k & 1, move stage k + 1 from its register slot to the other buffer,
+  // then reuse stage k's slot (stored to LDS one step earlier) for stage k + 3.
+  auto step = [&](int k, auto next_slot, auto own_slot) {
     const int buf = k & 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // two 64-byte halves of the stage
       u32x4 a[TM], b[TN];
-      const uint32_t col = h * 64u + 16u * q;
+      const uint32_t chunk = 4u * h + q;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][(wm * 64 + 16 * i + r16) * kRowPitch + col]);
+        a[i] = *reinterpret_cast<const u32x4*>(&lds_a[buf][stage_off(wm * 64 + 16 * i + r16, chunk)]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][(wn * 64 + 16 * j + r16) * kRowPitch + col]);
+        b[j] = *reinterpret_cast<const u32x4*>(&lds_b[buf][stage_off(wn * 64 + 16 * j + r16, chunk)]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<IN>::step(a[i], b[j], acc[i][j]);
     }
-    if (k + 1 < nst) lstore(buf ^ 1);
-    gload(first + k + 2);
+    if (k + 1 < nst) lstore(buf ^ 1, next_slot);
+    gload(first + k + 3, own_slot);
     __syncthreads();
+  };
+  gload(first, S0{});
+  gload(first + 1, S1{});
+  gload(first + 2, S2{});
+  lstore(0, S0{});
+  __syncthreads();
+  for (int k = 0; k < nst; k += 3) {
+    step(k, S1{}, S0{});
+    if (k + 1 < nst) step(k + 1, S2{}, S1{});
+    if (k + 2 < nst) step(k + 2, S0{}, S2{});
   }
 
   // Output: each 16-row strip of a wave's 64 x 64 tile goes through LDS (fp32,
@@ -241,6 +263,136 @@ __global__ __launch_bounds__(256) void gemm_nt_mfma_kernel(GemmArgs g) {
   }
 }
 
+// Short K (at most KS 64-byte slices per row: the dt projection, K = dt rank).
+// The general kernel spends most of its time waiting for the first operands of
+// each output block here, since a block has only a few K stages.  Instead each
+// wave keeps the B operands of one 64-column strip in registers for the whole
+// launch and streams 32-row chunks of A straight into the MFMA layout (lane l:
+// row l % 16, the 16 bytes at 16 (l / 16) of each 64-byte slice), the next
+// chunk's loads in flight while the current one is multiplied.  The four waves
+// of a workgroup take four adjacent strips of the same row chunks, so the A rows
+// (small, L2-resident) are fetched once per workgroup, and the workgroups that
+// share row chunks get ids congruent mod 8 (one XCD).  Results leave through a
+// per-wave LDS strip as 16-byte row segments.
+constexpr int kShortRows = 32;  // rows per chunk
+
+template <typename IN, typename OUT, int KS>
+__global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int chunks_per_wg) {
+  constexpr uint32_t E = sizeof(IN);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int ncg = (int)((g.N + 255) / 256);
+  const int64_t nchunks = (g.M + kShortRows - 1) / kShortRows;
+  const int64_t nrg = (nchunks + chunks_per_wg - 1) / chunks_per_wg;
+  const int64_t id = blockIdx.x;
+  const int64_t round = id / (8 * ncg), rem = id % (8 * ncg);
+  const int64_t rg = round * 8 + rem % 8;
+  if (rg >= nrg) return;
+  const int64_t n0 = (rem / 8) * 256 + 64 * w;  // this wave's column strip
+  const int64_t c0 = rg * chunks_per_wg;
+  const int64_t c1 = c0 + chunks_per_wg < nchunks ? c0 + chunks_per_wg : nchunks;
+  const uint32_t kbytes = (uint32_t)(g.K * E);
+
+  // B operands of the strip, for the whole launch
+  const int64_t nrows = g.N - n0 < 64 ? (g.N - n0 > 0 ? g.N - n0 : 0) : 64;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const IN*>(g.B) + (nrows > 0 ? n0 : 0) * g.ldb,
+                                              (uint32_t)(nrows > 0 ? ((nrows - 1) * g.ldb + g.K) * E : 0));
+  u32x4 b[4][KS];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t kb = (uint32_t)(64 * ks + 16 * q);
+      b[j][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+          rb, kb < kbytes ? (uint32_t)((16 * j + r16) * g.ldb * E) + kb : kOutOfRange, 0, 0);
+    }
+
+  // A rows of this workgroup's chunks
+  const int64_t arow0 = c0 * kShortRows;
+  const int64_t arows = (g.M < c1 * kShortRows ? g.M : c1 * kShortRows) - arow0;
+  const __amdgpu_buffer_rsrc_t ra =
+      make_rsrc(static_cast<const IN*>(g.A) + arow0 * g.lda, (uint32_t)(((arows - 1) * g.lda + g.K) * E));
+  auto aload = [&](u32x4 (&a)[2][KS], int64_t c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kb = (uint32_t)(64 * ks + 16 * q);
+        const int64_t row = (c - c0) * kShortRows + 16 * i + r16;  // < arows unless past M (then out of range)
+        a[i][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+            ra, c < c1 && kb < kbytes ? (uint32_t)(row * g.lda * E) + kb : kOutOfRange, 0, 0);
+      }
+  };
+
+  // output strip staging: 32 rows x 64 columns of fp32 per wave
+  __shared__ float stage[4][kShortRows][68];
+  float(*st)[68] = stage[w];
+  const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15u) == 0;
+  constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
+  constexpr int LPR = 64 / EPV;          // lanes per row
+  OUT* cbase = static_cast<OUT*>(g.C);
+
+  u32x4 a[2][KS], an[2][KS];
+  aload(a, c0);
+  for (int64_t c = c0; c < c1; ++c) {
+    aload(an, c + 1);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[i][j] = Mfma<IN>::step(a[i][ks], b[j][ks], acc[i][j]);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[16 * i + 4 * q + r][16 * j + r16] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave execute in order
+    const int64_t m0 = c * kShortRows;
+    const int64_t wrows = g.M - m0 < kShortRows ? g.M - m0 : kShortRows;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(cbase + m0 * g.ldc, (uint32_t)(((wrows - 1) * g.ldc + g.N) * sizeof(OUT)));
+#pragma unroll
+    for (int e0 = 0; e0 < kShortRows * LPR; e0 += 64) {
+      const int e = e0 + lane;
+      const int row = e / LPR, cc = (e % LPR) * EPV;
+      const int64_t gcol = n0 + cc;
+      float v[EPV];
+#pragma unroll
+      for (int kk = 0; kk < EPV; ++kk) v[kk] = st[row][cc + kk];
+      if (vec_ok && gcol + EPV <= g.N) {
+        const uint32_t off = (uint32_t)((row * g.ldc + gcol) * sizeof(OUT));
+        u32x4 pk;
+        if constexpr (sizeof(OUT) == 2) {
+          pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+          pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        } else {
+          pk = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(pk, rc, row < wrows ? off : kOutOfRange, 0, 0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < EPV; ++kk) {
+          const uint32_t off = gcol + kk < g.N ? (uint32_t)((row * g.ldc + gcol + kk) * sizeof(OUT)) : kOutOfRange;
+          store_elem<OUT>(rc, row < wrows ? off : kOutOfRange, v[kk]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[i][ks] = an[i][ks];
+  }
+}
+
 // Any alignment: one thread per output element, K FMAs.
 template <typename IN, typename OUT>
 __global__ void gemm_nt_valu_kernel(GemmArgs g) {
@@ -286,9 +438,43 @@ bool mfma_ok(const GemmArgs& g) {
 // C (OUT) = A B^T.  128 x 128 per workgroup of 2 x 2 waves of 4 x 4 tiles, two
 // K slices in flight; with parts > 1, K is split into parts and part z is
 // written (fp32) at C + z * split_stride.
+template <typename IN, typename OUT, int KS>
+hipError_t launch_shortk(const GemmArgs& g, hipStream_t st) {
+  const int64_t nchunks = (g.M + kShortRows - 1) / kShortRows;
+  const int64_t ncg = (g.N + 255) / 256;
+  // about four workgroups per CU over the launch, at least one chunk each
+  int64_t per = nchunks * ncg / 1024;
+  if (per < 1) per = 1;
+  const int64_t nrg = (nchunks + per - 1) / per;
+  const int64_t blocks = (nrg + 7) / 8 * 8 * ncg;  // whole groups of 8 (ids past the last row group exit)
+  hipLaunchKernelGGL((gemm_nt_shortk_kernel<IN, OUT, KS>), dim3((unsigned)blocks), dim3(256), 0, st, g, (int)per);
+  return hipGetLastError();
+}
+
+// Slices of 64 bytes per row that the short-K kernel is instantiated for: with
+// two workgroups per CU a wave has 256 VGPRs, which hold the B strip, two A
+// chunks and the accumulators up to six slices (384 bytes: dt rank 192 in bf16).
+constexpr int kShortMaxSlices = 6;
+
+template <typename IN, typename OUT>
+hipError_t gemm_nt_short(const GemmArgs& g, int ks, hipStream_t st) {
+  switch (ks) {
+    case 1: return launch_shortk<IN, OUT, 1>(g, st);
+    case 2: return launch_shortk<IN, OUT, 2>(g, st);
+    case 3: return launch_shortk<IN, OUT, 3>(g, st);
+    case 4: return launch_shortk<IN, OUT, 4>(g, st);
+    case 5: return launch_shortk<IN, OUT, 5>(g, st);
+    case 6: return launch_shortk<IN, OUT, 6>(g, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename IN, typename OUT>
 hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
+  if (mfma_ok<IN>(g) && parts == 1 && ks <= kShortMaxSlices && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr)
+    return gemm_nt_short<IN, OUT>(g, ks, st);
   if (mfma_ok<IN>(g)) {
     const int all = (int)((g.K * (int64_t)sizeof(IN) + kStageBytes - 1) / kStageBytes);
     g.sps = (all + parts - 1) / parts;
