@@ -124,6 +124,20 @@ int mamba_scan_fwd_complex(int64_t batch, int64_t seqlen, int64_t dim, int64_t d
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One recurrent decode step with complex A (the step of mamba_scan_fwd_complex,
+ * as mamba_state_update is the step of mamba_scan_fwd).
+ *   state            : (batch, dim, dstate, 2) float, (re, im) pairs, read and
+ *                      overwritten in place
+ *   A                : (dim, dstate, 2) float, (re, im) pairs
+ *   every other argument as for mamba_state_update.
+ * Limits as for mamba_state_update.
+ */
+int mamba_state_update_complex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
+                               const void* u, const void* delta, const float* delta_bias, const float* A,
+                               const void* B, const void* C, const float* Dskip, const void* z,
+                               int delta_softplus, void* out, void* stream);
+
+/*
  * One recurrent decode step (section 5: constant time per token, the state is
  * the whole memory): every (batch row, channel) advances by one token.
  *   state            : (batch, dim, dstate) float, read and overwritten in place

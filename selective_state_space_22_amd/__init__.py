@@ -10,10 +10,11 @@ from .binding import (MAMBA_IO_BF16, MAMBA_IO_F32, MambaError, load_library, mam
                       mamba_scan_bwd_workspace_size, mamba_scan_fwd, mamba_scan_fwd_complex,
                       mamba_scan_fwd_complex_workspace_size, mamba_scan_fwd_workspace_size,
                       mamba_selection_fwd, mamba_selection_fwd_workspace_size, mamba_ssm_fwd,
-                      mamba_ssm_fwd_workspace_size, mamba_state_update, mamba_version, status_string)
+                      mamba_ssm_fwd_workspace_size, mamba_state_update, mamba_state_update_complex, mamba_version,
+                      status_string)
 
 __all__ = ["mamba_scan_fwd", "mamba_scan_fwd_complex", "mamba_scan_fwd_complex_workspace_size", "mamba_scan_bwd",
-           "mamba_state_update", "mamba_scan_fwd_workspace_size",
+           "mamba_state_update", "mamba_state_update_complex", "mamba_scan_fwd_workspace_size",
            "mamba_scan_bwd_workspace_size", "mamba_selection_fwd", "mamba_selection_fwd_workspace_size",
            "mamba_ssm_fwd", "mamba_ssm_fwd_workspace_size", "mamba_version", "status_string", "load_library", "MambaError",
            "MAMBA_IO_F32", "MAMBA_IO_BF16"]

@@ -63,6 +63,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_scan_fwd_complex_workspace_size.restype = ctypes.c_size_t
     lib.mamba_scan_fwd_complex.argtypes = lib.mamba_scan_fwd.argtypes
     lib.mamba_scan_fwd_complex.restype = I
+    lib.mamba_state_update_complex.argtypes = lib.mamba_state_update.argtypes
+    lib.mamba_state_update_complex.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -229,6 +231,34 @@ def mamba_state_update(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=
         int(bool(delta_softplus)), _ptr(out, "out", u.dtype, (batch, D), dev), _stream(dev))
     if st != 0:
         raise MambaError("mamba_state_update", st)
+    return out
+
+
+def mamba_state_update_complex(state, u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True,
+                               out=None):
+    """One decode step with complex A, in place on state: (batch, D, N) complex64 or (batch, D, N, 2)
+    float32.  A: (D, N) complex64 or (D, N, 2) float32; the rest as for mamba_state_update."""
+    import torch
+
+    lib = load_library()
+    batch, D = u.shape
+    N = A.shape[1]
+    A = _re_im(A, "A")
+    st_ri = _re_im(state, "state")
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty_like(u)
+    st = lib.mamba_state_update_complex(
+        batch, D, N, io, _ptr(st_ri, "state", f32, (batch, D, N, 2), dev),
+        _ptr(u, "u", u.dtype, (batch, D), dev), _ptr(delta, "delta", u.dtype, (batch, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N, 2), dev),
+        _ptr(B, "B", u.dtype, (batch, N), dev), _ptr(C, "C", u.dtype, (batch, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, D), dev),
+        int(bool(delta_softplus)), _ptr(out, "out", u.dtype, (batch, D), dev), _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_state_update_complex", st)
     return out
 
 

@@ -53,6 +53,47 @@ struct PtrCheck {
   void opt(const void* p, const char* name) { req(p, false, name); }
 };
 
+// Validation and launch shared by the real and complex decode steps.
+int state_update(bool cplx, const char* where, int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
+                 float* state, const void* u, const void* delta, const float* delta_bias, const float* A,
+                 const void* B, const void* C, const float* Dskip, const void* z, int delta_softplus, void* out,
+                 void* stream) {
+  int st = check_shape(where, batch, 1, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  const bool any = batch > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(state, any, "state");
+  pc.req(u, any, "u");
+  pc.req(delta, any, "delta");
+  pc.req(A, any, "A");
+  pc.req(B, any, "B");
+  pc.req(C, any, "C");
+  pc.req(out, any, "out");
+  pc.opt(delta_bias, "delta_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(z, "z");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (!any) return MAMBA_OK;
+  s6::StepArgs a;
+  a.state = state;
+  a.u = u;
+  a.delta = delta;
+  a.bias = delta_bias;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.dskip = Dskip;
+  a.z = z;
+  a.out = out;
+  a.batch = batch;
+  a.D = dim;
+  a.softplus = delta_softplus != 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = cplx ? s6::launch_step_complex(a, io_dtype, (int)dstate, s) : s6::launch_step(a, io_dtype, (int)dstate, s);
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
+  return MAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,40 +239,16 @@ int mamba_state_update(int64_t batch, int64_t dim, int64_t dstate, int io_dtype,
                        const void* u, const void* delta, const float* delta_bias, const float* A,
                        const void* B, const void* C, const float* Dskip, const void* z,
                        int delta_softplus, void* out, void* stream) {
-  const char* where = "mamba_state_update";
-  int st = check_shape(where, batch, 1, dim, dstate, io_dtype);
-  if (st != MAMBA_OK) return st;
-  const bool any = batch > 0 && dim > 0;
-  PtrCheck pc{where};
-  pc.req(state, any, "state");
-  pc.req(u, any, "u");
-  pc.req(delta, any, "delta");
-  pc.req(A, any, "A");
-  pc.req(B, any, "B");
-  pc.req(C, any, "C");
-  pc.req(out, any, "out");
-  pc.opt(delta_bias, "delta_bias");
-  pc.opt(Dskip, "Dskip");
-  pc.opt(z, "z");
-  if (pc.status != MAMBA_OK) return pc.status;
-  if (!any) return MAMBA_OK;
-  s6::StepArgs a;
-  a.state = state;
-  a.u = u;
-  a.delta = delta;
-  a.bias = delta_bias;
-  a.A = A;
-  a.B = B;
-  a.C = C;
-  a.dskip = Dskip;
-  a.z = z;
-  a.out = out;
-  a.batch = batch;
-  a.D = dim;
-  a.softplus = delta_softplus != 0;
-  hipError_t e = s6::launch_step(a, io_dtype, (int)dstate, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(e));
-  return MAMBA_OK;
+  return state_update(false, "mamba_state_update", batch, dim, dstate, io_dtype, state, u, delta, delta_bias, A, B,
+                      C, Dskip, z, delta_softplus, out, stream);
+}
+
+int mamba_state_update_complex(int64_t batch, int64_t dim, int64_t dstate, int io_dtype, float* state,
+                               const void* u, const void* delta, const float* delta_bias, const float* A,
+                               const void* B, const void* C, const float* Dskip, const void* z,
+                               int delta_softplus, void* out, void* stream) {
+  return state_update(true, "mamba_state_update_complex", batch, dim, dstate, io_dtype, state, u, delta, delta_bias,
+                      A, B, C, Dskip, z, delta_softplus, out, stream);
 }
 
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype) {

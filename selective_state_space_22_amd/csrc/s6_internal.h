@@ -111,6 +111,8 @@ bool dstate_supported(int64_t N);
 ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N);
 hipError_t launch_scan_complex(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace,
                                hipStream_t stream);
+// One decode token with complex A: state is (batch, D, N, 2), A (D, N, 2).
+hipError_t launch_step_complex(const StepArgs& a, int io, int N, hipStream_t stream);
 // Carry pass over complex (batch, chunk, D, N, 2) chunk aggregates.
 hipError_t launch_cplx_carry(const ScanArgs& a, int N, hipStream_t stream);
 

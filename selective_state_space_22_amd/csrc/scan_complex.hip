@@ -188,6 +188,64 @@ __global__ __launch_bounds__(256) void cplx_output_kernel(CplxArgs c) {
   }
 }
 
+// One decode token with complex A: lane = channel d of batch row blockIdx.y,
+// its N (re, im) states read from and written back to state in place.
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void cplx_state_update_kernel(StepArgs a) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = blockIdx.y;
+  if (d >= a.D) return;
+  const int64_t idx = b * a.D + d;
+  float Bt[N], Ct[N], hr[N], hi[N];
+  load_bc<IO, N>(static_cast<const IO*>(a.B) + b * N, Bt);
+  load_bc<IO, N>(static_cast<const IO*>(a.C) + b * N, Ct);
+  CplxA cc[N];
+  const float maxim = load_a<N>(a.A + d * N * 2, cc);
+  float* __restrict__ st = a.state + (size_t)idx * N * 2;
+  if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {  // two (re, im) pairs per float4
+      const float4 v = reinterpret_cast<const float4*>(st)[j];
+      hr[2 * j] = v.x;
+      hi[2 * j] = v.y;
+      hr[2 * j + 1] = v.z;
+      hi[2 * j + 1] = v.w;
+    }
+  } else {
+    hr[0] = st[0];
+    hi[0] = st[1];
+  }
+  const float x = load_io(static_cast<const IO*>(a.u), idx);
+  const TokenFront f =
+      make_front(load_io(static_cast<const IO*>(a.delta), idx), a.bias ? a.bias[d] : 0.0f, a.softplus != 0);
+  const float y = ctoken<N, true>(cc, maxim, f, x, Bt, Ct, hr, hi);
+  const bool has_z = a.z != nullptr;
+  const float zv = has_z ? load_io(static_cast<const IO*>(a.z), idx) : 0.0f;
+  store_io(static_cast<IO*>(a.out), idx, epilogue(y, x, a.dskip ? a.dskip[d] : 0.0f, has_z, zv));
+  if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j)
+      reinterpret_cast<float4*>(st)[j] = make_float4(hr[2 * j], hi[2 * j], hr[2 * j + 1], hi[2 * j + 1]);
+  } else {
+    st[0] = hr[0];
+    st[1] = hi[0];
+  }
+}
+
+template <typename IO>
+hipError_t launch_cplx_step_io(const StepArgs& a, int N, hipStream_t st) {
+  const dim3 grid((unsigned)((a.D + 255) / 256), (unsigned)a.batch);
+  switch (N) {
+    case 1: hipLaunchKernelGGL((cplx_state_update_kernel<IO, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((cplx_state_update_kernel<IO, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((cplx_state_update_kernel<IO, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((cplx_state_update_kernel<IO, 8>), grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((cplx_state_update_kernel<IO, 16>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 __global__ void cplx_empty_kernel(float* last, const float* h0, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) last[i] = h0 ? h0[i] : 0.0f;
@@ -235,6 +293,11 @@ hipError_t launch_cplx_carry(const ScanArgs& a, int N, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
+}
+
+hipError_t launch_step_complex(const StepArgs& a, int io, int N, hipStream_t st) {
+  if (a.batch == 0 || a.D == 0) return hipSuccess;
+  return io == kIoBF16 ? launch_cplx_step_io<uint16_t>(a, N, st) : launch_cplx_step_io<float>(a, N, st);
 }
 
 hipError_t launch_scan_complex(const ScanArgs& in, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                                     "mamba_scan_fwd_complex", "mamba_scan_fwd_complex_workspace_size",
                                     "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
                                     "mamba_selection_fwd_workspace_size", "mamba_ssm_fwd",
-                                    "mamba_ssm_fwd_workspace_size", "mamba_state_update", "mamba_status_string",
+                                    "mamba_ssm_fwd_workspace_size", "mamba_state_update", "mamba_state_update_complex",
+                                    "mamba_status_string",
                                     "mamba_version"]
 
 
@@ -238,3 +239,17 @@ def test_complex_scan_validation_and_workspace(lib):
     assert call(L=1 << 20, D=256) == ERR_WORKSPACE
     assert call(L=1 << 20, D=256, ws_ptr=FAKE, ws_bytes=w - 1) == ERR_WORKSPACE
     assert call(batch=0, u=None, A=None, out=None) == OK
+
+
+def test_complex_state_update_validation(lib):
+    def call(batch=2, D=64, N=16, io=0, state=FAKE, u=FAKE, A=FAKE, out=FAKE):
+        return lib.mamba_state_update_complex(batch, D, N, io, state, u, FAKE, None, A, FAKE, FAKE, None, None, 1,
+                                              out, None)
+
+    assert call(io=4) == ERR_DTYPE
+    assert call(N=3) == ERR_UNSUPPORTED
+    assert call(D=-1) == ERR_DIM
+    for field in ("state", "u", "A", "out"):
+        assert call(**{field: None}) == ERR_NULL, field
+        assert call(**{field: FAKE + 4}) == ERR_ALIGN, field
+    assert call(batch=0, state=None, u=None, A=None, out=None) == OK

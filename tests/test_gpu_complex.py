@@ -191,3 +191,56 @@ def test_mamba3b_layer_sampled():
     el = cerr(gl[bs][:, chans], rl)
     print(f"mamba3b complex sampled: out err {eo:.3e} last err {el:.3e}")
     assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+def test_decode_matches_oracle(io, N):
+    """L one-token steps of mamba_state_update_complex from a complex h0 equal the
+    oracle's complex scan over the same L tokens: every step's output and the final state."""
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_state_update_complex
+
+    _announce(f"complex decode (3, 24 steps, 130, {N}) {io}")
+    L, D, batch = 24, 130, 3
+    inp, Ac = _cinputs(batch, L, D, N, io, seed=W.SEED_BASE + 81 + N)
+    h0 = _h0(batch, D, N, 10)
+    d = to_device(inp, "cuda")
+    At = torch.from_numpy(np.ascontiguousarray(Ac)).to("cuda")
+    state = torch.from_numpy(np.ascontiguousarray(h0)).to("cuda")
+    outs = []
+    for t in range(L):
+        sl = lambda x: None if x is None else x[:, t].contiguous()
+        outs.append(mamba_state_update_complex(state, sl(d["u"]), sl(d["delta"]), At, sl(d["B"]), sl(d["C"]),
+                                               d["delta_bias"], d["Dskip"], sl(d["z"]), True))
+    torch.cuda.synchronize()
+    go = to_host(torch.stack(outs, 1))
+    gl = state.cpu().numpy()
+    ro, rl = ref_cscan(inp, Ac, h0)
+    eo, el = parity_error(go, ro), cerr(gl, rl)
+    print(f"complex decode N={N} {io}: out err {eo:.3e} state err {el:.3e}")
+    assert eo <= TOL[io] and el <= TOL[io]
+
+
+def test_decode_continues_the_scan():
+    """A scan over the first 40 tokens, then 8 decode steps from its last state,
+    equals the scan over all 48 tokens (outputs of the last 8, final state)."""
+    _need_gpu()
+    from selective_state_space_22_amd import mamba_state_update_complex
+
+    inp, Ac = _cinputs(2, 48, 96, 16, "f32", seed=W.SEED_BASE + 99)
+    d = to_device(inp, "cuda")
+    go_all, gl_all = gpu_cscan(inp, Ac)
+    head = dataclasses.replace(inp, seqlen=40, **{k: np.ascontiguousarray(getattr(inp, k)[:, :40])
+                                                  for k in ("u", "delta", "z", "B", "C")})
+    _, gl_head = gpu_cscan(head, Ac)
+    At = torch.from_numpy(np.ascontiguousarray(Ac)).to("cuda")
+    state = torch.from_numpy(np.ascontiguousarray(gl_head)).to("cuda")
+    outs = []
+    for t in range(40, 48):
+        sl = lambda x: x[:, t].contiguous()
+        outs.append(mamba_state_update_complex(state, sl(d["u"]), sl(d["delta"]), At, sl(d["B"]), sl(d["C"]),
+                                               d["delta_bias"], d["Dskip"], sl(d["z"]), True))
+    torch.cuda.synchronize()
+    assert parity_error(to_host(torch.stack(outs, 1)), go_all[:, 40:]) <= 1e-5
+    assert cerr(state.cpu().numpy(), gl_all) <= 1e-5
