@@ -29,7 +29,9 @@ VALU_FP32_PACKED_TFLOPS = 157.3  # published fp32 vector peak (packed fp32, not 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak, published
 MFMA_F32_PEAK_TFLOPS = 157.3     # dense fp32 matrix peak, published
 # Algorithmic fp32 operations (FMA = 2, other ops and transcendentals = 1):
-FLOPS_PER_ELEMENT = 9.0          # per (b, l, d, n): dt*A, exp, input weight, *B, *x, h FMA, readout FMA
+# per (b, l, d, n): dt*A (1), exp (1), input weight (Abar - 1)/A as one FMA (2), B*x (1), beta*Bx (1),
+# h FMA (2), readout FMA (2); the small-dt*A guard of the input weight is not counted
+FLOPS_PER_ELEMENT = 10.0
 FLOPS_PER_TOKEN_CHANNEL = 15.0   # per (b, l, d): bias add, softplus (6), skip FMA, SiLU (5), gate mul
 # Backward, per (b, l, d, n) on top of the recomputed forward: gradient recurrence FMA, dC and dB products,
 # du FMA, d(beta) and d(Abar) products, ddt FMAs, d beta/d A (series or difference), two dA FMAs, state-gradient decay
