@@ -141,7 +141,8 @@ __device__ __forceinline__ void token_step_state(const ChanConst<N>& cc, const T
 // tokens, so any bias in Abar grows linearly in the state.  The hardware
 // v_sin_f32 / v_cos_f32 (errors up to ~3e-7, ~5 ulp) measured four times the
 // error budget of an fp32 scan this way; sin and cos are therefore evaluated
-// here from their Taylor series (about 1 ulp).  Below |dt A_n| = 0.02 the input
+// here from their Taylor series (about 1 ulp), with fewer terms when a wave's
+// angles of the token are all small.  Below |dt A_n| = 0.02 the input
 // weight is the series dt (1 + x/2 + x^2/6) (truncation <= |x|^3/24 < 4e-7);
 // above it the quotient, whose cancellation costs err(Abar)/|x| < 1e-5.
 constexpr float kCplxSeriesX2 = 0.02f * 0.02f;
@@ -149,6 +150,20 @@ constexpr float kQuarterPi = 0.78539816339744831f;
 constexpr float k2OverPi = 0.63661977236758134f;
 constexpr float kHalfPiHi = 1.57079637050628662f;    // float(pi/2)
 constexpr float kHalfPiLo = -4.37113900018624e-8f;   // pi/2 - kHalfPiHi
+
+constexpr float kTinyAngle = 0.25f;
+
+// sin r and cos r for |r| <= 1/4: Taylor series through r^7 and r^6
+// (truncation below 1e-11 and 4e-10).
+__device__ __forceinline__ void sincos_tiny(float r, float& s, float& c) {
+  const float r2 = r * r;
+  float ps = __builtin_fmaf(r2, -1.0f / 5040.0f, 1.0f / 120.0f);
+  ps = __builtin_fmaf(r2, ps, -1.0f / 6.0f);
+  s = __builtin_fmaf(r * r2, ps, r);
+  float pc = __builtin_fmaf(r2, -1.0f / 720.0f, 1.0f / 24.0f);
+  pc = __builtin_fmaf(r2, pc, -0.5f);
+  c = __builtin_fmaf(r2, pc, 1.0f);
+}
 
 // sin r and cos r for |r| <= pi/4: Taylor series through r^9 and r^10
 // (truncation below 2e-9 and 6e-11).
@@ -197,14 +212,18 @@ struct CplxA {
   }
 };
 
+// Angle ranges of the sin/cos evaluation: |dt Im A_n| <= 1/4, <= pi/4, any.
+enum AngleTier { kAngleTiny = 0, kAngleSmall = 1, kAngleAny = 2 };
+
 // One token of eq. (3a) for one complex state: h = Abar h + beta * bx, bx = B_t,n x_t.
-// SMALL: the caller has checked |dt Im A_n| <= pi/4 (no angle reduction needed).
-template <bool SMALL>
+// TIER: the range the caller has checked |dt Im A_n| to be in.
+template <int TIER>
 __device__ __forceinline__ void cplx_update(const CplxA& a, float dt, float dt2, float bx, float& hr, float& hi) {
   const float xr = dt * a.re, xi = dt * a.im;
   const float mag = ex2(xr * kLog2e);
   float sn, cs;
-  if (SMALL) sincos_small(xi, sn, cs);
+  if (TIER == kAngleTiny) sincos_tiny(xi, sn, cs);
+  else if (TIER == kAngleSmall) sincos_small(xi, sn, cs);
   else sincos_any(xi, sn, cs);
   const float abr = mag * cs, abi = mag * sn;
   // (Abar - 1) / A
@@ -224,9 +243,14 @@ __device__ __forceinline__ void cplx_update(const CplxA& a, float dt, float dt2,
   hi = ni;
 }
 
-// True when every active lane's angles dt |Im A_n| are at most pi/4 (maxim:
-// the lane's largest |Im A_n|), so that all of them can skip the reduction.
-__device__ __forceinline__ bool wave_small_angles(float dt, float maxim) { return __all(dt * maxim <= kQuarterPi); }
+// The smallest tier that holds for every active lane's angles dt |Im A_n|
+// (maxim: the lane's largest |Im A_n|); one decision per wave and token.
+__device__ __forceinline__ int wave_angle_tier(float dt, float maxim) {
+  const float m = dt * maxim;
+  if (__all(m <= kTinyAngle)) return kAngleTiny;
+  if (__all(m <= kQuarterPi)) return kAngleSmall;
+  return kAngleAny;
+}
 
 // e^{A_n s} for a sum s of dt (chunk carries).
 __device__ __forceinline__ void cplx_decay(const CplxA& a, float s, float& pr, float& pi) {

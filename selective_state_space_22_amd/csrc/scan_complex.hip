@@ -23,26 +23,29 @@
 namespace s6 {
 namespace {
 
+// One token for all N complex states with the sin/cos of one angle tier.
+template <int N, bool READ, int TIER>
+__device__ __forceinline__ float ctoken_tier(const CplxA (&c)[N], const TokenFront& f, float x, const float* Bt,
+                                             const float* Ct, float (&hr)[N], float (&hi)[N]) {
+  float y = 0.0f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    cplx_update<TIER>(c[n], f.dt, f.dt2, Bt[n] * x, hr[n], hi[n]);
+    if (READ) y = __builtin_fmaf(Ct[n], hr[n], y);
+  }
+  return y;
+}
+
 // One token for all N complex states; returns Re(C . h) when READ.  maxim: the
 // lane's largest |Im A_n| (small angles take the shorter sin/cos).
 template <int N, bool READ>
 __device__ __forceinline__ float ctoken(const CplxA (&c)[N], float maxim, const TokenFront& f, float x,
                                         const float* Bt, const float* Ct, float (&hr)[N], float (&hi)[N]) {
-  float y = 0.0f;
-  if (wave_small_angles(f.dt, maxim)) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      cplx_update<true>(c[n], f.dt, f.dt2, Bt[n] * x, hr[n], hi[n]);
-      if (READ) y = __builtin_fmaf(Ct[n], hr[n], y);
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      cplx_update<false>(c[n], f.dt, f.dt2, Bt[n] * x, hr[n], hi[n]);
-      if (READ) y = __builtin_fmaf(Ct[n], hr[n], y);
-    }
+  switch (wave_angle_tier(f.dt, maxim)) {
+    case kAngleTiny: return ctoken_tier<N, READ, kAngleTiny>(c, f, x, Bt, Ct, hr, hi);
+    case kAngleSmall: return ctoken_tier<N, READ, kAngleSmall>(c, f, x, Bt, Ct, hr, hi);
+    default: return ctoken_tier<N, READ, kAngleAny>(c, f, x, Bt, Ct, hr, hi);
   }
-  return y;
 }
 
 // The channel's A (N (re, im) pairs); returns the largest |Im A_n|.

@@ -297,24 +297,27 @@ struct WgScan {
     }
   }
 
+  // Complex A: one token for this wave's S states with the sin/cos of one angle tier.
+  template <int TIER>
+  __device__ __forceinline__ float cstep(const Tok& t) {
+    float y = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      cplx_update<TIER>(ca[s], t.fv.x, t.fv.y, t.bc[s] * t.fv.z, h[s], hq[s]);
+      if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
+    }
+    return y;
+  }
+
   // One token of the recurrence for this wave's S states (eq. (2), (3a)) and
   // its partial readout sum_s C_t[s] h_t[s] (eq. (3b)).
   __device__ __forceinline__ void step(const Tok& t, int y2, int j) {
     float y = 0.0f;
     if constexpr (CPLX) {
-      if (wave_small_angles(t.fv.x, maxim)) {
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          cplx_update<true>(ca[s], t.fv.x, t.fv.y, t.bc[s] * t.fv.z, h[s], hq[s]);
-          if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          cplx_update<false>(ca[s], t.fv.x, t.fv.y, t.bc[s] * t.fv.z, h[s], hq[s]);
-          if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
-        }
-      }
+      const int tier = wave_angle_tier(t.fv.x, maxim);
+      if (tier == kAngleTiny) y = cstep<kAngleTiny>(t);
+      else if (tier == kAngleSmall) y = cstep<kAngleSmall>(t);
+      else y = cstep<kAngleAny>(t);
       if (kOut) sm.yp[y2][j][w][lane] = y;
       return;
     }

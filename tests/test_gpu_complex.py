@@ -244,3 +244,19 @@ def test_decode_continues_the_scan():
     torch.cuda.synchronize()
     assert parity_error(to_host(torch.stack(outs, 1)), go_all[:, 40:]) <= 1e-5
     assert cerr(state.cpu().numpy(), gl_all) <= 1e-5
+
+
+@pytest.mark.parametrize("engine", ["default", "lane"])
+def test_angles_in_every_sin_cos_range(engine, monkeypatch):
+    """Per-token angles dt Im A_n from below 1/4 rad to ~40 rad, so that waves take the
+    short series, the pi/4 series and the reduced evaluation of sin and cos."""
+    _need_gpu()
+    _engine(monkeypatch, engine)
+    rng = np.random.default_rng(12)
+    D, N = 128, 16
+    Ac = (-rng.uniform(0.2, 3.0, (D, N)) + 1j * rng.uniform(-200.0, 200.0, (D, N))).astype(np.complex64)
+    Ac[:64] = (Ac[:64].real + 1j * rng.uniform(-1.0, 1.0, (64, N))).astype(np.complex64)  # one wave of small angles
+    inp, _ = _cinputs(2, 400, D, N, "f32", seed=W.SEED_BASE + 100)
+    inp = dataclasses.replace(inp, delta_bias=None, delta=(np.abs(inp.delta) * 0.05).astype(np.float32))
+    eo, el = check(inp, Ac, h0=_h0(2, D, N, 13), softplus=False, label=f"angles {engine}")
+    print(f"angle ranges {engine}: out err {eo:.3e} last err {el:.3e}")
