@@ -170,3 +170,52 @@ def test_ssm_graph_replays_match_eager():
                               last_state=last, workspace=ws)
 
     _replay_matches(call, [out, last])
+
+
+@pytest.mark.parametrize("shape", [(5, 1100, 4096, 16, "bf16"), (1, 4096, 64, 16, "f32"), (1, 600, 64, 4, "f32")],
+                         ids=["chained", "split", "lane"])
+def test_complex_scan_graph_replays_match_eager(shape):
+    """mamba_scan_fwd_complex on the workgroup engine (chained and split, whose carry
+    pass composes complex aggregates) and on the lane kernels."""
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+
+    batch, L, D, N, io = shape
+    print(f"\n[gpu-test] graph replay of mamba_scan_fwd_complex {shape}", flush=True)
+    inp = W.generate(batch, L, D, N, io, seed=321)
+    d = to_device(inp)
+    A = torch.from_numpy(W.a_init_complex(D, N)).cuda()
+    h0 = torch.randn((batch, D, N), dtype=torch.complex64, device="cuda")
+    out = torch.empty_like(d["u"])
+    last = torch.empty((batch, D, N, 2), device="cuda")
+    ws = torch.empty(max(binding.mamba_scan_fwd_complex_workspace_size(batch, L, D, N, 1 if io == "bf16" else 0), 1),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.mamba_scan_fwd_complex(d["u"], d["delta"], A, d["B"], d["C"], d["delta_bias"], d["Dskip"], d["z"], True,
+                                       h0, out=out, last_state=last, workspace=ws)
+
+    _replay_matches(call, [out, last])
+
+
+def test_complex_decode_graph_replays_match_eager():
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+
+    print("\n[gpu-test] graph replay of 8 mamba_state_update_complex steps (4, 512, 16) bf16", flush=True)
+    inp = W.generate(4, 8, 512, 16, "bf16", seed=77)
+    d = to_device(inp)
+    A = torch.from_numpy(W.a_init_complex(512, 16)).cuda()
+    state0 = torch.randn((4, 512, 16), dtype=torch.complex64, device="cuda")
+    state = state0.clone()
+    steps = [(d["u"][:, t].contiguous(), d["delta"][:, t].contiguous(), d["B"][:, t].contiguous(),
+              d["C"][:, t].contiguous(), d["z"][:, t].contiguous()) for t in range(8)]
+    outs = [torch.empty_like(steps[0][0]) for _ in range(8)]
+    view = torch.view_as_real(state)
+
+    def call():
+        state.copy_(state0)
+        for (u, dl, B, C, z), o in zip(steps, outs):
+            binding.mamba_state_update_complex(state, u, dl, A, B, C, d["delta_bias"], d["Dskip"], z, True, out=o)
+
+    _replay_matches(call, outs + [view])
