@@ -14,7 +14,10 @@ Two independent implementations of the same definition live here:
   * ``scan_complex``: the forward with complex diagonal A (the page's
     -1/2 + ni initialisation), real x, B, C and output Re(C . h);
   * ``selection``: the section 3.2 projections (B, C = Linear_N(x), dt from a
-    rank-R projection of x expanded to the D channels), fp64 matrix products.
+    rank-R projection of x expanded to the D channels), fp64 matrix products;
+  * ``block``: a Mamba block as Figure 3 and section 5 describe it (input
+    projection to a SiLU-activated SSM branch and a gate branch, the selective
+    SSM, output projection), composed of ``selection`` and ``scan``.
 Both follow "Mamba 状态空间模型原理与 Transformer 对比" (kb.agiseed.tech):
 section 2.1 eq. (2) (ZOH), eq. (3a)/(3b) (recurrence and readout),
 section 3.2 (selection: per-token dt through softplus, B/C shared by channels)
@@ -230,3 +233,35 @@ def selection(x, W_x, W_dt, dstate, store=None, store_delta=True):
     if store_delta:
         delta = keep(delta)
     return delta, np.ascontiguousarray(xdbl[..., R:R + N]), np.ascontiguousarray(xdbl[..., R + N:])
+
+
+def _silu64(v):
+    v = np.asarray(v, np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def block(hidden, W_in, W_x, W_dt, dt_bias, A, Dskip, W_out, dstate, softplus=True, h0=None, store=None,
+          nthreads: int | None = None):
+    """fp64 forward of one Mamba block (Figure 3; section 5: the block widens the
+    model dimension by an expansion factor through linear projections around the SSM).
+    hidden (batch, L, d_model); W_in (2 D, d_model): its first D rows project to the
+    SSM branch, the last D rows to the gate branch; W_out (d_model, D).
+        x   = SiLU(hidden W_in[:D]^T)        (the activation that replaces H3's first gate)
+        z   = hidden W_in[D:]^T              (the gate branch)
+        delta, B, C = selection(x, W_x, W_dt)
+        y   = scan(x, delta, A, B, C, dt_bias, Dskip, z)   (skip term, then the SiLU(z) gate)
+        out = y W_out^T
+    The page shows no convolution in the block; none is applied.  ``store`` maps
+    fp64 values to the type the intermediate per-token tensors (x, z, the selection
+    results, y) are kept in; None keeps fp64.  Returns (out, last_state)."""
+    keep = store if store is not None else (lambda a: a)
+    hidden = np.asarray(hidden, np.float64)
+    W_in = np.asarray(W_in, np.float64)
+    W_out = np.asarray(W_out, np.float64)
+    D = W_in.shape[0] // 2
+    assert W_in.shape == (2 * D, hidden.shape[-1]) and W_out.shape == (hidden.shape[-1], D)
+    x = keep(_silu64(hidden @ W_in[:D].T))
+    z = keep(hidden @ W_in[D:].T)
+    delta, B, C = selection(x, W_x, W_dt, dstate, store=store)
+    y, last = scan(x, delta, A, B, C, dt_bias, Dskip, z, softplus, h0, nthreads=nthreads)
+    return keep(y) @ W_out.T, last
