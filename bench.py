@@ -165,9 +165,10 @@ def main():
     ap.add_argument("--flush", action="store_true", help="evict the 256 MB Infinity Cache before every step")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step from a captured HIP graph (auto: on for decode, whose step is 64 launches)")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "sel", "ssm", "complex"], default="fwd",
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "sel", "ssm", "complex", "block"], default="fwd",
                     help="fwd: mamba_scan_fwd (the headline); bwd: mamba_scan_bwd on the same workload; "
                          "complex: mamba_scan_fwd_complex with A_n = -1/2 + n i; "
+                         "block: mamba_block_fwd, d_model = D / 2 (input and output projections around ssm); "
                          "sel: the selection projections (mamba_selection_fwd, dt rank d_model/16); "
                          "ssm: selection then scan (mamba_ssm_fwd)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -195,7 +196,7 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     if args.which != "fwd" and w.decode_steps > 0:
-        print("bench.py: --pass bwd/sel/ssm/complex apply to the full-sequence workloads, not decode",
+        print("bench.py: --pass bwd/sel/ssm/complex/block apply to the full-sequence workloads, not decode",
               file=sys.stderr)
         sys.exit(2)
     inp = W.generate_workload(args.workload)
@@ -252,6 +253,28 @@ def main():
         bytes_per_step = (4 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
                           + 3 * io_bytes * w.batch * w.seqlen * w.dim + 2 * io_bytes * w.batch * w.seqlen * w.dstate
                           + 8 * w.dim * w.dstate + 16 * w.dim + 8 * w.batch * w.dim * w.dstate)
+    elif args.which == "block":
+        R = W.dt_rank_for(w.dim)
+        dm = w.dim // 2
+        sw = W.selection_weights(w.dim, w.dstate, R, w.io, seed=w.seed)
+        bw = W.block_weights(dm, w.dim, w.io, seed=w.seed)
+        hidden = t(W.block_hidden(w.batch, w.seqlen, dm, w.io, seed=w.seed))
+        wx, wdt, win, wout = t(sw.W_x), t(sw.W_dt), t(bw.W_in), t(bw.W_out)
+        out = torch.empty_like(hidden)
+        last = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(binding.mamba_block_fwd_workspace_size(w.batch, w.seqlen, dm, w.dim, w.dstate, R,
+                                                                    1 if w.io == "bf16" else 0), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.mamba_block_fwd(hidden, win, wx, wdt, A, wout, dt_bias=bias, Dskip=dskip, out=out,
+                                    last_state=last, workspace=ws)
+
+        units = w.elements
+        M = w.batch * w.seqlen
+        # matrix-core work: input projection (2 D outputs), x_proj, dt_proj, output projection
+        block_mfma_flops = 2.0 * M * (2 * w.dim * dm + w.dim * (R + 2 * w.dstate) + R * w.dim + dm * w.dim)
+        bytes_per_step = io_bytes * (2 * M * dm + 3 * w.dim * dm + M * w.dim) + 8 * w.dim + 4 * w.dim * w.dstate
     elif args.which in ("sel", "ssm"):
         R = W.dt_rank_for(w.dim)
         sw = W.selection_weights(w.dim, w.dstate, R, w.io, seed=w.seed)
@@ -363,7 +386,13 @@ def main():
         # per (b, l, d, n): forward recompute (9) as above plus the reverse step (~20 fp32 ops, FMA = 2)
         flops = units * (FLOPS_PER_ELEMENT + BWD_FLOPS_PER_ELEMENT) + (units / w.dstate) * 30.0
         tflops = flops / (ms * 1e-3) / 1e12
-    if args.which == "sel":
+    if args.which == "block":
+        peak = MFMA_BF16_PEAK_TFLOPS if w.io == "bf16" else MFMA_F32_PEAK_TFLOPS
+        mt = block_mfma_flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(mt, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(mt / peak, 4),
+                "traffic": traffic, "scan_alu_tflops": round(tflops, 2),
+                "note": "projection flops over the whole step, whose time includes the VALU-bound scan"}
+    elif args.which == "sel":
         peak = MFMA_BF16_PEAK_TFLOPS if w.io == "bf16" else MFMA_F32_PEAK_TFLOPS
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -384,7 +413,8 @@ def main():
                    "bwd": "selective-scan bwd elements(B*L*D*N)/s (all gradients, states recomputed)",
                    "sel": "selection projections: delta elements (B*L*D)/s (x_proj + dt_proj GEMMs)",
                    "ssm": "selective SSM from x: elements(B*L*D*N)/s (selection GEMMs + scan)",
-                   "complex": "selective-scan fwd with complex A: elements(B*L*D*N)/s"}[args.which],
+                   "complex": "selective-scan fwd with complex A: elements(B*L*D*N)/s",
+                   "block": "Mamba block fwd (projections + selection + scan): elements(B*L*D*N)/s"}[args.which],
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,

@@ -242,6 +242,32 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
                   const float* A, const float* Dskip, int delta_softplus, const float* h0,
                   void* out, float* last_state, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One Mamba block (Figure 3: the H3 block merged with an MLP block, its first
+ * multiplicative gate replaced by an activation; section 5: the block widens the
+ * model dimension d_model to dim = E * d_model through linear projections):
+ *   x   = SiLU(hidden W_in[:dim]^T)      SSM branch
+ *   z   = hidden W_in[dim:]^T            gate branch
+ *   y   = mamba_ssm_fwd(x, z, ...)       selection, scan, skip, SiLU(z) gate
+ *   out = y W_out^T
+ * The page shows no convolution inside the block and none is applied.
+ *   hidden, out      : (batch, seqlen, d_model)   I/O type
+ *   W_in             : (2 * dim, d_model)         I/O type
+ *   W_out            : (d_model, dim)             I/O type
+ *   W_x, W_dt, dt_bias, A, Dskip, delta_softplus, h0, last_state: as for mamba_ssm_fwd
+ *   workspace        : at least mamba_block_fwd_workspace_size() bytes: x, z and
+ *                      y (I/O type) and the selective SSM's workspace.
+ * The three projections run on the matrix cores with fp32 accumulation; x, z
+ * and y are stored in the I/O type, as a framework would keep them.
+ */
+size_t mamba_block_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim, int64_t dstate,
+                                      int64_t dt_rank, int io_dtype);
+int mamba_block_fwd(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim, int64_t dstate, int64_t dt_rank,
+                    int io_dtype, const void* hidden, const void* W_in, const void* W_x, const void* W_dt,
+                    const float* dt_bias, const float* A, const float* Dskip, const void* W_out, int delta_softplus,
+                    const float* h0, void* out, float* last_state, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_scan_fwd_complex.restype = I
     lib.mamba_state_update_complex.argtypes = lib.mamba_state_update.argtypes
     lib.mamba_state_update_complex.restype = I
+    lib.mamba_block_fwd_workspace_size.argtypes = [I64, I64, I64, I64, I64, I64, I]
+    lib.mamba_block_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_block_fwd.argtypes = [I64] * 6 + [I] + [P] * 8 + [I, P, P, P, P, ctypes.c_size_t, P]
+    lib.mamba_block_fwd.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -380,4 +384,42 @@ def mamba_ssm_fwd(x, W_x, W_dt, A, z=None, dt_bias=None, Dskip=None, delta_softp
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
     if st != 0:
         raise MambaError("mamba_ssm_fwd", st)
+    return out, last_state
+
+
+def mamba_block_fwd_workspace_size(batch, seqlen, d_model, dim, dstate, dt_rank, io_dtype) -> int:
+    return int(load_library().mamba_block_fwd_workspace_size(batch, seqlen, d_model, dim, dstate, dt_rank, io_dtype))
+
+
+def mamba_block_fwd(hidden, W_in, W_x, W_dt, A, W_out, dt_bias=None, Dskip=None, delta_softplus=True, h0=None,
+                    out=None, last_state=None, workspace=None, return_last_state=True):
+    """One Mamba block: hidden (batch, L, d_model); W_in (2 D, d_model); W_out (d_model, D);
+    W_x, W_dt, A, dt_bias, Dskip as for mamba_ssm_fwd.  Returns (out (batch, L, d_model), last_state)."""
+    import torch
+
+    lib = load_library()
+    batch, L, dm = hidden.shape
+    D = W_out.shape[1]
+    N = A.shape[1]
+    R = W_dt.shape[1]
+    io = _io_dtype(hidden)
+    dev = hidden.device
+    f32 = torch.float32
+    t = hidden.dtype
+    out = torch.empty_like(hidden) if out is None else out
+    if last_state is None and return_last_state:
+        last_state = torch.empty((batch, D, N), dtype=f32, device=dev)
+    ws_bytes = mamba_block_fwd_workspace_size(batch, L, dm, D, N, R, io)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.mamba_block_fwd(
+        batch, L, dm, D, N, R, io, _ptr(hidden, "hidden", t, (batch, L, dm), dev),
+        _ptr(W_in, "W_in", t, (2 * D, dm), dev), _ptr(W_x, "W_x", t, (R + 2 * N, D), dev),
+        _ptr(W_dt, "W_dt", t, (D, R), dev), _ptr(dt_bias, "dt_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(W_out, "W_out", t, (dm, D), dev), int(bool(delta_softplus)),
+        _ptr(h0, "h0", f32, (batch, D, N), dev), _ptr(out, "out", t, (batch, L, dm), dev),
+        _ptr(last_state, "last_state", f32, (batch, D, N), dev), _ptr(workspace, "workspace", device=dev),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_block_fwd", st)
     return out, last_state

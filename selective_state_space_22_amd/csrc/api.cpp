@@ -465,4 +465,71 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
   return MAMBA_OK;
 }
 
+size_t mamba_block_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim, int64_t dstate,
+                                      int64_t dt_rank, int io_dtype) {
+  if (check_shape("mamba_block_fwd_workspace_size", batch, seqlen, dim, dstate, io_dtype) != MAMBA_OK) return 0;
+  if (d_model < 1 || d_model > kMaxDim || dt_rank < 1 || dt_rank > kMaxDim) return 0;
+  const size_t e = io_dtype == MAMBA_IO_BF16 ? 2 : 4;
+  const size_t tok = (size_t)batch * seqlen;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return 3 * al(tok * dim * e) + mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype);
+}
+
+int mamba_block_fwd(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim, int64_t dstate, int64_t dt_rank,
+                    int io_dtype, const void* hidden, const void* W_in, const void* W_x, const void* W_dt,
+                    const float* dt_bias, const float* A, const float* Dskip, const void* W_out, int delta_softplus,
+                    const float* h0, void* out, float* last_state, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const char* where = "mamba_block_fwd";
+  int st = check_shape(where, batch, seqlen, dim, dstate, io_dtype);
+  if (st != MAMBA_OK) return st;
+  if (d_model < 1 || d_model > kMaxDim) return fail(MAMBA_ERR_DIM, where, "d_model");
+  if (dt_rank < 1 || dt_rank > kMaxDim) return fail(MAMBA_ERR_DIM, where, "dt_rank");
+  const bool tokens = batch > 0 && seqlen > 0 && dim > 0;
+  PtrCheck pc{where};
+  pc.req(hidden, tokens, "hidden");
+  pc.req(W_in, tokens, "W_in");
+  pc.req(W_x, tokens, "W_x");
+  pc.req(W_dt, tokens, "W_dt");
+  pc.req(A, tokens, "A");
+  pc.req(W_out, tokens, "W_out");
+  pc.req(out, tokens, "out");
+  pc.opt(dt_bias, "dt_bias");
+  pc.opt(Dskip, "Dskip");
+  pc.opt(h0, "h0");
+  pc.opt(last_state, "last_state");
+  pc.opt(workspace, "workspace");
+  if (pc.status != MAMBA_OK) return pc.status;
+  if (batch == 0 || dim == 0) return MAMBA_OK;
+  const size_t need = mamba_block_fwd_workspace_size(batch, seqlen, d_model, dim, dstate, dt_rank, io_dtype);
+  if (tokens && (!workspace || workspace_bytes < need)) return fail(MAMBA_ERR_WORKSPACE, where, "workspace");
+  const size_t e = io_dtype == MAMBA_IO_BF16 ? 2 : 4;
+  const int64_t M = batch * seqlen;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  void* x = tokens ? w : nullptr;
+  void* z = tokens ? w + al((size_t)M * dim * e) : nullptr;
+  void* y = tokens ? w + 2 * al((size_t)M * dim * e) : nullptr;
+  void* ssm_ws = tokens ? w + 3 * al((size_t)M * dim * e) : nullptr;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t he = hipSuccess;
+  if (tokens) {
+    // input projection: SSM branch (first dim rows of W_in) through SiLU, gate branch plain
+    he = s6::launch_gemm_nt(hidden, W_in, x, M, dim, d_model, d_model, d_model, dim, io_dtype, 1, hs);
+    if (he == hipSuccess)
+      he = s6::launch_gemm_nt(hidden, static_cast<const uint8_t*>(W_in) + (size_t)dim * d_model * e, z, M, dim,
+                              d_model, d_model, d_model, dim, io_dtype, 0, hs);
+    if (he != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(he));
+  }
+  st = mamba_ssm_fwd(batch, seqlen, dim, dstate, dt_rank, io_dtype, x, z, W_x, W_dt, dt_bias, A, Dskip,
+                     delta_softplus, h0, y, last_state, ssm_ws,
+                     tokens ? workspace_bytes - 3 * al((size_t)M * dim * e) : 0, stream);
+  if (st != MAMBA_OK) return st;
+  if (tokens) {
+    he = s6::launch_gemm_nt(y, W_out, out, M, d_model, dim, dim, dim, d_model, io_dtype, 0, hs);
+    if (he != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(he));
+  }
+  return MAMBA_OK;
+}
+
 }  // extern "C"

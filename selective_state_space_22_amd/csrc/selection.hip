@@ -83,6 +83,7 @@ struct GemmArgs {
   int64_t split_stride = 0;  // split K (parts > 1): part z covers stages [z*sps, (z+1)*sps), output at C + z*split_stride
   int32_t sps = 0;
   int32_t parts = 1;
+  int32_t act = 0;  // 1: SiLU of every output element (applied in fp32 before rounding)
 };
 
 // 128 x 128 output block per workgroup of 2 x 2 waves (4 x 4 tiles of 16 x 16
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_mfma_kernel(GemmArgs g) {
       const int64_t gcol = n0 + c0;
       float v[EPV];
 #pragma unroll
-      for (int kk = 0; kk < EPV; ++kk) v[kk] = st[row][c0 + kk];
+      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][c0 + kk]) : st[row][c0 + kk];
       if (vec_ok && gcol + EPV <= g.N) {
         const uint32_t off = (uint32_t)((grow * g.ldc + gcol) * sizeof(OUT));
         u32x4 pk;
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
       const int64_t gcol = n0 + cc;
       float v[EPV];
 #pragma unroll
-      for (int kk = 0; kk < EPV; ++kk) v[kk] = st[row][cc + kk];
+      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][cc + kk]) : st[row][cc + kk];
       if (vec_ok && gcol + EPV <= g.N) {
         const uint32_t off = (uint32_t)((row * g.ldc + gcol) * sizeof(OUT));
         u32x4 pk;
@@ -403,7 +404,7 @@ __global__ void gemm_nt_valu_kernel(GemmArgs g) {
   const IN* b = static_cast<const IN*>(g.B) + n * g.ldb;
   float acc = 0.0f;
   for (int64_t k = 0; k < g.K; ++k) acc = __builtin_fmaf(load_io(a, k), load_io(b, k), acc);
-  store_io(static_cast<OUT*>(g.C), (size_t)(m * g.ldc + n), acc);
+  store_io(static_cast<OUT*>(g.C), (size_t)(m * g.ldc + n), g.act ? silu(acc) : acc);
 }
 
 // Sum of the split-K parts of x W_x^T, rounded once to the I/O type: the
@@ -537,8 +538,9 @@ hipError_t launch_selection(const SelArgs& s, int io, hipStream_t st) {
 }
 
 hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                          int64_t ldb, int64_t ldc, int io, hipStream_t st) {
+                          int64_t ldb, int64_t ldc, int io, int act, hipStream_t st) {
   GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc};
+  g.act = act;
   return io == kIoBF16 ? gemm_nt<uint16_t, uint16_t>(g, st) : gemm_nt<float, float>(g, st);
 }
 

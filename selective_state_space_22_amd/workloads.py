@@ -276,6 +276,36 @@ def selection_weights(dim: int, dstate: int, dt_rank: int, io: str = "f32", seed
     return SelectionWeights(W_x, W_dt)
 
 
+@dataclasses.dataclass
+class BlockWeights:
+    W_in: np.ndarray   # (2 D, d_model)
+    W_out: np.ndarray  # (d_model, D)
+
+
+def block_weights(d_model: int, dim: int, io: str = "f32", seed: int = SEED_BASE) -> BlockWeights:
+    """Random-init block projections in the usual linear-layer ranges:
+    W_in ~ U(-1/sqrt(d_model), 1/sqrt(d_model)), W_out ~ U(-1/sqrt(D), 1/sqrt(D))
+    (own streams of SeedSequence(seed + 800000)); bf16 rounds once (RNE)."""
+    seqs = np.random.SeedSequence(seed + 800_000).spawn(2)
+    bi = 1.0 / math.sqrt(d_model)
+    bo = 1.0 / math.sqrt(dim)
+    W_in = _fill(seqs[0], (2 * dim, d_model), "uniform", -bi, bi)
+    W_out = _fill(seqs[1], (d_model, dim), "uniform", -bo, bo)
+    if io == "bf16":
+        W_in = bf16_round(W_in)[1].reshape(W_in.shape)
+        W_out = bf16_round(W_out)[1].reshape(W_out.shape)
+    return BlockWeights(W_in, W_out)
+
+
+def block_hidden(batch: int, seqlen: int, d_model: int, io: str = "f32", seed: int = SEED_BASE) -> np.ndarray:
+    """Block input (batch, L, d_model) ~ N(0, 1) from its own stream (SeedSequence(seed + 900000)),
+    bf16-rounded once for bf16 I/O."""
+    h = _fill(np.random.SeedSequence(seed + 900_000), (batch, seqlen, d_model), "normal")
+    if io == "bf16":
+        h = bf16_round(h)[1].reshape(h.shape)
+    return h
+
+
 def generate_workload(name: str) -> ScanInputs:
     """The seeded inputs of a named workload (decode: the 64 tokens as one (B, 64, D) block)."""
     w = WORKLOADS[name]

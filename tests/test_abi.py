@@ -31,7 +31,7 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
+    assert declared_functions() == ["mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
                                     "mamba_scan_fwd_complex", "mamba_scan_fwd_complex_workspace_size",
                                     "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
                                     "mamba_selection_fwd_workspace_size", "mamba_ssm_fwd",
@@ -253,3 +253,25 @@ def test_complex_state_update_validation(lib):
         assert call(**{field: None}) == ERR_NULL, field
         assert call(**{field: FAKE + 4}) == ERR_ALIGN, field
     assert call(batch=0, state=None, u=None, A=None, out=None) == OK
+
+
+def test_block_validation_and_workspace(lib):
+    ws = binding.mamba_block_fwd_workspace_size
+    # x, z and y of the block ahead of the selective SSM's workspace
+    tok, D = 4 * 4096, 5120
+    need = ws(4, 4096, 2560, D, 16, 160, 1)
+    assert need >= 3 * tok * D * 2 + binding.mamba_ssm_fwd_workspace_size(4, 4096, D, 16, 160, 1)
+    assert ws(1, 8, 0, 64, 16, 4, 0) == 0 and ws(1, 8, 32, 64, 16, 0, 0) == 0 and ws(1, 8, 32, 64, 5, 4, 0) == 0
+
+    def call(d_model=32, R=4, N=16, io=0, hidden=FAKE, W_in=FAKE, W_out=FAKE, out=FAKE, ws_ptr=None, ws_bytes=0):
+        return lib.mamba_block_fwd(1, 8, d_model, 64, N, R, io, hidden, W_in, FAKE, FAKE, None, FAKE, None, W_out, 1,
+                                   None, out, None, ws_ptr, ws_bytes, None)
+
+    assert call(io=2) == ERR_DTYPE
+    assert call(N=3) == ERR_UNSUPPORTED
+    assert call(d_model=0) == ERR_DIM and call(R=0) == ERR_DIM
+    for field in ("hidden", "W_in", "W_out", "out"):
+        assert call(**{field: None}) == ERR_NULL, field
+        assert call(**{field: FAKE + 2}) == ERR_ALIGN, field
+    assert call() == ERR_WORKSPACE
+    assert call(ws_ptr=FAKE, ws_bytes=ws(1, 8, 32, 64, 16, 4, 0) - 1) == ERR_WORKSPACE
