@@ -394,6 +394,197 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
   }
 }
 
+// Large products (the block's input and output projections): 256 x 256 output
+// blocks, each of the 4 waves owning 128 x 128 (8 x 8 tiles of 16 x 16; the
+// accumulators live in AGPRs, one wave per SIMD).  A wave then reads 16 KB of
+// operands from LDS per 64-byte K slice for 64 MFMAs, half the LDS traffic per
+// product of the 64 x 64 wave tiles above, which leaves the matrix cores rather
+// than LDS bandwidth as the limit.  Operands go from global memory straight
+// into a ring of four LDS stages (buffer loads with the lds bit: lane i of a
+// load writes the 16 bytes at 16 i of its 1 KB destination), three stages in
+// flight while one is multiplied; a stage holds 64 bytes of K for 256 rows of
+// A and of B, the 16-byte chunk c of row r at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3),
+// so that any 8 (and any 16) consecutive rows an MFMA operand read touches fall on
+// distinct 16-byte bank groups of a 128-byte (and of a 256-byte) bank row.
+constexpr int kBigBM = 256;
+constexpr int kBigStage = 64;  // K bytes per row per stage
+constexpr int kBigBufs = 4;
+
+__device__ __forceinline__ uint32_t big_swz(uint32_t row) { return ((row >> 1) ^ (row >> 3)) & 3u; }
+__device__ __forceinline__ uint32_t big_off(uint32_t row, uint32_t chunk) {
+  return row * kBigStage + 16u * (chunk ^ big_swz(row));
+}
+
+// s_waitcnt with vmcnt = n and lgkmcnt = 0 (expcnt not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0070);
+}
+
+template <typename IN, typename OUT>
+__global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmArgs g) {
+  constexpr int TM = 8, TN = 8;
+  constexpr uint32_t E = sizeof(IN);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int r16 = lane & 15, q = lane >> 4;
+  // Block order.  Workgroup ids go to the 8 XCDs in turn (id mod 8), so XCD x
+  // gets a contiguous range of output blocks t = x * per_xcd + id / 8.  Within the
+  // range, blocks are grouped 8 row blocks high: the 32 workgroups an XCD runs at
+  // once cover about 8 row blocks x 4 column blocks, whose A and B stages they
+  // share through that XCD's L2.
+  const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
+  const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
+  const int64_t per_xcd = (nbm * nbn + 7) / 8;
+  const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= nbm * nbn) return;
+  constexpr int64_t kGroup = 8;
+  const int64_t grp = t / (kGroup * nbn);
+  const int64_t rows_in_grp = nbm - grp * kGroup < kGroup ? nbm - grp * kGroup : kGroup;
+  const int64_t in_grp = t - grp * kGroup * nbn;
+  const int64_t bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
+  const int64_t bn0 = (in_grp / rows_in_grp) * kBigBM;
+  const int64_t mrows = g.M - bm0 < kBigBM ? g.M - bm0 : kBigBM;
+  const int64_t nrows = g.N - bn0 < kBigBM ? g.N - bn0 : kBigBM;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda,
+                                              (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb,
+                                              (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBigBufs][2][kBigBM * kBigStage];
+
+  const uint32_t kbytes = (uint32_t)(g.K * E);
+  const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);
+  // DMA share of this wave: rows 64 w .. 64 w + 63 of A and of B, four 16-row loads each.
+  // Lane i of a load lands at row base + i / 4, physical chunk i % 4, so it fetches
+  // the logical chunk (i % 4) ^ big_swz(row).
+  const uint32_t lrow = (uint32_t)(lane >> 2);
+  const uint32_t ldaE = (uint32_t)(g.lda * E), ldbE = (uint32_t)(g.ldb * E);
+  auto dma = [&](int s) {
+    if (s >= nst) return;
+    const int buf = s & (kBigBufs - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = (uint32_t)(64 * w + 16 * j) + lrow;
+      const uint32_t kb = (uint32_t)s * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
+      // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
+      const uint32_t kcut = kb < kbytes ? 0u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(64 * w + 16 * j) * kBigStage], 16,
+                                               (row * ldaE + kb) | kcut, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(64 * w + 16 * j) * kBigStage], 16,
+                                               (row * ldbE + kb) | kcut, 0, 0, 0);
+    }
+  };
+  // A barrier without a memory fence: a fence here would make every wave wait for
+  // all of its loads in flight (they write LDS); instead each wave waits for its
+  // loads of the stage it is about to read (vmcnt) before the barrier.  The signal
+  // fences keep the compiler from moving LDS accesses across it.
+  auto stage_barrier = [] {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Stage s is complete once this wave's loads of it have landed (the loads of
+  // the up to two later stages already issued may still be in flight: 8 per
+  // stage) and every wave has passed the barrier; the lgkmcnt wait before it
+  // makes sure this wave's operand reads of the previous stage, whose buffer the
+  // loads of stage s + 3 overwrite, have returned.
+  auto sync_for = [&](int s) {
+    const int later = (s + 2 < nst - 1 ? s + 2 : nst - 1) - s;
+    if (later >= 2) wait_vm_lgkm0<16>();
+    else if (later == 1) wait_vm_lgkm0<8>();
+    else wait_vm_lgkm0<0>();
+    stage_barrier();
+    dma(s + 3);
+  };
+  auto read = [&](int s, u32x4 (&a)[TM], u32x4 (&b)[TN]) {
+    const int buf = s & (kBigBufs - 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      a[i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][big_off(wm * 128 + 16 * i + r16, q)]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(&lds[buf][1][big_off(wn * 128 + 16 * j + r16, q)]);
+  };
+  auto mma = [&](const u32x4 (&a)[TM], const u32x4 (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<IN>::step(a[i], b[j], acc[i][j]);
+  };
+
+  u32x4 a[TM], b[TN];
+  dma(0);
+  dma(1);
+  dma(2);
+  for (int k = 0; k < nst; ++k) {
+    sync_for(k);
+    read(k, a, b);
+    // all 16 operand reads in flight before the first MFMA waits on them
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a, b);
+  }
+  __syncthreads();  // the stage buffers become the output staging area
+
+  // Output: 16-row strips of the wave's 128 x 128 tile through LDS (fp32), then
+  // 16-byte row segments; rows and columns past the edges are dropped.
+  OUT* cbase = static_cast<OUT*>(g.C);
+  const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 128;
+  const int64_t wrows = g.M - m0 < 128 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 128;
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(cbase + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
+  const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15u) == 0;
+  float(*st)[132] = reinterpret_cast<float(*)[132]>(&lds[0][0][0] + w * 16 * 132 * 4);
+  constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
+  constexpr int LPR = 128 / EPV;         // lanes per row
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[4 * q + r][16 * j + r16] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave execute in order
+#pragma unroll
+    for (int e0 = 0; e0 < 16 * LPR; e0 += 64) {
+      const int e = e0 + lane;
+      const int row = e / LPR, c0 = (e % LPR) * EPV;
+      const int64_t grow = 16 * i + row;  // relative to m0
+      const int64_t gcol = n0 + c0;
+      float v[EPV];
+#pragma unroll
+      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][c0 + kk]) : st[row][c0 + kk];
+      if (vec_ok && gcol + EPV <= g.N) {
+        const uint32_t off = (uint32_t)((grow * g.ldc + gcol) * sizeof(OUT));
+        u32x4 pk;
+        if constexpr (sizeof(OUT) == 2) {
+          pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+          pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        } else {
+          pk = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(pk, rc, grow < wrows ? off : kOutOfRange, 0, 0);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < EPV; ++kk) {
+          const uint32_t off =
+              gcol + kk < g.N ? (uint32_t)((grow * g.ldc + gcol + kk) * sizeof(OUT)) : kOutOfRange;
+          store_elem<OUT>(rc, grow < wrows ? off : kOutOfRange, v[kk]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Any alignment: one thread per output element, K FMAs.
 template <typename IN, typename OUT>
 __global__ void gemm_nt_valu_kernel(GemmArgs g) {
@@ -470,9 +661,26 @@ hipError_t gemm_nt_short(const GemmArgs& g, int ks, hipStream_t st) {
   }
 }
 
+// The large-block kernel pays off once both output dimensions fill several of
+// its 256 x 256 blocks and K spans a few stages.
+template <typename IN>
+bool big_ok(const GemmArgs& g) {
+  const int64_t e = sizeof(IN);
+  // row offsets inside a 256-row block must stay below the out-of-range bit
+  const bool offsets = 256 * g.lda * e + g.K * e < (int64_t)kOutOfRange && 256 * g.ldb * e + g.K * e < (int64_t)kOutOfRange;
+  return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr;
+}
+
 template <typename IN, typename OUT>
 hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (mfma_ok<IN>(g) && parts == 1 && big_ok<IN>(g)) {
+    const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
+    const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
+    const int64_t blocks = (nbm * nbn + 7) / 8 * 8;  // 8 equal XCD ranges (ids past the last block exit)
+    hipLaunchKernelGGL((gemm_nt_big_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
   if (mfma_ok<IN>(g) && parts == 1 && ks <= kShortMaxSlices && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr)
     return gemm_nt_short<IN, OUT>(g, ks, st);

@@ -49,6 +49,8 @@ def _gpu_block(inp, sw, bw, hidden, io):
     (1, 64, 40, 72, 4, 5, "bf16"),      # rows not 16-byte aligned: vector GEMM paths
     (1, 129, 768, 1536, 16, 48, "bf16"),  # Mamba-130M block widths
     (2, 200, 96, 192, 8, 12, "f32"),
+    (2, 600, 520, 1040, 16, 66, "bf16"),  # large-block GEMM kernel: ragged rows, columns and K
+    (2, 600, 520, 1040, 8, 66, "f32"),
 ], ids=str)
 def test_block_matches_oracle(case):
     _need_gpu()
