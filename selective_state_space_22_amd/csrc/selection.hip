@@ -395,20 +395,23 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
 }
 
 // Large products (the block's input and output projections): 256 x 256 output
-// blocks, each of the 4 waves owning 128 x 128 (8 x 8 tiles of 16 x 16; the
-// accumulators live in AGPRs, one wave per SIMD).  A wave then reads 16 KB of
-// operands from LDS per 64-byte K slice for 64 MFMAs, half the LDS traffic per
-// product of the 64 x 64 wave tiles above, which leaves the matrix cores rather
-// than LDS bandwidth as the limit.  Operands go from global memory straight
-// into a ring of four LDS stages (buffer loads with the lds bit: lane i of a
-// load writes the 16 bytes at 16 i of its 1 KB destination), three stages in
-// flight while one is multiplied; a stage holds 64 bytes of K for 256 rows of
-// A and of B, the 16-byte chunk c of row r at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3),
-// so that any 8 (and any 16) consecutive rows an MFMA operand read touches fall on
-// distinct 16-byte bank groups of a 128-byte (and of a 256-byte) bank row.
+// blocks of 8 waves, two per SIMD (one wave per SIMD cannot issue MFMAs fast enough
+// to keep its matrix core busy), each wave owning 128 x 64 (8 x 4 tiles of 16 x 16,
+// accumulators in AGPRs).  Operands go from global memory straight into a ring of
+// five LDS stages of 32 KB, the whole 160 KB of a CU (buffer loads with the lds bit:
+// lane i of a load writes the 16 bytes at 16 i of its 1 KB destination).  While
+// stage k is multiplied, the operands of stage k + 1 are read from LDS between its
+// MFMAs and stages k + 2 .. k + 5 are in flight: four stages, 128 KB per CU, to
+// cover the latency of the loads that miss L2 (every stage has some, its first
+// touches of the A and B rows), since each stage waits for all of its loads.  A
+// stage holds 64 bytes of K for 256 rows of A and of B, the 16-byte chunk c of row
+// r at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3), so that any 8 (and any 16) consecutive
+// rows an MFMA operand read touches fall on distinct 16-byte bank groups of a
+// 128-byte (and of a 256-byte) bank row.
 constexpr int kBigBM = 256;
 constexpr int kBigStage = 64;  // K bytes per row per stage
-constexpr int kBigBufs = 4;
+constexpr int kBigBufs = 5;
+constexpr int kBigThreads = 512;
 
 __device__ __forceinline__ uint32_t big_swz(uint32_t row) { return ((row >> 1) ^ (row >> 3)) & 3u; }
 __device__ __forceinline__ uint32_t big_off(uint32_t row, uint32_t chunk) {
@@ -422,12 +425,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 }
 
 template <typename IN, typename OUT>
-__global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmArgs g) {
-  constexpr int TM = 8, TN = 8;
+__global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
+  constexpr int TM = 8, TN = 4;  // 16 x 16 tiles of a wave: 128 rows x 64 columns
   constexpr uint32_t E = sizeof(IN);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   const int r16 = lane & 15, q = lane >> 4;
   // Block order.  Workgroup ids go to the 8 XCDs in turn (id mod 8), so XCD x
   // gets a contiguous range of output blocks t = x * per_xcd + id / 8.  Within the
@@ -455,23 +458,24 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmArgs g) {
 
   const uint32_t kbytes = (uint32_t)(g.K * E);
   const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);
-  // DMA share of this wave: rows 64 w .. 64 w + 63 of A and of B, four 16-row loads each.
-  // Lane i of a load lands at row base + i / 4, physical chunk i % 4, so it fetches
-  // the logical chunk (i % 4) ^ big_swz(row).
+  // DMA share of this wave: rows 32 w .. 32 w + 31 of A and of B, two 16-row loads
+  // each.  Lane i of a load lands at row base + i / 4, physical chunk i % 4, so it
+  // fetches the logical chunk (i % 4) ^ big_swz(row).  Stages past the last are still
+  // issued, as loads past every row (read as zero): every stage then has 4 loads per
+  // wave in flight, whatever the position in K.
   const uint32_t lrow = (uint32_t)(lane >> 2);
   const uint32_t ldaE = (uint32_t)(g.lda * E), ldbE = (uint32_t)(g.ldb * E);
-  auto dma = [&](int s) {
-    if (s >= nst) return;
-    const int buf = s & (kBigBufs - 1);
+  auto dma = [&](int s, int buf) {
+    const uint32_t scut = s < nst ? 0u : kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t row = (uint32_t)(64 * w + 16 * j) + lrow;
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = (uint32_t)(32 * w + 16 * j) + lrow;
       const uint32_t kb = (uint32_t)s * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
       // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
-      const uint32_t kcut = kb < kbytes ? 0u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(64 * w + 16 * j) * kBigStage], 16,
+      const uint32_t kcut = kb < kbytes ? scut : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(32 * w + 16 * j) * kBigStage], 16,
                                                (row * ldaE + kb) | kcut, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(64 * w + 16 * j) * kBigStage], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(32 * w + 16 * j) * kBigStage], 16,
                                                (row * ldbE + kb) | kcut, 0, 0, 0);
     }
   };
@@ -484,6 +488,23 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
+  auto read_a = [&](int buf, int i) {
+    return *reinterpret_cast<const u32x4*>(&lds[buf][0][big_off(wm * 128 + 16 * i + r16, q)]);
+  };
+  auto read_b = [&](int buf, int j) {
+    return *reinterpret_cast<const u32x4*>(&lds[buf][1][big_off(wn * 64 + 16 * j + r16, q)]);
+  };
+  // acc += a b^T on one 16 x 16 tile.  For bf16 the MFMA is written out so that its
+  // accumulator is tied to its result register: the compiler's own form may put the
+  // result in another AGPR quad, which across the K loop turns into a rotation of the
+  // accumulators through VGPRs at every stage.  The "memory" clobber keeps the LDS
+  // reads where they are written, between the MFMAs.
+  auto mma = [](f32x4& c, const u32x4& a, const u32x4& b) {
+    if constexpr (sizeof(IN) == 2)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+    else
+      c = Mfma<IN>::step(a, b, c);
+  };
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -491,59 +512,71 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_big_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Stage s is complete once this wave's loads of it have landed (the loads of
-  // the up to two later stages already issued may still be in flight: 8 per
-  // stage) and every wave has passed the barrier; the lgkmcnt wait before it
-  // makes sure this wave's operand reads of the previous stage, whose buffer the
-  // loads of stage s + 3 overwrite, have returned.
-  auto sync_for = [&](int s) {
-    const int later = (s + 2 < nst - 1 ? s + 2 : nst - 1) - s;
-    if (later >= 2) wait_vm_lgkm0<16>();
-    else if (later == 1) wait_vm_lgkm0<8>();
-    else wait_vm_lgkm0<0>();
+  // Stage k (operands a, b in registers, read during stage k - 1, those reads done):
+  // once this wave's loads of stage k + 1 have landed (those of k + 2 .. k + 4 may
+  // be in flight, 4 each) and every wave has passed the barrier, stage k + 1 is
+  // readable and the buffer of stage k is free, so the loads of stage k + 5 go there.
+  // Rows 0..5 of the tiles read, once a[i] is spent, the fragment i of A for stage
+  // k + 1 into a[i] itself; rows 0..3 read the fragment i of B into nb[i] after their
+  // first MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The last read is two
+  // rows before the end, so the wait for all of them before the next barrier is short.
+  int rbuf = 1, dbuf = 0;  // buffers of stages k + 1 and k + 5
+  auto step = [&](int k, u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
+    wait_vm_lgkm0<12>();
     stage_barrier();
-    dma(s + 3);
-  };
-  auto read = [&](int s, u32x4 (&a)[TM], u32x4 (&b)[TN]) {
-    const int buf = s & (kBigBufs - 1);
+    dma(k + 5, dbuf);
+    u32x4 na[2];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      a[i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][big_off(wm * 128 + 16 * i + r16, q)]);
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(&lds[buf][1][big_off(wn * 128 + 16 * j + r16, q)]);
-  };
-  auto mma = [&](const u32x4 (&a)[TM], const u32x4 (&b)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<IN>::step(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) {
+        mma(acc[i][j], a[i], b[j]);
+        if (j == 0 && i < TN) nb[i] = read_b(rbuf, i);
+        if (j == 0 && (i == 4 || i == 5)) na[i - 4] = read_a(rbuf, i + 2);
+      }
+      if (i < 6) a[i] = read_a(rbuf, i);
+    }
+    a[6] = na[0];
+    a[7] = na[1];
+    rbuf = rbuf == kBigBufs - 1 ? 0 : rbuf + 1;
+    dbuf = dbuf == kBigBufs - 1 ? 0 : dbuf + 1;
   };
 
-  u32x4 a[TM], b[TN];
-  dma(0);
-  dma(1);
-  dma(2);
-  for (int k = 0; k < nst; ++k) {
-    sync_for(k);
-    read(k, a, b);
-    // all 16 operand reads in flight before the first MFMA waits on them
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a, b);
+  u32x4 a[TM], b0[TN], b1[TN];
+  dma(0, 0);
+  dma(1, 1);
+  dma(2, 2);
+  dma(3, 3);
+  dma(4, 4);
+  wait_vm_lgkm0<16>();
+  stage_barrier();
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a[i] = read_a(0, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b0[j] = read_b(0, j);
+  // Stages in pairs; an odd count gets one more, all zeros (its loads are past K).
+  for (int k = 0; k < nst; k += 2) {
+    step(k, a, b0, b1);
+    step(k + 1, a, b1, b0);
   }
-  __syncthreads();  // the stage buffers become the output staging area
+  // Every load in flight (the zero stages past the end) lands before the buffers
+  // become the output staging area, and the last MFMAs finish before their
+  // accumulators are read.
+  wait_vm_lgkm0<0>();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __syncthreads();
 
-  // Output: 16-row strips of the wave's 128 x 128 tile through LDS (fp32), then
+  // Output: 16-row strips of the wave's 128 x 64 tile through LDS (fp32), then
   // 16-byte row segments; rows and columns past the edges are dropped.
   OUT* cbase = static_cast<OUT*>(g.C);
-  const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 128;
+  const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 64;
   const int64_t wrows = g.M - m0 < 128 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 128;
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(cbase + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
   const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15u) == 0;
-  float(*st)[132] = reinterpret_cast<float(*)[132]>(&lds[0][0][0] + w * 16 * 132 * 4);
+  float(*st)[68] = reinterpret_cast<float(*)[68]>(&lds[0][0][0] + w * 16 * 68 * 4);
   constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
-  constexpr int LPR = 128 / EPV;         // lanes per row
+  constexpr int LPR = 64 / EPV;          // lanes per row
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -678,7 +711,7 @@ hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
     const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
     const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
     const int64_t blocks = (nbm * nbn + 7) / 8 * 8;  // 8 equal XCD ranges (ids past the last block exit)
-    hipLaunchKernelGGL((gemm_nt_big_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st, g);
+    hipLaunchKernelGGL((gemm_nt_big_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(kBigThreads), 0, st, g);
     return hipGetLastError();
   }
   const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
