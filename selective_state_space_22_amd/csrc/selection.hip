@@ -465,19 +465,24 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   // wave in flight, whatever the position in K.
   const uint32_t lrow = (uint32_t)(lane >> 2);
   const uint32_t ldaE = (uint32_t)(g.lda * E), ldbE = (uint32_t)(g.ldb * E);
-  auto dma = [&](int s, int buf) {
+  // Load n (0..3) of this wave for stage s: rows 32 w + 16 (n >> 1) + (0..15) of A
+  // (n even) or of B (n odd).
+  auto dma_one = [&](int s, int buf, int n) {
     const uint32_t scut = s < nst ? 0u : kOutOfRange;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = (uint32_t)(32 * w + 16 * j) + lrow;
-      const uint32_t kb = (uint32_t)s * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
-      // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
-      const uint32_t kcut = kb < kbytes ? scut : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(32 * w + 16 * j) * kBigStage], 16,
-                                               (row * ldaE + kb) | kcut, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(32 * w + 16 * j) * kBigStage], 16,
+    const uint32_t row = (uint32_t)(32 * w + 16 * (n >> 1)) + lrow;
+    const uint32_t kb = (uint32_t)s * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
+    // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
+    const uint32_t kcut = kb < kbytes ? scut : kOutOfRange;
+    if (n & 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(32 * w + 16 * (n >> 1)) * kBigStage], 16,
                                                (row * ldbE + kb) | kcut, 0, 0, 0);
-    }
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(32 * w + 16 * (n >> 1)) * kBigStage], 16,
+                                               (row * ldaE + kb) | kcut, 0, 0, 0);
+  };
+  auto dma = [&](int s, int buf) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) dma_one(s, buf, n);
   };
   // A barrier without a memory fence: a fence here would make every wave wait for
   // all of its loads in flight (they write LDS); instead each wave waits for its
@@ -515,7 +520,8 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   // Stage k (operands a, b in registers, read during stage k - 1, those reads done):
   // once this wave's loads of stage k + 1 have landed (those of k + 2 .. k + 4 may
   // be in flight, 4 each) and every wave has passed the barrier, stage k + 1 is
-  // readable and the buffer of stage k is free, so the loads of stage k + 5 go there.
+  // readable and the buffer of stage k is free, so the loads of stage k + 5 go there,
+  // spread over the MFMAs.
   // Rows 0..5 of the tiles read, once a[i] is spent, the fragment i of A for stage
   // k + 1 into a[i] itself; rows 0..3 read the fragment i of B into nb[i] after their
   // first MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The last read is two
@@ -524,7 +530,6 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   auto step = [&](int k, u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
     wait_vm_lgkm0<12>();
     stage_barrier();
-    dma(k + 5, dbuf);
     u32x4 na[2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -533,6 +538,9 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
         mma(acc[i][j], a[i], b[j]);
         if (j == 0 && i < TN) nb[i] = read_b(rbuf, i);
         if (j == 0 && (i == 4 || i == 5)) na[i - 4] = read_a(rbuf, i + 2);
+        // the loads of stage k + 5, one per 8 MFMAs: issued together, the 32 loads
+        // of a workgroup queue up behind each other and hold back the MFMAs after them
+        if (j == 2 && (i & 1) == 0) dma_one(k + 5, dbuf, i >> 1);
       }
       if (i < 6) a[i] = read_a(rbuf, i);
     }
