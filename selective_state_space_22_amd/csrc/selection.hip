@@ -405,15 +405,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
 // cover the latency of the loads that miss L2 (every stage has some, its first
 // touches of the A and B rows), since each stage waits for all of its loads.  A
 // stage holds 64 bytes of K for 256 rows of A and of B, the 16-byte chunk c of row
-// r at chunk c ^ (((r >> 1) ^ (r >> 3)) & 3), so that any 8 (and any 16) consecutive
-// rows an MFMA operand read touches fall on distinct 16-byte bank groups of a
-// 128-byte (and of a 256-byte) bank row.
+// r at chunk c ^ ((r >> 1) & 3): an MFMA operand read (lane l: row l % 16, chunk
+// l / 16) then takes the 16 rows x 64 bytes of a fragment at the rate of a plain
+// 1 KB read, while without the swizzle, or with rows 8 apart also told apart, it
+// runs 25-40% slower (LDS serves the lanes of a 16-byte read in groups of 8).
 constexpr int kBigBM = 256;
 constexpr int kBigStage = 64;  // K bytes per row per stage
 constexpr int kBigBufs = 5;
 constexpr int kBigThreads = 512;
 
-__device__ __forceinline__ uint32_t big_swz(uint32_t row) { return ((row >> 1) ^ (row >> 3)) & 3u; }
+__device__ __forceinline__ uint32_t big_swz(uint32_t row) { return (row >> 1) & 3u; }
 __device__ __forceinline__ uint32_t big_off(uint32_t row, uint32_t chunk) {
   return row * kBigStage + 16u * (chunk ^ big_swz(row));
 }
