@@ -32,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int32_t kBufferDword3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -413,6 +414,7 @@ constexpr int kBigBM = 256;
 constexpr int kBigStage = 64;  // K bytes per row per stage
 constexpr int kBigBufs = 5;
 constexpr int kBigThreads = 512;
+constexpr int64_t kBigCus = 256;  // compute units of an MI355X: the kernel's grid
 
 __device__ __forceinline__ uint32_t big_swz(uint32_t row) { return (row >> 1) & 3u; }
 __device__ __forceinline__ uint32_t big_off(uint32_t row, uint32_t chunk) {
@@ -433,45 +435,63 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 2, wn = w & 3;
   const int r16 = lane & 15, q = lane >> 4;
-  // Block order.  Workgroup ids go to the 8 XCDs in turn (id mod 8), so XCD x
-  // gets a contiguous range of output blocks t = x * per_xcd + id / 8.  Within the
-  // range, blocks are grouped 8 row blocks high: the 32 workgroups an XCD runs at
-  // once cover about 8 row blocks x 4 column blocks, whose A and B stages they
-  // share through that XCD's L2.
+  // Output blocks.  The grid is one workgroup per CU (a multiple of 8) and each
+  // workgroup works through several blocks.  Workgroup ids go to the 8 XCDs in turn
+  // (id mod 8): XCD x owns the contiguous range of blocks [x per_xcd, (x + 1) per_xcd),
+  // and its workgroup j takes blocks x per_xcd + j, + j + G / 8, ..., so at any time
+  // the XCD's workgroups hold consecutive blocks.  Blocks are numbered in groups 8 row
+  // blocks high, so consecutive blocks share rows of A or of B through the XCD's L2.
   const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
   const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
-  const int64_t per_xcd = (nbm * nbn + 7) / 8;
-  const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (t >= nbm * nbn) return;
-  constexpr int64_t kGroup = 8;
-  const int64_t grp = t / (kGroup * nbn);
-  const int64_t rows_in_grp = nbm - grp * kGroup < kGroup ? nbm - grp * kGroup : kGroup;
-  const int64_t in_grp = t - grp * kGroup * nbn;
-  const int64_t bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
-  const int64_t bn0 = (in_grp / rows_in_grp) * kBigBM;
-  const int64_t mrows = g.M - bm0 < kBigBM ? g.M - bm0 : kBigBM;
-  const int64_t nrows = g.N - bn0 < kBigBM ? g.N - bn0 : kBigBM;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda,
-                                              (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb,
-                                              (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
+  const int64_t ntiles = nbm * nbn;
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t wpx = gridDim.x / 8;
+  const int64_t xcd = blockIdx.x % 8;
+  const int64_t t0 = xcd * per_xcd + blockIdx.x / 8;
+  const int64_t t_end = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
+  if (t0 >= t_end) return;
+  const int ntl = (int)((t_end - t0 + wpx - 1) / wpx);  // blocks of this workgroup
+  auto origin = [&](int u, int64_t& bm0, int64_t& bn0) {
+    const int64_t t = t0 + (int64_t)u * wpx;
+    constexpr int64_t kGroup = 8;
+    const int64_t grp = t / (kGroup * nbn);
+    const int64_t rows_in_grp = nbm - grp * kGroup < kGroup ? nbm - grp * kGroup : kGroup;
+    const int64_t in_grp = t - grp * kGroup * nbn;
+    bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
+    bn0 = (in_grp / rows_in_grp) * kBigBM;
+  };
   __shared__ __attribute__((aligned(16))) uint8_t lds[kBigBufs][2][kBigBM * kBigStage];
 
   const uint32_t kbytes = (uint32_t)(g.K * E);
-  const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);
-  // DMA share of this wave: rows 32 w .. 32 w + 31 of A and of B, two 16-row loads
-  // each.  Lane i of a load lands at row base + i / 4, physical chunk i % 4, so it
-  // fetches the logical chunk (i % 4) ^ big_swz(row).  Stages past the last are still
-  // issued, as loads past every row (read as zero): every stage then has 4 loads per
-  // wave in flight, whatever the position in K.
+  // stages per block, even: an odd count gets one more, past K (read as zero)
+  const int nst = (int)((kbytes + 2 * kBigStage - 1) / (2 * kBigStage)) * 2;
+  // The loads run through the workgroup's blocks as one stream of K stages: the
+  // stages of its next block follow those of the current one in the ring, so the
+  // next block's first stages land while the current one finishes and is written.
+  // Load cursor: stage ds of block du, with that block's buffer resources; past the
+  // last block, loads past every row (read as zero), so every stage has 4 loads per
+  // wave in flight.  DMA share of this wave: rows 32 w .. 32 w + 31 of A and of B,
+  // two 16-row loads each.  Lane i of a load lands at row base + i / 4, physical chunk
+  // i % 4, so it fetches the logical chunk (i % 4) ^ big_swz(row).
   const uint32_t lrow = (uint32_t)(lane >> 2);
   const uint32_t ldaE = (uint32_t)(g.lda * E), ldbE = (uint32_t)(g.ldb * E);
-  // Load n (0..3) of this wave for stage s: rows 32 w + 16 (n >> 1) + (0..15) of A
-  // (n even) or of B (n odd).
-  auto dma_one = [&](int s, int buf, int n) {
-    const uint32_t scut = s < nst ? 0u : kOutOfRange;
+  int du = 0, ds = 0;
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, 0), rb = make_rsrc(g.B, 0);
+  auto load_block = [&](int u) {
+    if (u >= ntl) return;
+    int64_t bm0, bn0;
+    origin(u, bm0, bn0);
+    const int64_t mrows = g.M - bm0 < kBigBM ? g.M - bm0 : kBigBM;
+    const int64_t nrows = g.N - bn0 < kBigBM ? g.N - bn0 : kBigBM;
+    ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda, (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
+    rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb, (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
+  };
+  // Load n (0..3) of this wave for the cursor's stage: rows 32 w + 16 (n >> 1) + (0..15)
+  // of A (n even) or of B (n odd).
+  auto dma_one = [&](int buf, int n) {
+    const uint32_t scut = du < ntl ? 0u : kOutOfRange;
     const uint32_t row = (uint32_t)(32 * w + 16 * (n >> 1)) + lrow;
-    const uint32_t kb = (uint32_t)s * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
+    const uint32_t kb = (uint32_t)ds * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
     // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
     const uint32_t kcut = kb < kbytes ? scut : kOutOfRange;
     if (n & 1)
@@ -481,9 +501,11 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(32 * w + 16 * (n >> 1)) * kBigStage], 16,
                                                (row * ldaE + kb) | kcut, 0, 0, 0);
   };
-  auto dma = [&](int s, int buf) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) dma_one(s, buf, n);
+  auto next_load = [&] {
+    if (++ds == nst) {
+      ds = 0;
+      load_block(++du);
+    }
   };
   // A barrier without a memory fence: a fence here would make every wave wait for
   // all of its loads in flight (they write LDS); instead each wave waits for its
@@ -500,35 +522,88 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   auto read_b = [&](int buf, int j) {
     return *reinterpret_cast<const u32x4*>(&lds[buf][1][big_off(wn * 64 + 16 * j + r16, q)]);
   };
-  // acc += a b^T on one 16 x 16 tile.  For bf16 the MFMA is written out so that its
-  // accumulator is tied to its result register: the compiler's own form may put the
-  // result in another AGPR quad, which across the K loop turns into a rotation of the
-  // accumulators through VGPRs at every stage.  The "memory" clobber keeps the LDS
-  // reads where they are written, between the MFMAs.
+  // acc += (a b^T)^T on one 16 x 16 tile: the B fragment goes in as the first MFMA
+  // operand, so lane (q, r) holds the outputs (row r, columns 4q .. 4q + 3) of the tile,
+  // which it stores as one 8- or 16-byte segment.  For bf16 the MFMA is written out so
+  // that its accumulator is tied to its result register: the compiler's own form may
+  // put the result in another AGPR quad, which across the K loop turns into a rotation
+  // of the accumulators through VGPRs at every stage.  The "memory" clobber keeps the
+  // LDS reads where they are written, between the MFMAs.
   auto mma = [](f32x4& c, const u32x4& a, const u32x4& b) {
     if constexpr (sizeof(IN) == 2)
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a) : "memory");
     else
-      c = Mfma<IN>::step(a, b, c);
+      c = Mfma<IN>::step(b, a, c);
   };
 
   f32x4 acc[TM][TN];
+  auto clear = [&] {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  clear();
 
-  // Stage k (operands a, b in registers, read during stage k - 1, those reads done):
-  // once this wave's loads of stage k + 1 have landed (those of k + 2 .. k + 4 may
-  // be in flight, 4 each) and every wave has passed the barrier, stage k + 1 is
-  // readable and the buffer of stage k is free, so the loads of stage k + 5 go there,
-  // spread over the MFMAs.
-  // Rows 0..5 of the tiles read, once a[i] is spent, the fragment i of A for stage
-  // k + 1 into a[i] itself; rows 0..3 read the fragment i of B into nb[i] after their
-  // first MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The last read is two
-  // rows before the end, so the wait for all of them before the next barrier is short.
+  // Output of block u straight from the accumulators: tile (i, j) of the wave gives
+  // lane (q, r) the 4 columns 16 j + 4 q .. + 3 of row 16 i + r; rows and columns past
+  // the edges are dropped.
+  OUT* cbase = static_cast<OUT*>(g.C);
+  // 32-bit offsets: a per-lane part (row r, columns 4q..) and a uniform part per tile.
+  // The lane index is counted afresh here (v_mbcnt, in a volatile statement the
+  // compiler cannot hoist), so that nothing per-lane is kept live across the K loop.
+  const uint32_t ldcB = (uint32_t)(g.ldc * (int64_t)sizeof(OUT));
+  auto write_block = [&](int u) {
+    uint32_t ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int r16 = (int)(ln & 15), q = (int)(ln >> 4);
+    const uint32_t lane_off = (uint32_t)r16 * ldcB + (uint32_t)(4 * q * (int)sizeof(OUT));
+    int64_t bm0, bn0;
+    origin(u, bm0, bn0);
+    const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 64;
+    const int64_t wrows = g.M - m0 < 128 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 128;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(
+        cbase + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
+    // the last MFMAs' results must be written before the accumulators are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const int wr = (int)wrows;                     // rows of this wave's part inside M
+    const int cl = (int)(g.N - n0) - 4 * q;        // columns left for this lane's segments
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const bool row_ok = 16 * i + r16 < wr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t off = lane_off + (uint32_t)(16 * i) * ldcB + (uint32_t)((n0 + 16 * j) * (int64_t)sizeof(OUT));
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = g.act ? silu(acc[i][j][r]) : acc[i][j][r];
+        // N and ldc are multiples of 4 and C is aligned to a segment (see big_ok)
+        const uint32_t o = row_ok && 16 * j < cl ? off : kOutOfRange;
+        if constexpr (sizeof(OUT) == 2) {
+          u32x2 pk;
+          pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(pk, rc, o, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, rc, o, 0,
+              0);
+        }
+      }
+    }
+  };
+
+  // Stage k of the stream (operands a, b in registers, read during stage k - 1, those
+  // reads done): once this wave's loads of stage k + 1 have landed (those of k + 2 ..
+  // k + 4 may be in flight, 4 each) and every wave has passed the barrier, stage k + 1
+  // is readable and the buffer of stage k is free, so the loads of stage k + 5 go there,
+  // spread over the MFMAs.  Rows 0..5 of the tiles read, once a[i] is spent, the fragment
+  // i of A for stage k + 1 into a[i] itself; rows 0..3 read the fragment i of B into
+  // nb[i] after their first MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The
+  // last read is two rows before the end, so the wait for all of them before the next
+  // barrier is short.
   int rbuf = 1, dbuf = 0;  // buffers of stages k + 1 and k + 5
-  auto step = [&](int k, u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
+  auto step = [&](u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
     wait_vm_lgkm0<12>();
     stage_barrier();
     u32x4 na[2];
@@ -541,90 +616,41 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
         if (j == 0 && (i == 4 || i == 5)) na[i - 4] = read_a(rbuf, i + 2);
         // the loads of stage k + 5, one per 8 MFMAs: issued together, the 32 loads
         // of a workgroup queue up behind each other and hold back the MFMAs after them
-        if (j == 2 && (i & 1) == 0) dma_one(k + 5, dbuf, i >> 1);
+        if (j == 2 && (i & 1) == 0) dma_one(dbuf, i >> 1);
       }
       if (i < 6) a[i] = read_a(rbuf, i);
     }
     a[6] = na[0];
     a[7] = na[1];
+    next_load();
     rbuf = rbuf == kBigBufs - 1 ? 0 : rbuf + 1;
     dbuf = dbuf == kBigBufs - 1 ? 0 : dbuf + 1;
   };
 
   u32x4 a[TM], b0[TN], b1[TN];
-  dma(0, 0);
-  dma(1, 1);
-  dma(2, 2);
-  dma(3, 3);
-  dma(4, 4);
+  load_block(0);
+#pragma unroll
+  for (int k = 0; k < kBigBufs; ++k) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) dma_one(k, n);
+    next_load();
+  }
   wait_vm_lgkm0<16>();
   stage_barrier();
 #pragma unroll
   for (int i = 0; i < TM; ++i) a[i] = read_a(0, i);
 #pragma unroll
   for (int j = 0; j < TN; ++j) b0[j] = read_b(0, j);
-  // Stages in pairs; an odd count gets one more, all zeros (its loads are past K).
-  for (int k = 0; k < nst; k += 2) {
-    step(k, a, b0, b1);
-    step(k + 1, a, b1, b0);
-  }
-  // Every load in flight (the zero stages past the end) lands before the buffers
-  // become the output staging area, and the last MFMAs finish before their
-  // accumulators are read.
-  wait_vm_lgkm0<0>();
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __syncthreads();
-
-  // Output: 16-row strips of the wave's 128 x 64 tile through LDS (fp32), then
-  // 16-byte row segments; rows and columns past the edges are dropped.
-  OUT* cbase = static_cast<OUT*>(g.C);
-  const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 64;
-  const int64_t wrows = g.M - m0 < 128 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 128;
-  const __amdgpu_buffer_rsrc_t rc =
-      make_rsrc(cbase + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
-  const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15u) == 0;
-  float(*st)[68] = reinterpret_cast<float(*)[68]>(&lds[0][0][0] + w * 16 * 68 * 4);
-  constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
-  constexpr int LPR = 64 / EPV;          // lanes per row
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st[4 * q + r][16 * j + r16] = acc[i][j][r];
-    __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave execute in order
-#pragma unroll
-    for (int e0 = 0; e0 < 16 * LPR; e0 += 64) {
-      const int e = e0 + lane;
-      const int row = e / LPR, c0 = (e % LPR) * EPV;
-      const int64_t grow = 16 * i + row;  // relative to m0
-      const int64_t gcol = n0 + c0;
-      float v[EPV];
-#pragma unroll
-      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][c0 + kk]) : st[row][c0 + kk];
-      if (vec_ok && gcol + EPV <= g.N) {
-        const uint32_t off = (uint32_t)((grow * g.ldc + gcol) * sizeof(OUT));
-        u32x4 pk;
-        if constexpr (sizeof(OUT) == 2) {
-          pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-          pk.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-          pk.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-        } else {
-          pk = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(pk, rc, grow < wrows ? off : kOutOfRange, 0, 0);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < EPV; ++kk) {
-          const uint32_t off =
-              gcol + kk < g.N ? (uint32_t)((grow * g.ldc + gcol + kk) * sizeof(OUT)) : kOutOfRange;
-          store_elem<OUT>(rc, grow < wrows ? off : kOutOfRange, v[kk]);
-        }
-      }
+  for (int u = 0; u < ntl; ++u) {
+    for (int k = 0; k < nst; k += 2) {
+      step(a, b0, b1);
+      step(a, b1, b0);
     }
-    __builtin_amdgcn_wave_barrier();
+    write_block(u);
+    clear();
   }
+  // every load in flight (the zero stages past the end) lands before the workgroup ends
+  wait_vm_lgkm0<0>();
 }
 
 // Any alignment: one thread per output element, K FMAs.
@@ -706,20 +732,24 @@ hipError_t gemm_nt_short(const GemmArgs& g, int ks, hipStream_t st) {
 // The large-block kernel pays off once both output dimensions fill several of
 // its 256 x 256 blocks and K spans a few stages.
 template <typename IN>
-bool big_ok(const GemmArgs& g) {
+bool big_ok(const GemmArgs& g, size_t out_bytes) {
   const int64_t e = sizeof(IN);
   // row offsets inside a 256-row block must stay below the out-of-range bit
   const bool offsets = 256 * g.lda * e + g.K * e < (int64_t)kOutOfRange && 256 * g.ldb * e + g.K * e < (int64_t)kOutOfRange;
-  return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr;
+  // each lane stores 4 consecutive outputs of a row as one aligned segment
+  const bool segments = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % (4 * out_bytes) == 0;
+  return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && segments &&
+         std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr;
 }
 
 template <typename IN, typename OUT>
 hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  if (mfma_ok<IN>(g) && parts == 1 && big_ok<IN>(g)) {
+  if (mfma_ok<IN>(g) && parts == 1 && big_ok<IN>(g, sizeof(OUT))) {
     const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
     const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
-    const int64_t blocks = (nbm * nbn + 7) / 8 * 8;  // 8 equal XCD ranges (ids past the last block exit)
+    // one workgroup per CU (the LDS holds one), in 8 equal XCD shares
+    const int64_t blocks = nbm * nbn < kBigCus ? (nbm * nbn + 7) / 8 * 8 : kBigCus;
     hipLaunchKernelGGL((gemm_nt_big_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(kBigThreads), 0, st, g);
     return hipGetLastError();
   }

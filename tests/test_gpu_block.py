@@ -51,7 +51,8 @@ def _gpu_block(inp, sw, bw, hidden, io):
     (2, 200, 96, 192, 8, 12, "f32"),
     (2, 600, 520, 1040, 16, 66, "bf16"),  # large-block GEMM kernel: ragged rows, columns and K
     (2, 600, 520, 1040, 8, 66, "f32"),
-    (2, 520, 512, 1036, 16, 66, "bf16"),  # large-block input projection with an unaligned output row (scalar stores)
+    (2, 520, 512, 1036, 16, 66, "bf16"),  # large-block input projection, output rows 8-byte but not 16-byte aligned
+    (2, 520, 512, 1034, 8, 66, "bf16"),   # D not a multiple of 4: input projection on the general kernel
 ], ids=str)
 def test_block_matches_oracle(case):
     _need_gpu()
