@@ -398,27 +398,23 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
 // Large products (the block's input and output projections): 256 x 256 output
 // blocks of 8 waves, two per SIMD (one wave per SIMD cannot issue MFMAs fast enough
 // to keep its matrix core busy), each wave owning 128 x 64 (8 x 4 tiles of 16 x 16,
-// accumulators in AGPRs).  Operands go from global memory straight into a ring of
-// five LDS stages of 32 KB, the whole 160 KB of a CU (buffer loads with the lds bit:
-// lane i of a load writes the 16 bytes at 16 i of its 1 KB destination).  While
-// stage k is multiplied, the operands of stage k + 1 are read from LDS between its
-// MFMAs and stages k + 2 .. k + 5 are in flight: four stages, 128 KB per CU, to
-// cover the latency of the loads that miss L2 (every stage has some, its first
-// touches of the A and B rows), since each stage waits for all of its loads.  A
-// stage holds 64 bytes of K for 256 rows of A and of B, the 16-byte chunk c of row
-// r at chunk c ^ ((r >> 1) & 3): an MFMA operand read (lane l: row l % 16, chunk
-// l / 16) then takes the 16 rows x 64 bytes of a fragment at the rate of a plain
-// 1 KB read, while without the swizzle, or with rows 8 apart also told apart, it
-// runs 25-40% slower (LDS serves the lanes of a 16-byte read in groups of 8).
-constexpr int kBigBM = 256;
-constexpr int kBigStage = 64;  // K bytes per row per stage
-constexpr int kBigBufs = 5;
+// accumulators in AGPRs).  K advances in stages of 128 bytes per row, one cache
+// line: operands go from global memory straight into LDS with buffer loads that
+// carry the lds bit (lane i of a load writes the 16 bytes at 16 i of its 1 KB
+// destination, so one load moves 8 rows x 128 bytes); such loads of whole lines move
+// 1.7x the bytes per unit time of loads of half lines.  A stage is 512 rows x 128
+// bytes = 64 KB and LDS holds two: while stage p is multiplied (in two halves of 64
+// bytes of K), stage p + 1 lands.  Row r's 16-byte chunk c sits at chunk
+// c ^ ((r >> 1) & 7): the MFMA operand reads (lane l: row l % 16, chunk 4h + l / 16)
+// then run at the rate of plain 1 KB reads.
+constexpr int kBigBM = 256;     // rows of A (and of B) per output block
+constexpr int kBigStage = 128;  // K bytes per row per stage
+constexpr int kBigBufs = 2;
 constexpr int kBigThreads = 512;
 constexpr int64_t kBigCus = 256;  // compute units of an MI355X: the kernel's grid
 
-__device__ __forceinline__ uint32_t big_swz(uint32_t row) { return (row >> 1) & 3u; }
 __device__ __forceinline__ uint32_t big_off(uint32_t row, uint32_t chunk) {
-  return row * kBigStage + 16u * (chunk ^ big_swz(row));
+  return row * kBigStage + 16u * (chunk ^ ((row >> 1) & 7u));
 }
 
 // s_waitcnt with vmcnt = n and lgkmcnt = 0 (expcnt not waited for).
@@ -460,20 +456,20 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
     bn0 = (in_grp / rows_in_grp) * kBigBM;
   };
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBigBufs][2][kBigBM * kBigStage];
+  // LDS rows 0..255: A; rows 256..511: B.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBigBufs][2 * kBigBM * kBigStage];
 
   const uint32_t kbytes = (uint32_t)(g.K * E);
-  // stages per block, even: an odd count gets one more, past K (read as zero)
-  const int nst = (int)((kbytes + 2 * kBigStage - 1) / (2 * kBigStage)) * 2;
+  const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);  // stages per block
   // The loads run through the workgroup's blocks as one stream of K stages: the
   // stages of its next block follow those of the current one in the ring, so the
   // next block's first stages land while the current one finishes and is written.
   // Load cursor: stage ds of block du, with that block's buffer resources; past the
-  // last block, loads past every row (read as zero), so every stage has 4 loads per
-  // wave in flight.  DMA share of this wave: rows 32 w .. 32 w + 31 of A and of B,
-  // two 16-row loads each.  Lane i of a load lands at row base + i / 4, physical chunk
-  // i % 4, so it fetches the logical chunk (i % 4) ^ big_swz(row).
-  const uint32_t lrow = (uint32_t)(lane >> 2);
+  // last block, loads past every row (read as zero).  DMA share of this wave per
+  // stage: rows 32 w .. 32 w + 31 of A and of B, four loads of 8 rows each.  Lane i
+  // of a load lands at row base + i / 8, physical chunk i % 8, so it fetches the
+  // logical chunk (i % 8) ^ ((row >> 1) & 7).
+  const uint32_t lrow = (uint32_t)(lane >> 3), lch = (uint32_t)(lane & 7);
   const uint32_t ldaE = (uint32_t)(g.lda * E), ldbE = (uint32_t)(g.ldb * E);
   int du = 0, ds = 0;
   __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, 0), rb = make_rsrc(g.B, 0);
@@ -486,20 +482,24 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     ra = make_rsrc(static_cast<const IN*>(g.A) + bm0 * g.lda, (uint32_t)(((mrows - 1) * g.lda + g.K) * E));
     rb = make_rsrc(static_cast<const IN*>(g.B) + bn0 * g.ldb, (uint32_t)(((nrows - 1) * g.ldb + g.K) * E));
   };
-  // Load n (0..3) of this wave for the cursor's stage: rows 32 w + 16 (n >> 1) + (0..15)
-  // of A (n even) or of B (n odd).
+  // Load n (0..7) of this wave for the cursor's stage: rows 32 w + 8 m + (0..7) of A
+  // (n = 2m) or of B (n = 2m + 1).  Row r = 32 w + 8 m + lrow has the swizzle
+  // (r >> 1) & 7 = (lrow >> 1) ^ 4 (m & 1): two per-lane chunk offsets serve all loads.
+  const uint32_t la = lrow * ldaE, lb = lrow * ldbE;
+  const uint32_t ch0 = 16u * (lch ^ (lrow >> 1)), ch1 = 16u * (lch ^ ((lrow >> 1) ^ 4u));
   auto dma_one = [&](int buf, int n) {
-    const uint32_t scut = du < ntl ? 0u : kOutOfRange;
-    const uint32_t row = (uint32_t)(32 * w + 16 * (n >> 1)) + lrow;
-    const uint32_t kb = (uint32_t)ds * kBigStage + 16u * ((uint32_t)(lane & 3) ^ big_swz(row));
-    // past K: an offset past every row (rows are at most 256 x lda apart), read as zero
-    const uint32_t kcut = kb < kbytes ? scut : kOutOfRange;
+    const uint32_t m = (uint32_t)(n >> 1);
+    const uint32_t ch = (m & 1) ? ch1 : ch0;
+    const uint32_t kb = (uint32_t)ds * kBigStage + ch;
+    // past K or past the last block: an offset past every row, read as zero
+    const uint32_t cut = kb < kbytes && du < ntl ? 0u : kOutOfRange;
+    const uint32_t r0 = (uint32_t)(32 * w) + 8u * m;  // first row of the load
     if (n & 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][1][(32 * w + 16 * (n >> 1)) * kBigStage], 16,
-                                               (row * ldbE + kb) | kcut, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, &lds[buf][(kBigBM + r0) * kBigStage], 16,
+                                               (r0 * ldbE + lb + kb) | cut, 0, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][0][(32 * w + 16 * (n >> 1)) * kBigStage], 16,
-                                               (row * ldaE + kb) | kcut, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, &lds[buf][r0 * kBigStage], 16, (r0 * ldaE + la + kb) | cut, 0, 0,
+                                               0);
   };
   auto next_load = [&] {
     if (++ds == nst) {
@@ -516,11 +516,12 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
-  auto read_a = [&](int buf, int i) {
-    return *reinterpret_cast<const u32x4*>(&lds[buf][0][big_off(wm * 128 + 16 * i + r16, q)]);
+  // Operand fragments of half h (64 bytes of K) of a stage.
+  auto read_a = [&](int buf, int i, int h) {
+    return *reinterpret_cast<const u32x4*>(&lds[buf][big_off(wm * 128 + 16 * i + r16, 4 * h + q)]);
   };
-  auto read_b = [&](int buf, int j) {
-    return *reinterpret_cast<const u32x4*>(&lds[buf][1][big_off(wn * 64 + 16 * j + r16, q)]);
+  auto read_b = [&](int buf, int j, int h) {
+    return *reinterpret_cast<const u32x4*>(&lds[buf][big_off(kBigBM + wn * 64 + 16 * j + r16, 4 * h + q)]);
   };
   // acc += (a b^T)^T on one 16 x 16 tile: the B fragment goes in as the first MFMA
   // operand, so lane (q, r) holds the outputs (row r, columns 4q .. 4q + 3) of the tile,
@@ -593,58 +594,65 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     }
   };
 
-  // Stage k of the stream (operands a, b in registers, read during stage k - 1, those
-  // reads done): once this wave's loads of stage k + 1 have landed (those of k + 2 ..
-  // k + 4 may be in flight, 4 each) and every wave has passed the barrier, stage k + 1
-  // is readable and the buffer of stage k is free, so the loads of stage k + 5 go there,
-  // spread over the MFMAs.  Rows 0..5 of the tiles read, once a[i] is spent, the fragment
-  // i of A for stage k + 1 into a[i] itself; rows 0..3 read the fragment i of B into
-  // nb[i] after their first MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The
-  // last read is two rows before the end, so the wait for all of them before the next
-  // barrier is short.
-  int rbuf = 1, dbuf = 0;  // buffers of stages k + 1 and k + 5
-  auto step = [&](u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
-    wait_vm_lgkm0<12>();
-    stage_barrier();
+  // Stage p of the stream in two halves of 64 bytes of K, with the operands of the
+  // current half in registers (read during the previous half):
+  // - first half: 32 MFMAs, and the second half's operands read from stage p's buffer
+  //   between them;
+  // - second half: once this wave's loads of stage p + 1 have landed and every wave has
+  //   passed the barrier (each wave waits for its LDS reads before it), stage p + 1 is
+  //   readable and stage p's buffer is read by no one, so the loads of stage p + 2 go
+  //   there, spread over the MFMAs, while the first half of stage p + 1 is read between
+  //   them.
+  // Rows 0..5 of the tiles read, once a[i] is spent, the next half's fragment i of A
+  // into a[i] itself; rows 0..3 read fragment i of B into nb[i] after their first
+  // MFMA, rows 4 and 5 the A fragments 6 and 7 into na.  The last read is two rows
+  // before the end, so the wait for all of them before the next barrier is short.
+  int pbuf = 0;  // buffer of stage p; stage p + 1 in the other
+  auto half = [&](int h, u32x4 (&a)[TM], const u32x4 (&b)[TN], u32x4 (&nb)[TN]) {
+    const int nbuf = h == 0 ? pbuf : pbuf ^ 1;
+    if (h == 1) {
+      wait_vm_lgkm0<0>();
+      stage_barrier();
+    }
     u32x4 na[2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         mma(acc[i][j], a[i], b[j]);
-        if (j == 0 && i < TN) nb[i] = read_b(rbuf, i);
-        if (j == 0 && (i == 4 || i == 5)) na[i - 4] = read_a(rbuf, i + 2);
-        // the loads of stage k + 5, one per 8 MFMAs: issued together, the 32 loads
-        // of a workgroup queue up behind each other and hold back the MFMAs after them
-        if (j == 2 && (i & 1) == 0) dma_one(dbuf, i >> 1);
+        if (j == 0 && i < TN) nb[i] = read_b(nbuf, i, h ^ 1);
+        if (j == 0 && (i == 4 || i == 5)) na[i - 4] = read_a(nbuf, i + 2, h ^ 1);
+        // the loads of stage p + 2, one per 4 MFMAs
+        if (h == 1 && j == 2) dma_one(pbuf, i);
       }
-      if (i < 6) a[i] = read_a(rbuf, i);
+      if (i < 6) a[i] = read_a(nbuf, i, h ^ 1);
     }
     a[6] = na[0];
     a[7] = na[1];
-    next_load();
-    rbuf = rbuf == kBigBufs - 1 ? 0 : rbuf + 1;
-    dbuf = dbuf == kBigBufs - 1 ? 0 : dbuf + 1;
+    if (h == 1) {
+      next_load();
+      pbuf ^= 1;
+    }
   };
 
   u32x4 a[TM], b0[TN], b1[TN];
   load_block(0);
-#pragma unroll
+#pragma unroll 1
   for (int k = 0; k < kBigBufs; ++k) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) dma_one(k, n);
+    for (int n = 0; n < 8; ++n) dma_one(k, n);
     next_load();
   }
-  wait_vm_lgkm0<16>();
+  wait_vm_lgkm0<8>();
   stage_barrier();
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a[i] = read_a(0, i);
+  for (int i = 0; i < TM; ++i) a[i] = read_a(0, i, 0);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b0[j] = read_b(0, j);
+  for (int j = 0; j < TN; ++j) b0[j] = read_b(0, j, 0);
   for (int u = 0; u < ntl; ++u) {
-    for (int k = 0; k < nst; k += 2) {
-      step(a, b0, b1);
-      step(a, b1, b0);
+    for (int k = 0; k < nst; ++k) {
+      half(0, a, b0, b1);
+      half(1, a, b1, b0);
     }
     write_block(u);
     clear();
