@@ -32,13 +32,14 @@ def _problem(batch, L, dm, D, N, R, io, seed):
     return inp, sw, bw, hidden
 
 
-def _gpu_block(inp, sw, bw, hidden, io):
+def _gpu_block(inp, sw, bw, hidden, io, h0=None):
     from selective_state_space_22_amd import mamba_block_fwd
 
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
     out, last = mamba_block_fwd(torch_io(hidden, io, "cuda"), torch_io(bw.W_in, io, "cuda"),
                                 torch_io(sw.W_x, io, "cuda"), torch_io(sw.W_dt, io, "cuda"), f(inp.A),
-                                torch_io(bw.W_out, io, "cuda"), dt_bias=f(inp.delta_bias), Dskip=f(inp.Dskip))
+                                torch_io(bw.W_out, io, "cuda"), dt_bias=f(inp.delta_bias), Dskip=f(inp.Dskip),
+                                h0=None if h0 is None else f(h0))
     torch.cuda.synchronize()
     return to_host(out), last.cpu().numpy()
 
@@ -81,3 +82,50 @@ def test_block_mamba3b_shape_row_sampled():
     eo, el = parity_error(go[:1], ro), parity_error(gl[:1], rl)
     print(f"mamba3b block row 0: out err {eo:.3e} last err {el:.3e}")
     assert np.isfinite(go).all() and eo <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_block_initial_state_matches_oracle(io):
+    """An initial state h0 enters the selective SSM of the block (the oracle's block with the same h0)."""
+    _need_gpu()
+    batch, L, dm, D, N, R = 2, 150, 96, 192, 16, 12
+    print(f"\n[gpu-test] mamba block with h0 {io}", flush=True)
+    inp, sw, bw, hidden = _problem(batch, L, dm, D, N, R, io, seed=W.SEED_BASE + 410)
+    h0 = np.random.default_rng(7).standard_normal((batch, D, N)).astype(np.float32)
+    go, gl = _gpu_block(inp, sw, bw, hidden, io, h0=h0)
+    ro, rl = oracle.block(hidden, bw.W_in, sw.W_x, sw.W_dt, inp.delta_bias, inp.A, inp.Dskip, bw.W_out, N,
+                          h0=h0.astype(np.float64), store=_store(io))
+    eo, el = parity_error(go, ro), parity_error(gl, rl)
+    print(f"block with h0 {io}: out err {eo:.3e} last err {el:.3e}")
+    assert eo <= TOL[io] and el <= TOL[io]
+
+
+def test_block_chains_over_the_sequence():
+    """Two calls over the halves of a sequence, the second from the first one's last state, give the
+    outputs and last state of one call over the whole sequence (the projections act per token)."""
+    _need_gpu()
+    batch, L, dm, D, N, R, io = 2, 300, 64, 128, 16, 8, "f32"
+    print("\n[gpu-test] mamba block chained over two halves", flush=True)
+    inp, sw, bw, hidden = _problem(batch, L, dm, D, N, R, io, seed=W.SEED_BASE + 420)
+    full_o, full_l = _gpu_block(inp, sw, bw, hidden, io)
+    o1, l1 = _gpu_block(inp, sw, bw, np.ascontiguousarray(hidden[:, :L // 2]), io)
+    o2, l2 = _gpu_block(inp, sw, bw, np.ascontiguousarray(hidden[:, L // 2:]), io, h0=l1)
+    eo = parity_error(np.concatenate([o1, o2], axis=1), full_o)
+    el = parity_error(l2, full_l)
+    print(f"chained block: out err {eo:.3e} last err {el:.3e}")
+    assert eo <= TOL[io] and el <= TOL[io]
+
+
+def test_block_empty_sequence_passes_the_state():
+    """No tokens: no output rows, and the last state is the initial state (zero without one)."""
+    _need_gpu()
+    batch, dm, D, N, R, io = 2, 64, 128, 16, 8, "f32"
+    print("\n[gpu-test] mamba block with no tokens", flush=True)
+    inp, sw, bw, _ = _problem(batch, 1, dm, D, N, R, io, seed=W.SEED_BASE + 430)
+    hidden = np.zeros((batch, 0, dm), np.float32)
+    h0 = np.random.default_rng(3).standard_normal((batch, D, N)).astype(np.float32)
+    o, last = _gpu_block(inp, sw, bw, hidden, io, h0=h0)
+    assert o.shape == (batch, 0, dm)
+    assert np.array_equal(last, h0)
+    _, last0 = _gpu_block(inp, sw, bw, hidden, io)
+    assert not np.any(last0)
