@@ -219,3 +219,52 @@ def test_complex_decode_graph_replays_match_eager():
             binding.mamba_state_update_complex(state, u, dl, A, B, C, d["delta_bias"], d["Dskip"], z, True, out=o)
 
     _replay_matches(call, outs + [view])
+
+
+def test_block_graph_replays_match_eager():
+    """mamba_block_fwd captured whole: the projections on the persistent large-product
+    kernel, the selection GEMMs with their split-K reduction, and the scan."""
+    _need_gpu()
+    from selective_state_space_22_amd import binding
+    from gpu_util import torch_io
+
+    batch, L, dm, D, N, R, io = 2, 600, 520, 1040, 16, 66, "bf16"
+    print(f"\n[gpu-test] graph replay of mamba_block_fwd {(batch, L, dm, D, N, R, io)}", flush=True)
+    inp = W.generate(batch, 1, D, N, io, seed=321)
+    sw = W.selection_weights(D, N, R, io, seed=321)
+    bw = W.block_weights(dm, D, io, seed=321)
+    hidden = torch_io(W.block_hidden(batch, L, dm, io, seed=321), io, "cuda")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    win, wx, wdt, wout = (torch_io(w, io, "cuda") for w in (bw.W_in, sw.W_x, sw.W_dt, bw.W_out))
+    A, bias, dskip = f(inp.A), f(inp.delta_bias), f(inp.Dskip)
+    out = torch.empty_like(hidden)
+    last = torch.empty((batch, D, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(binding.mamba_block_fwd_workspace_size(batch, L, dm, D, N, R, 1), 1), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        binding.mamba_block_fwd(hidden, win, wx, wdt, A, wout, dt_bias=bias, Dskip=dskip, out=out, last_state=last,
+                                workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_out, ref_last = out.clone(), last.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm the stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        last.fill_(float("nan"))
+        ws.fill_(rep * 37 % 256)  # scratch contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {rep}: out differs"
+        assert torch.equal(last, ref_last), f"replay {rep}: last_state differs"
+        _ = (hidden.float() * 2).sum().item()  # unrelated eager work between replays
