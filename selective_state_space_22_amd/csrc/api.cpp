@@ -472,7 +472,9 @@ size_t mamba_block_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_m
   const size_t e = io_dtype == MAMBA_IO_BF16 ? 2 : 4;
   const size_t tok = (size_t)batch * seqlen;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  return 3 * al(tok * dim * e) + mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype);
+  // x, z, y, the projections' split-K partial blocks, then the selective SSM's workspace
+  return 3 * al(tok * dim * e) + al(s6::gemm_nt_part_bytes()) +
+         mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype);
 }
 
 int mamba_block_fwd(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim, int64_t dstate, int64_t dt_rank,
@@ -510,23 +512,25 @@ int mamba_block_fwd(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim,
   void* x = tokens ? w : nullptr;
   void* z = tokens ? w + al((size_t)M * dim * e) : nullptr;
   void* y = tokens ? w + 2 * al((size_t)M * dim * e) : nullptr;
-  void* ssm_ws = tokens ? w + 3 * al((size_t)M * dim * e) : nullptr;
+  float* part = tokens ? reinterpret_cast<float*>(w + 3 * al((size_t)M * dim * e)) : nullptr;
+  const size_t head = 3 * al((size_t)M * dim * e) + al(s6::gemm_nt_part_bytes());
+  void* ssm_ws = tokens ? w + head : nullptr;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t he = hipSuccess;
   if (tokens) {
     // input projection: SSM branch (first dim rows of W_in) through SiLU, gate branch plain
-    he = s6::launch_gemm_nt(hidden, W_in, x, M, dim, d_model, d_model, d_model, dim, io_dtype, 1, hs);
+    he = s6::launch_gemm_nt(hidden, W_in, x, M, dim, d_model, d_model, d_model, dim, io_dtype, 1, part, hs);
     if (he == hipSuccess)
       he = s6::launch_gemm_nt(hidden, static_cast<const uint8_t*>(W_in) + (size_t)dim * d_model * e, z, M, dim,
-                              d_model, d_model, d_model, dim, io_dtype, 0, hs);
+                              d_model, d_model, d_model, dim, io_dtype, 0, part, hs);
     if (he != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(he));
   }
   st = mamba_ssm_fwd(batch, seqlen, dim, dstate, dt_rank, io_dtype, x, z, W_x, W_dt, dt_bias, A, Dskip,
                      delta_softplus, h0, y, last_state, ssm_ws,
-                     tokens ? workspace_bytes - 3 * al((size_t)M * dim * e) : 0, stream);
+                     tokens ? workspace_bytes - head : 0, stream);
   if (st != MAMBA_OK) return st;
   if (tokens) {
-    he = s6::launch_gemm_nt(y, W_out, out, M, d_model, dim, dim, dim, d_model, io_dtype, 0, hs);
+    he = s6::launch_gemm_nt(y, W_out, out, M, d_model, dim, dim, dim, d_model, io_dtype, 0, part, hs);
     if (he != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(he));
   }
   return MAMBA_OK;

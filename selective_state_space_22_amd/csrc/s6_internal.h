@@ -185,9 +185,12 @@ int64_t selection_ld(int64_t R, int64_t N);
 size_t selection_ws_bytes(int64_t batch, int64_t L, int64_t R, int64_t N, int io);
 hipError_t launch_selection(const SelArgs& s, int io, hipStream_t stream);
 // C (I/O type) = A B^T, A: M x K, B: N x K (row strides lda, ldb, ldc); act = 1
-// applies SiLU to every output element before rounding.
+// applies SiLU to every output element before rounding.  part: scratch of
+// gemm_nt_part_bytes() for the large-product kernel's K-split last round (may be
+// null: no split).
+size_t gemm_nt_part_bytes();
 hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                          int64_t ldb, int64_t ldc, int io, int act, hipStream_t stream);
+                          int64_t ldb, int64_t ldc, int io, int act, float* part, hipStream_t stream);
 
 // Enqueue the kernels of one scan / one decode step on `stream`.
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);

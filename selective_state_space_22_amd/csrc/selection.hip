@@ -85,6 +85,9 @@ struct GemmArgs {
   int32_t sps = 0;
   int32_t parts = 1;
   int32_t act = 0;  // 1: SiLU of every output element (applied in fp32 before rounding)
+  // large-product kernel: one fp32 256 x 256 slot per workgroup for the halves of the
+  // blocks of a last, at most half-filled round, split in K (null: no split)
+  float* part = nullptr;
 };
 
 // 128 x 128 output block per workgroup of 2 x 2 waves (4 x 4 tiles of 16 x 16
@@ -437,18 +440,31 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   // and its workgroup j takes blocks x per_xcd + j, + j + G / 8, ..., so at any time
   // the XCD's workgroups hold consecutive blocks.  Blocks are numbered in groups 8 row
   // blocks high, so consecutive blocks share rows of A or of B through the XCD's L2.
+  // When the XCD's last round is at most half full (rem blocks for G / 8 workgroups),
+  // its blocks are split in K instead: workgroup j takes half j / rem of block
+  // j % rem and writes fp32 partial sums to its slot of g.part, which
+  // big_fixup_kernel adds up (so no workgroup idles for a whole block).
   const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
   const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
   const int64_t ntiles = nbm * nbn;
   const int64_t per_xcd = (ntiles + 7) / 8;
   const int64_t wpx = gridDim.x / 8;
   const int64_t xcd = blockIdx.x % 8;
-  const int64_t t0 = xcd * per_xcd + blockIdx.x / 8;
-  const int64_t t_end = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
-  if (t0 >= t_end) return;
-  const int ntl = (int)((t_end - t0 + wpx - 1) / wpx);  // blocks of this workgroup
+  const int64_t jw = blockIdx.x / 8;
+  const int64_t xbeg = xcd * per_xcd;
+  const int64_t xend = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
+  const int64_t nx = xend > xbeg ? xend - xbeg : 0;  // blocks of this XCD
+  const int64_t rounds = nx / wpx, rem = nx % wpx;
+  const bool split = g.part != nullptr && rem > 0 && 2 * rem <= wpx;
+  const int nfull = (int)rounds + (!split && jw < rem ? 1 : 0);
+  const bool has_half = split && jw < 2 * rem;
+  const int ntl = nfull + (has_half ? 1 : 0);  // items (blocks or halves) of this workgroup
+  if (ntl == 0) return;
+  auto tile_of = [&](int u) -> int64_t {
+    return u < nfull ? xbeg + jw + (int64_t)u * wpx : xbeg + rounds * wpx + jw % (rem > 0 ? rem : 1);
+  };
   auto origin = [&](int u, int64_t& bm0, int64_t& bn0) {
-    const int64_t t = t0 + (int64_t)u * wpx;
+    const int64_t t = tile_of(u);
     constexpr int64_t kGroup = 8;
     const int64_t grp = t / (kGroup * nbn);
     const int64_t rows_in_grp = nbm - grp * kGroup < kGroup ? nbm - grp * kGroup : kGroup;
@@ -461,6 +477,11 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
 
   const uint32_t kbytes = (uint32_t)(g.K * E);
   const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);  // stages per block
+  // stages [s_begin, s_end) of item u: a half takes the first nh stages or the rest
+  const int nh = (nst + 1) / 2;
+  const int half_no = has_half ? (int)(jw / rem) : 0;
+  auto s_begin = [&](int u) { return u == nfull && half_no == 1 ? nh : 0; };
+  auto s_end = [&](int u) { return u == nfull && half_no == 0 ? nh : nst; };
   // The loads run through the workgroup's blocks as one stream of K stages: the
   // stages of its next block follow those of the current one in the ring, so the
   // next block's first stages land while the current one finishes and is written.
@@ -502,9 +523,10 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
                                                0);
   };
   auto next_load = [&] {
-    if (++ds == nst) {
-      ds = 0;
-      load_block(++du);
+    if (du < ntl && ++ds == s_end(du)) {
+      ++du;
+      ds = du < ntl ? s_begin(du) : 0;
+      load_block(du);
     }
   };
   // A barrier without a memory fence: a fence here would make every wave wait for
@@ -594,6 +616,26 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     }
   };
 
+  // A half block's fp32 partial sums, to this workgroup's slot of g.part (256 x 256,
+  // row-major, whole: the edges are dropped when the halves are added up).
+  auto write_partial = [&] {
+    uint32_t ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const uint32_t r16 = ln & 15, q = ln >> 4;
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(g.part + (size_t)blockIdx.x * kBigBM * kBigBM, (uint32_t)(kBigBM * kBigBM * sizeof(float)));
+    const uint32_t lane_off = ((uint32_t)(wm * 128) + r16) * (kBigBM * 4) + ((uint32_t)(wn * 64) + 4 * q) * 4;
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[i][j][0]), __float_as_uint(acc[i][j][1]), __float_as_uint(acc[i][j][2]),
+                  __float_as_uint(acc[i][j][3])},
+            rp, lane_off + (uint32_t)(16 * i * kBigBM * 4 + 16 * j * 4), 0, 0);
+  };
+
   // Stage p of the stream in two halves of 64 bytes of K, with the operands of the
   // current half in registers (read during the previous half):
   // - first half: 32 MFMAs, and the second half's operands read from stage p's buffer
@@ -636,6 +678,7 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   };
 
   u32x4 a[TM], b0[TN], b1[TN];
+  ds = s_begin(0);
   load_block(0);
 #pragma unroll 1
   for (int k = 0; k < kBigBufs; ++k) {
@@ -650,15 +693,66 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) b0[j] = read_b(0, j, 0);
   for (int u = 0; u < ntl; ++u) {
-    for (int k = 0; k < nst; ++k) {
+    for (int k = s_begin(u); k < s_end(u); ++k) {
       half(0, a, b0, b1);
       half(1, a, b1, b0);
     }
-    write_block(u);
+    if (u < nfull) write_block(u);
+    else write_partial();
     clear();
   }
   // every load in flight (the zero stages past the end) lands before the workgroup ends
   wait_vm_lgkm0<0>();
+}
+
+// The blocks that gemm_nt_big_kernel split in K, added up: workgroup b takes rows
+// 16 (b % 16) .. + 15 of XCD x's split block r (x = (b / 16) % 8, r = b / 128), whose
+// halves are in the slots of workgroups 8 r + x and 8 (r + rem) + x of the big kernel's
+// grid of G; it applies the SiLU where asked and stores 4 outputs at a time (N and ldc
+// are multiples of 4 and C is aligned to 4 outputs, see big_ok).
+template <typename OUT>
+__global__ __launch_bounds__(256) void big_fixup_kernel(GemmArgs g, int64_t grid) {
+  const int64_t nbn = (g.N + kBigBM - 1) / kBigBM;
+  const int64_t nbm = (g.M + kBigBM - 1) / kBigBM;
+  const int64_t ntiles = nbm * nbn;
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t wpx = grid / 8;
+  const int64_t strip = blockIdx.x % 16, xcd = (blockIdx.x / 16) % 8, r = blockIdx.x / 128;
+  const int64_t xbeg = xcd * per_xcd;
+  const int64_t xend = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
+  const int64_t nx = xend > xbeg ? xend - xbeg : 0;
+  const int64_t rounds = nx / wpx, rem = nx % wpx;
+  if (!(rem > 0 && 2 * rem <= wpx && r < rem)) return;
+  const int64_t t = xbeg + rounds * wpx + r;
+  constexpr int64_t kGroup = 8;
+  const int64_t grp = t / (kGroup * nbn);
+  const int64_t rows_in_grp = nbm - grp * kGroup < kGroup ? nbm - grp * kGroup : kGroup;
+  const int64_t in_grp = t - grp * kGroup * nbn;
+  const int64_t bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
+  const int64_t bn0 = (in_grp / rows_in_grp) * kBigBM;
+  const float4* p0 = reinterpret_cast<const float4*>(g.part + (size_t)(8 * r + xcd) * kBigBM * kBigBM);
+  const float4* p1 = reinterpret_cast<const float4*>(g.part + (size_t)(8 * (r + rem) + xcd) * kBigBM * kBigBM);
+  OUT* c = static_cast<OUT*>(g.C);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = (int)strip * 16 * (kBigBM / 4) + k * 256 + (int)threadIdx.x;  // float4 index in the block
+    const int64_t row = bm0 + e / (kBigBM / 4), col = bn0 + (e % (kBigBM / 4)) * 4;
+    if (row >= g.M || col >= g.N) continue;
+    const float4 x = p0[e], y = p1[e];
+    float v[4] = {x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w};
+    if (g.act)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = silu(v[i]);
+    OUT* dst = c + row * g.ldc + col;
+    if constexpr (sizeof(OUT) == 2) {
+      u32x2 pk;
+      pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst) = pk;
+    } else {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
 }
 
 // Any alignment: one thread per output element, K FMAs.
@@ -759,6 +853,18 @@ hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
     // one workgroup per CU (the LDS holds one), in 8 equal XCD shares
     const int64_t blocks = nbm * nbn < kBigCus ? (nbm * nbn + 7) / 8 * 8 : kBigCus;
     hipLaunchKernelGGL((gemm_nt_big_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(kBigThreads), 0, st, g);
+    if (g.part != nullptr) {  // any XCD with a split last round?
+      const int64_t ntiles = nbm * nbn, per_xcd = (ntiles + 7) / 8, wpx = blocks / 8;
+      bool any = false;
+      for (int64_t x = 0; x < 8; ++x) {
+        const int64_t lo = x * per_xcd, hi = (x + 1) * per_xcd < ntiles ? (x + 1) * per_xcd : ntiles;
+        const int64_t rem = (hi > lo ? hi - lo : 0) % wpx;
+        any = any || (rem > 0 && 2 * rem <= wpx);
+      }
+      // 16 row strips of each possible split block: 8 XCDs x wpx / 2 blocks
+      if (any)
+        hipLaunchKernelGGL((big_fixup_kernel<OUT>), dim3((unsigned)(16 * 8 * (wpx / 2))), dim3(256), 0, st, g, blocks);
+    }
     return hipGetLastError();
   }
   const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
@@ -825,10 +931,13 @@ hipError_t launch_selection(const SelArgs& s, int io, hipStream_t st) {
   return io == kIoBF16 ? launch_selection_t<uint16_t>(s, st) : launch_selection_t<float>(s, st);
 }
 
+size_t gemm_nt_part_bytes() { return (size_t)kBigCus * kBigBM * kBigBM * sizeof(float); }
+
 hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
-                          int64_t ldb, int64_t ldc, int io, int act, hipStream_t st) {
+                          int64_t ldb, int64_t ldc, int io, int act, float* part, hipStream_t st) {
   GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc};
   g.act = act;
+  g.part = part;
   return io == kIoBF16 ? gemm_nt<uint16_t, uint16_t>(g, st) : gemm_nt<float, float>(g, st);
 }
 
