@@ -256,7 +256,9 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
  *   W_out            : (d_model, dim)             I/O type
  *   W_x, W_dt, dt_bias, A, Dskip, delta_softplus, h0, last_state: as for mamba_ssm_fwd
  *   workspace        : at least mamba_block_fwd_workspace_size() bytes: x, z and
- *                      y (I/O type) and the selective SSM's workspace.
+ *                      y (I/O type), 64 MiB of fp32 partial sums for the
+ *                      projections (products whose last round of output blocks
+ *                      is split in K) and the selective SSM's workspace.
  * The three projections run on the matrix cores with fp32 accumulation; x, z
  * and y are stored in the I/O type, as a framework would keep them.
  */
