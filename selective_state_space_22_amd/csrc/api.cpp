@@ -519,10 +519,8 @@ int mamba_block_fwd(int64_t batch, int64_t seqlen, int64_t d_model, int64_t dim,
   hipError_t he = hipSuccess;
   if (tokens) {
     // input projection: SSM branch (first dim rows of W_in) through SiLU, gate branch plain
-    he = s6::launch_gemm_nt(hidden, W_in, x, M, dim, d_model, d_model, d_model, dim, io_dtype, 1, part, hs);
-    if (he == hipSuccess)
-      he = s6::launch_gemm_nt(hidden, static_cast<const uint8_t*>(W_in) + (size_t)dim * d_model * e, z, M, dim,
-                              d_model, d_model, d_model, dim, io_dtype, 0, part, hs);
+    he = s6::launch_gemm_nt_pair(hidden, W_in, x, z, M, dim, dim, d_model, d_model, d_model, dim, io_dtype, 1, part,
+                                 hs);
     if (he != hipSuccess) return fail(MAMBA_ERR_HIP, where, hipGetErrorString(he));
   }
   st = mamba_ssm_fwd(batch, seqlen, dim, dstate, dt_rank, io_dtype, x, z, W_x, W_dt, dt_bias, A, Dskip,

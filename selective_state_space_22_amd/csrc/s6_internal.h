@@ -191,6 +191,12 @@ hipError_t launch_selection(const SelArgs& s, int io, hipStream_t stream);
 size_t gemm_nt_part_bytes();
 hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int64_t lda,
                           int64_t ldb, int64_t ldc, int io, int act, float* part, hipStream_t stream);
+// Two products with a common A: C = act(A B[0:N1]^T) and C2 = A B[N1:N1+N2]^T (the rows
+// of B consecutive, C and C2 with row stride ldc), one launch where the large-product
+// kernel takes the pair, else two.
+hipError_t launch_gemm_nt_pair(const void* A, const void* B, void* C, void* C2, int64_t M, int64_t N1, int64_t N2,
+                               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int io, int act, float* part,
+                               hipStream_t stream);
 
 // Enqueue the kernels of one scan / one decode step on `stream`.
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);

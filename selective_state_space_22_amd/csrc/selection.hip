@@ -88,6 +88,11 @@ struct GemmArgs {
   // large-product kernel: one fp32 256 x 256 slot per workgroup for the halves of the
   // blocks of a last, at most half-filled round, split in K (null: no split)
   float* part = nullptr;
+  // large-product kernel: the output columns from n2 on (n2 a multiple of its block
+  // width) go to C2 instead, as columns 0 .. N - n2 - 1 with the same row stride and
+  // without the activation (null: every column to C)
+  void* C2 = nullptr;
+  int64_t n2 = 0;
 };
 
 // 128 x 128 output block per workgroup of 2 x 2 waves (4 x 4 tiles of 16 x 16
@@ -399,8 +404,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
 }
 
 // Large products (the block's input and output projections): 256 x 256 output
-// blocks of 8 waves, two per SIMD (one wave per SIMD cannot issue MFMAs fast enough
-// to keep its matrix core busy), each wave owning 128 x 64 (8 x 4 tiles of 16 x 16,
+// blocks of 8 waves, two per SIMD, each wave owning 128 x 64 (8 x 4 tiles of 16 x 16,
 // accumulators in AGPRs).  K advances in stages of 128 bytes per row, one cache
 // line: operands go from global memory straight into LDS with buffer loads that
 // carry the lds bit (lane i of a load writes the 16 bytes at 16 i of its 1 KB
@@ -477,6 +481,15 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
 
   const uint32_t kbytes = (uint32_t)(g.K * E);
   const int nst = (int)((kbytes + kBigStage - 1) / kBigStage);  // stages per block
+  // Each XCD takes the K stages in its own rotated order, starting at stage x nst / 8:
+  // the workgroups of one XCD keep one order (they share stages through its L2), while
+  // the XCDs, which share HBM and the Infinity Cache, do not all ask for the same
+  // columns of K at the same time.
+  const uint32_t krot = (uint32_t)((xcd * nst) / 8);
+  auto kstage = [&](int st) -> uint32_t {
+    const uint32_t v = (uint32_t)st + krot;
+    return v >= (uint32_t)nst ? v - (uint32_t)nst : v;
+  };
   // stages [s_begin, s_end) of item u: a half takes the first nh stages or the rest
   const int nh = (nst + 1) / 2;
   const int half_no = has_half ? (int)(jw / rem) : 0;
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
   auto dma_one = [&](int buf, int n) {
     const uint32_t m = (uint32_t)(n >> 1);
     const uint32_t ch = (m & 1) ? ch1 : ch0;
-    const uint32_t kb = (uint32_t)ds * kBigStage + ch;
+    const uint32_t kb = kstage(ds) * kBigStage + ch;
     // past K or past the last block: an offset past every row, read as zero
     const uint32_t cut = kb < kbytes && du < ntl ? 0u : kOutOfRange;
     const uint32_t r0 = (uint32_t)(32 * w) + 8u * m;  // first row of the load
@@ -583,14 +596,19 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
     const uint32_t lane_off = (uint32_t)r16 * ldcB + (uint32_t)(4 * q * (int)sizeof(OUT));
     int64_t bm0, bn0;
     origin(u, bm0, bn0);
-    const int64_t m0 = bm0 + wm * 128, n0 = bn0 + wn * 64;
+    // the block's output: its columns of C, or of C2 past n2
+    const bool second = g.C2 != nullptr && bn0 >= g.n2;
+    OUT* const cb = second ? static_cast<OUT*>(g.C2) : cbase;
+    const int64_t ncols = second ? g.N - g.n2 : (g.C2 != nullptr ? g.n2 : g.N);
+    const bool act = g.act != 0 && !second;
+    const int64_t m0 = bm0 + wm * 128, n0 = (second ? bn0 - g.n2 : bn0) + wn * 64;
     const int64_t wrows = g.M - m0 < 128 ? (g.M - m0 > 0 ? g.M - m0 : 0) : 128;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(
-        cbase + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + g.N) * sizeof(OUT) : 0));
+        cb + (wrows > 0 ? m0 : 0) * g.ldc, (uint32_t)(wrows > 0 ? ((wrows - 1) * g.ldc + ncols) * sizeof(OUT) : 0));
     // the last MFMAs' results must be written before the accumulators are read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     const int wr = (int)wrows;                     // rows of this wave's part inside M
-    const int cl = (int)(g.N - n0) - 4 * q;        // columns left for this lane's segments
+    const int cl = (int)(ncols - n0) - 4 * q;      // columns left for this lane's segments
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const bool row_ok = 16 * i + r16 < wr;
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(kBigThreads) void gemm_nt_big_kernel(GemmArgs g) {
         const uint32_t off = lane_off + (uint32_t)(16 * i) * ldcB + (uint32_t)((n0 + 16 * j) * (int64_t)sizeof(OUT));
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = g.act ? silu(acc[i][j][r]) : acc[i][j][r];
+        for (int r = 0; r < 4; ++r) v[r] = act ? silu(acc[i][j][r]) : acc[i][j][r];
         // N and ldc are multiples of 4 and C is aligned to a segment (see big_ok)
         const uint32_t o = row_ok && 16 * j < cl ? off : kOutOfRange;
         if constexpr (sizeof(OUT) == 2) {
@@ -730,17 +748,21 @@ __global__ __launch_bounds__(256) void big_fixup_kernel(GemmArgs g, int64_t grid
   const int64_t in_grp = t - grp * kGroup * nbn;
   const int64_t bm0 = (grp * kGroup + in_grp % rows_in_grp) * kBigBM;
   const int64_t bn0 = (in_grp / rows_in_grp) * kBigBM;
+  const bool second = g.C2 != nullptr && bn0 >= g.n2;  // columns past n2 go to C2
+  const int64_t ncols = second ? g.N - g.n2 : (g.C2 != nullptr ? g.n2 : g.N);
+  const int64_t cn0 = second ? bn0 - g.n2 : bn0;
+  const bool act = g.act != 0 && !second;
   const float4* p0 = reinterpret_cast<const float4*>(g.part + (size_t)(8 * r + xcd) * kBigBM * kBigBM);
   const float4* p1 = reinterpret_cast<const float4*>(g.part + (size_t)(8 * (r + rem) + xcd) * kBigBM * kBigBM);
-  OUT* c = static_cast<OUT*>(g.C);
+  OUT* c = static_cast<OUT*>(second ? g.C2 : g.C);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = (int)strip * 16 * (kBigBM / 4) + k * 256 + (int)threadIdx.x;  // float4 index in the block
-    const int64_t row = bm0 + e / (kBigBM / 4), col = bn0 + (e % (kBigBM / 4)) * 4;
-    if (row >= g.M || col >= g.N) continue;
+    const int64_t row = bm0 + e / (kBigBM / 4), col = cn0 + (e % (kBigBM / 4)) * 4;
+    if (row >= g.M || col >= ncols) continue;
     const float4 x = p0[e], y = p1[e];
     float v[4] = {x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w};
-    if (g.act)
+    if (act)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = silu(v[i]);
     OUT* dst = c + row * g.ldc + col;
@@ -840,7 +862,10 @@ bool big_ok(const GemmArgs& g, size_t out_bytes) {
   const bool offsets = 256 * g.lda * e + g.K * e < (int64_t)kOutOfRange && 256 * g.ldb * e + g.K * e < (int64_t)kOutOfRange;
   // each lane stores 4 consecutive outputs of a row as one aligned segment
   const bool segments = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % (4 * out_bytes) == 0;
-  return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && segments &&
+  // a second output starts at a block edge and is aligned like the first
+  const bool second = g.C2 == nullptr ||
+                      (g.n2 > 0 && g.n2 < g.N && g.n2 % kBigBM == 0 && reinterpret_cast<uintptr_t>(g.C2) % (4 * out_bytes) == 0);
+  return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && segments && second &&
          std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr;
 }
 
@@ -867,6 +892,7 @@ hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
     }
     return hipGetLastError();
   }
+  if (g.C2 != nullptr) return hipErrorInvalidValue;  // only the large-product kernel routes columns
   const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
   if (mfma_ok<IN>(g) && parts == 1 && ks <= kShortMaxSlices && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr)
     return gemm_nt_short<IN, OUT>(g, ks, st);
@@ -939,6 +965,33 @@ hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int64_t M, int6
   g.act = act;
   g.part = part;
   return io == kIoBF16 ? gemm_nt<uint16_t, uint16_t>(g, st) : gemm_nt<float, float>(g, st);
+}
+
+template <typename IO>
+hipError_t gemm_nt_pair_t(const GemmArgs& g, hipStream_t st) {
+  if (mfma_ok<IO>(g) && big_ok<IO>(g, sizeof(IO))) return gemm_nt<IO, IO>(g, st);
+  // two launches: the first n2 rows of B into C, the rest into C2
+  GemmArgs g1 = g, g2 = g;
+  g1.C2 = g2.C2 = nullptr;
+  g1.N = g.n2;
+  g2.B = static_cast<const IO*>(g.B) + g.n2 * g.ldb;
+  g2.C = g.C2;
+  g2.N = g.N - g.n2;
+  g2.act = 0;
+  hipError_t e = gemm_nt<IO, IO>(g1, st);
+  return e == hipSuccess ? gemm_nt<IO, IO>(g2, st) : e;
+}
+
+hipError_t launch_gemm_nt_pair(const void* A, const void* B, void* C, void* C2, int64_t M, int64_t N1, int64_t N2,
+                               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int io, int act, float* part,
+                               hipStream_t st) {
+  if (N1 <= 0 || N2 <= 0) return hipErrorInvalidValue;
+  GemmArgs g{A, B, C, M, N1 + N2, K, lda, ldb, ldc};
+  g.act = act;
+  g.part = part;
+  g.C2 = C2;
+  g.n2 = N1;
+  return io == kIoBF16 ? gemm_nt_pair_t<uint16_t>(g, st) : gemm_nt_pair_t<float>(g, st);
 }
 
 }  // namespace s6

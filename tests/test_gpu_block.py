@@ -54,6 +54,8 @@ def _gpu_block(inp, sw, bw, hidden, io, h0=None):
     (2, 600, 520, 1040, 8, 66, "f32"),
     (2, 520, 512, 1036, 16, 66, "bf16"),  # large-block input projection, output rows 8-byte but not 16-byte aligned
     (2, 520, 512, 1034, 8, 66, "bf16"),   # D not a multiple of 4: input projection on the general kernel
+    (2, 600, 256, 1024, 8, 66, "f32"),    # both input-projection halves in one launch
+    (2, 3800, 512, 1280, 16, 66, "bf16"),  # one launch, ragged rows, split last round with x and z blocks
 ], ids=str)
 def test_block_matches_oracle(case):
     _need_gpu()
