@@ -347,7 +347,9 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
     h[s] = 0.0f;
     q[s] = 0.0f;
   }
-  float csum = 0.0f, ccomp = 0.0f;  // compensated running sum of dt (identical in every wave)
+  // running sum of dt (identical in every wave): the tile's dt summed plainly, then
+  // added to the chunk's sum with compensation (one Kahan step per tile)
+  float csum = 0.0f, ccomp = 0.0f;
 
   typename K::Raw r;
   auto front = [&](int kt, int slot) {
@@ -377,6 +379,7 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
       p[s] = ex2(k.a2[s] * cs);  // product of Abar over the chunk so far, re-anchored per tile
     }
     if (k.w == 0) stf(cs, r_cdt, dv ? (uint32_t)kt * (uint32_t)(a.D * 4) + dbytes : kOutOfRange);
+    float tsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       const float4 fv = fr[slot][j][k.lane];
@@ -391,7 +394,10 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
         p[s] *= ab;
         q[s] = __builtin_fmaf(p[s], fv.w * bcs[S + s], q[s]);
       }
-      const float yk = fv.x - ccomp;
+      tsum += fv.x;
+    }
+    {
+      const float yk = tsum - ccomp;
       const float tk = csum + yk;
       ccomp = (tk - csum) - yk;
       csum = tk;
