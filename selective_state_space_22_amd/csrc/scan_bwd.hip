@@ -548,7 +548,7 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
 
   // one tile: rebuild the start state, recompute the tile's states, reverse
   auto scan = [&](int kt, int slot, int eslot) {
-    float hh[T][S], ab[T][S], be[T][S];
+    float hh[T][S], ab[T][S], be[T][S], xx[T][S], bx[T][S];  // per element: h, Abar, beta, dt A log2(e), B x
     float hst[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) hst[s] = __builtin_fmaf(ex2(k.a2[s] * cdt), hs0[s], srel[s]);
@@ -562,11 +562,12 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
       float y = 0.0f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const float x2 = fv.x * k.a2[s];
-        ab[j][s] = ex2(x2);
-        be[j][s] = input_weight(ab[j][s], x2, fv.x, fv.y, k.ka[s], k.ah[s]);
+        xx[j][s] = fv.x * k.a2[s];
+        ab[j][s] = ex2(xx[j][s]);
+        be[j][s] = input_weight(ab[j][s], xx[j][s], fv.x, fv.y, k.ka[s], k.ah[s]);
+        bx[j][s] = bcs[s] * fv.z;
         const float hp = j == 0 ? hst[s] : hh[j - 1][s];
-        hh[j][s] = __builtin_fmaf(ab[j][s], hp, be[j][s] * (bcs[s] * fv.z));
+        hh[j][s] = __builtin_fmaf(ab[j][s], hp, be[j][s] * bx[j][s]);
         y = __builtin_fmaf(bcs[S + s], hh[j][s], y);
       }
       sm.ex[eslot][0][j][w][lane] = y;
@@ -587,13 +588,12 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
         const float gb = g[s] * be[j][s];
         red[(j * 2) * S + s] = gb * fv.z;               // dB contribution
         dxp = __builtin_fmaf(gb, Bv, dxp);
-        const float qq = g[s] * (Bv * fv.z);            // gradient at beta_t
+        const float qq = g[s] * bx[j][s];                // gradient at beta_t
         const float hp = j == 0 ? hst[s] : hh[j - 1][s];
         const float da = g[s] * hp;                      // gradient at Abar_t
         dtp = __builtin_fmaf(ab[j][s], __builtin_fmaf(da, k.av[s], qq), dtp);
-        const float x2 = fv.x * k.a2[s];
         dacc[s] = __builtin_fmaf(da * ab[j][s], fv.x, dacc[s]);
-        dacc[s] = __builtin_fmaf(qq, dbeta_dA(ab[j][s], be[j][s], x2, fv.x, fv.y, k.ka[s]), dacc[s]);
+        dacc[s] = __builtin_fmaf(qq, dbeta_dA(ab[j][s], be[j][s], xx[j][s], fv.x, fv.y, k.ka[s]), dacc[s]);
         g[s] *= ab[j][s];                                // gradient at h_{t-1} through h_t
       }
       sm.ex[eslot][1][j][w][lane] = dxp;
