@@ -247,7 +247,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_mfma_kernel(GemmArgs g) {
       const int64_t gcol = n0 + c0;
       float v[EPV];
 #pragma unroll
-      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][c0 + kk]) : st[row][c0 + kk];
+      for (int k4 = 0; k4 < EPV / 4; ++k4) {  // 16-byte reads (rows of 68 floats, 16-byte aligned)
+        const float4 f = *reinterpret_cast<const float4*>(&st[row][c0 + 4 * k4]);
+        v[4 * k4] = f.x;
+        v[4 * k4 + 1] = f.y;
+        v[4 * k4 + 2] = f.z;
+        v[4 * k4 + 3] = f.w;
+      }
+      if (g.act)
+#pragma unroll
+        for (int kk = 0; kk < EPV; ++kk) v[kk] = silu(v[kk]);
       if (vec_ok && gcol + EPV <= g.N) {
         const uint32_t off = (uint32_t)((grow * g.ldc + gcol) * sizeof(OUT));
         u32x4 pk;
@@ -335,8 +344,10 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
       }
   };
 
-  // output strip staging: 32 rows x 64 columns of fp32 per wave
-  __shared__ float stage[4][kShortRows][68];
+  // output strip staging: 32 rows x 64 columns of fp32 per wave; rows of 68 floats
+  // (16-byte aligned): the tile writes below hit 64 distinct banks, and the 16-byte
+  // read-back of 8 lanes (one row's 32-byte pieces) 32 distinct banks
+  __shared__ __attribute__((aligned(16))) float stage[4][kShortRows][68];
   float(*st)[68] = stage[w];
   const bool vec_ok = (g.ldc * sizeof(OUT)) % 16 == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15u) == 0;
   constexpr int EPV = 16 / sizeof(OUT);  // output elements per 16-byte store
@@ -374,7 +385,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_shortk_kernel(GemmArgs g, int 
       const int64_t gcol = n0 + cc;
       float v[EPV];
 #pragma unroll
-      for (int kk = 0; kk < EPV; ++kk) v[kk] = g.act ? silu(st[row][cc + kk]) : st[row][cc + kk];
+      for (int k4 = 0; k4 < EPV / 4; ++k4) {
+        const float4 f = *reinterpret_cast<const float4*>(&st[row][cc + 4 * k4]);
+        v[4 * k4] = f.x;
+        v[4 * k4 + 1] = f.y;
+        v[4 * k4 + 2] = f.z;
+        v[4 * k4 + 3] = f.w;
+      }
+      if (g.act)
+#pragma unroll
+        for (int kk = 0; kk < EPV; ++kk) v[kk] = silu(v[kk]);
       if (vec_ok && gcol + EPV <= g.N) {
         const uint32_t off = (uint32_t)((row * g.ldc + gcol) * sizeof(OUT));
         u32x4 pk;
