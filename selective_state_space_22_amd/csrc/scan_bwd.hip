@@ -657,6 +657,22 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- pass 4: reductions
 
+// sum_{k < n} p[k * stride] in the order k = 0, 1, ..., with eight loads in flight
+// at a time (a thread's loads are independent; only the adds are chained).
+__device__ __forceinline__ float strided_sum(const float* p, int64_t n, int64_t stride) {
+  float acc = 0.0f;
+  int64_t k = 0;
+  for (; k + 8 <= n; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; k < n; ++k) acc += p[(size_t)k * stride];
+  return acc;
+}
+
 template <typename IO, int N>
 __global__ void bwd_reduce_bc_kernel(BwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, q, n)
@@ -668,9 +684,7 @@ __global__ void bwd_reduce_bc_kernel(BwdArgs a) {
   const int64_t t = rest / (2 * N);
   const int q = (int)((rest / N) & 1);
   const int n = (int)(rest % N);
-  const float* p = a.pbc + (size_t)b * a.nblk * per_b + rest;
-  float acc = 0.0f;
-  for (int k = 0; k < a.nblk; ++k) acc += p[(size_t)k * per_b];
+  const float acc = strided_sum(a.pbc + (size_t)b * a.nblk * per_b + rest, a.nblk, per_b);
   IO* dst = static_cast<IO*>(q == 0 ? a.dB : a.dC);
   store_io(dst, (size_t)(b * a.L + t) * N + n, acc);
 }
@@ -681,16 +695,11 @@ __global__ void bwd_reduce_param_kernel(BwdArgs a) {
   const int64_t nbg = a.batch * a.nchunks;
   if (i < (int64_t)N * a.D) {
     const int64_t n = i / a.D, d = i % a.D;
-    float acc = 0.0f;
-    for (int64_t k = 0; k < nbg; ++k) acc += a.pA[(size_t)(k * N + n) * a.D + d];
-    a.dA[d * N + n] = acc;
+    a.dA[d * N + n] = strided_sum(a.pA + (size_t)n * a.D + d, nbg, (int64_t)N * a.D);
   } else if (i < (int64_t)N * a.D + a.D) {
     const int64_t d = i - (int64_t)N * a.D;
-    float s0 = 0.0f, s1 = 0.0f;
-    for (int64_t k = 0; k < nbg; ++k) {
-      s0 += a.pD[(size_t)(k * 2 + 0) * a.D + d];
-      s1 += a.pD[(size_t)(k * 2 + 1) * a.D + d];
-    }
+    const float s0 = strided_sum(a.pD + d, nbg, 2 * a.D);
+    const float s1 = strided_sum(a.pD + a.D + d, nbg, 2 * a.D);
     if (a.dDskip) a.dDskip[d] = s0;
     if (a.dbias) a.dbias[d] = s1;
   }
