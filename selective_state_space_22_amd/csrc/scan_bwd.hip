@@ -418,6 +418,8 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- pass 2: carries over chunks
 
+constexpr int kCarryBatch = 16;
+
 template <int N>
 __global__ void bwd_carry_kernel(BwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, n, d), d fastest
@@ -428,21 +430,43 @@ __global__ void bwd_carry_kernel(BwdArgs a) {
   const int64_t b = i / (a.D * N);
   const float a2 = a.A[d * N + n] * kLog2e;
   const int G = a.nchunks;
+  auto idx = [&](int c) { return ((size_t)(b * G + c) * N + n) * a.D + d; };
+  auto sdt = [&](int c) { return a.sdt[(size_t)(b * G + c) * a.D + d]; };
+  // Chunks in groups of kCarryBatch: the group's loads are issued together (they do
+  // not depend on the chain), then the chain runs through them in order.
   float hcur = a.h0 ? a.h0[(b * a.D + d) * N + n] : 0.0f;
-  for (int c = 0; c < G; ++c) {
-    const size_t idx = ((size_t)(b * G + c) * N + n) * a.D + d;
-    const float send = a.hs[idx];
-    const float P = ex2(a2 * a.sdt[(size_t)(b * G + c) * a.D + d]);
-    a.hs[idx] = hcur;  // state entering chunk c
-    hcur = __builtin_fmaf(P, hcur, send);
+  for (int c0 = 0; c0 < G; c0 += kCarryBatch) {
+    float sv[kCarryBatch], tv[kCarryBatch];
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u)
+      if (c0 + u < G) {
+        sv[u] = a.hs[idx(c0 + u)];
+        tv[u] = sdt(c0 + u);
+      }
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u)
+      if (c0 + u < G) {
+        const float P = ex2(a2 * tv[u]);
+        a.hs[idx(c0 + u)] = hcur;  // state entering chunk c
+        hcur = __builtin_fmaf(P, hcur, sv[u]);
+      }
   }
   float gcur = a.dlast ? a.dlast[(b * a.D + d) * N + n] : 0.0f;
-  for (int c = G - 1; c >= 0; --c) {
-    const size_t idx = ((size_t)(b * G + c) * N + n) * a.D + d;
-    const float qc = a.gq[idx];
-    const float P = ex2(a2 * a.sdt[(size_t)(b * G + c) * a.D + d]);
-    a.gq[idx] = gcur;  // gradient arriving at the end of chunk c from later tokens
-    gcur = __builtin_fmaf(P, gcur, qc);
+  for (int c0 = G - 1; c0 >= 0; c0 -= kCarryBatch) {
+    float qv[kCarryBatch], tv[kCarryBatch];
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u)
+      if (c0 - u >= 0) {
+        qv[u] = a.gq[idx(c0 - u)];
+        tv[u] = sdt(c0 - u);
+      }
+#pragma unroll
+    for (int u = 0; u < kCarryBatch; ++u)
+      if (c0 - u >= 0) {
+        const float P = ex2(a2 * tv[u]);
+        a.gq[idx(c0 - u)] = gcur;  // gradient arriving at the end of chunk c from later tokens
+        gcur = __builtin_fmaf(P, gcur, qv[u]);
+      }
   }
 }
 
@@ -689,19 +713,35 @@ __global__ void bwd_reduce_bc_kernel(BwdArgs a) {
   store_io(dst, (size_t)(b * a.L + t) * N + n, acc);
 }
 
+// The same sum over a wave: lane l takes k = l, l + 64, ... in order, then the 64 lane
+// sums are added pairwise in a fixed butterfly (every lane ends with the same total).
+__device__ __forceinline__ float wave_strided_sum(const float* p, int64_t n, int64_t stride, int lane) {
+  const int64_t cnt = n > lane ? (n - lane + 63) / 64 : 0;
+  float v = strided_sum(p + (size_t)lane * stride, cnt, 64 * stride);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per parameter gradient: (n, d) for dA, then d for dDskip and the dt bias.
+// Each sums batch x chunks partials (thousands for long sequences).
 template <int N>
-__global__ void bwd_reduce_param_kernel(BwdArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (n, d) for dA, then d for the vectors
+__global__ __launch_bounds__(256) void bwd_reduce_param_kernel(BwdArgs a) {
+  const int64_t o = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // wave-uniform
+  const int lane = threadIdx.x & 63;
   const int64_t nbg = a.batch * a.nchunks;
-  if (i < (int64_t)N * a.D) {
-    const int64_t n = i / a.D, d = i % a.D;
-    a.dA[d * N + n] = strided_sum(a.pA + (size_t)n * a.D + d, nbg, (int64_t)N * a.D);
-  } else if (i < (int64_t)N * a.D + a.D) {
-    const int64_t d = i - (int64_t)N * a.D;
-    const float s0 = strided_sum(a.pD + d, nbg, 2 * a.D);
-    const float s1 = strided_sum(a.pD + a.D + d, nbg, 2 * a.D);
-    if (a.dDskip) a.dDskip[d] = s0;
-    if (a.dbias) a.dbias[d] = s1;
+  if (o < (int64_t)N * a.D) {
+    const int64_t n = o / a.D, d = o % a.D;
+    const float s = wave_strided_sum(a.pA + (size_t)n * a.D + d, nbg, (int64_t)N * a.D, lane);
+    if (lane == 0) a.dA[d * N + n] = s;
+  } else if (o < (int64_t)N * a.D + a.D) {
+    const int64_t d = o - (int64_t)N * a.D;
+    const float s0 = wave_strided_sum(a.pD + d, nbg, 2 * a.D, lane);
+    const float s1 = wave_strided_sum(a.pD + a.D + d, nbg, 2 * a.D, lane);
+    if (lane == 0) {
+      if (a.dDskip) a.dDskip[d] = s0;
+      if (a.dbias) a.dbias[d] = s1;
+    }
   }
 }
 
@@ -734,7 +774,7 @@ hipError_t launch_bwd_t(const BwdArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL((bwd_main_kernel<IO, N, W, T>), dim3(items), dim3(64 * W), 0, st, a);
   hipLaunchKernelGGL((bwd_reduce_bc_kernel<IO, N>), dim3(blocks_for(a.batch * a.L * 2 * N, 256)), dim3(256), 0, st,
                      a);
-  hipLaunchKernelGGL((bwd_reduce_param_kernel<N>), dim3(blocks_for((int64_t)N * a.D + a.D, 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_reduce_param_kernel<N>), dim3(blocks_for(((int64_t)N * a.D + a.D) * 64, 256)), dim3(256), 0, st,
                      a);
   return hipGetLastError();
 }

@@ -106,12 +106,26 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs a) {
   const float a2 = a.A[d * N + n] * kLog2e;
   float carry = a.h0 ? a.h0[lane] : 0.0f;
   const int G = a.nchunks;
-  for (int g = 0; g < G - 1; ++g) {
-    const size_t base = ((size_t)b * G + g) * D + d;
-    const float decay = ex2(a2 * a.agg_s[base]);
-    const float bg = a.agg_h[base * N + n];
-    a.agg_h[base * N + n] = carry;
-    carry = __builtin_fmaf(decay, carry, bg);
+  // chunks in groups of 16: the group's loads are issued together (they do not depend
+  // on the chain), then the chain runs through them in order
+  constexpr int kBatch = 16;
+  for (int g0 = 0; g0 < G - 1; g0 += kBatch) {
+    float sv[kBatch], hv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (g0 + u < G - 1) {
+        const size_t base = ((size_t)b * G + g0 + u) * D + d;
+        sv[u] = a.agg_s[base];
+        hv[u] = a.agg_h[base * N + n];
+      }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (g0 + u < G - 1) {
+        const size_t base = ((size_t)b * G + g0 + u) * D + d;
+        const float decay = ex2(a2 * sv[u]);
+        a.agg_h[base * N + n] = carry;
+        carry = __builtin_fmaf(decay, carry, hv[u]);
+      }
   }
   a.agg_h[(((size_t)b * G + (G - 1)) * D + d) * N + n] = carry;
 }
