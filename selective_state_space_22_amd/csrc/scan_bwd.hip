@@ -418,10 +418,10 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- pass 2: carries over chunks
 
-constexpr int kCarryBatch = 16;
+constexpr int kCarryBatch = 32;
 
 template <int N>
-__global__ void bwd_carry_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_carry_kernel(BwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, n, d), d fastest
   const int64_t total = a.batch * N * a.D;
   if (i >= total) return;
