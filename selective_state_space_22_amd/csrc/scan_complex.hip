@@ -123,18 +123,34 @@ __global__ __launch_bounds__(256) void cplx_carry_kernel(CplxArgs c) {
   an.load(a.A[(d * N + n) * 2], a.A[(d * N + n) * 2 + 1]);
   float cr = a.h0 ? a.h0[lane * 2] : 0.0f, ci = a.h0 ? a.h0[lane * 2 + 1] : 0.0f;
   const int G = a.nchunks;
-  for (int g = 0; g < G - 1; ++g) {
-    const size_t base = ((size_t)b * G + g) * D + d;
-    float pr, pi;
-    cplx_decay(an, a.agg_s[base], pr, pi);
-    const size_t k = (base * N + n) * 2;
-    const float br = a.agg_h[k], bi = a.agg_h[k + 1];
-    a.agg_h[k] = cr;
-    a.agg_h[k + 1] = ci;
-    const float nr = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, br));
-    const float ni = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, bi));
-    cr = nr;
-    ci = ni;
+  // chunks in groups of 16: the group's loads are issued together (they do not depend
+  // on the chain), then the chain runs through them in order
+  constexpr int kBatch = 16;
+  for (int g0 = 0; g0 < G - 1; g0 += kBatch) {
+    float sv[kBatch], hr[kBatch], hi[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (g0 + u < G - 1) {
+        const size_t base = ((size_t)b * G + g0 + u) * D + d;
+        const size_t k = (base * N + n) * 2;
+        sv[u] = a.agg_s[base];
+        hr[u] = a.agg_h[k];
+        hi[u] = a.agg_h[k + 1];
+      }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (g0 + u < G - 1) {
+        const size_t base = ((size_t)b * G + g0 + u) * D + d;
+        float pr, pi;
+        cplx_decay(an, sv[u], pr, pi);
+        const size_t k = (base * N + n) * 2;
+        a.agg_h[k] = cr;
+        a.agg_h[k + 1] = ci;
+        const float nr = __builtin_fmaf(pr, cr, __builtin_fmaf(-pi, ci, hr[u]));
+        const float ni = __builtin_fmaf(pr, ci, __builtin_fmaf(pi, cr, hi[u]));
+        cr = nr;
+        ci = ni;
+      }
   }
   const size_t k = ((((size_t)b * G + (G - 1)) * D + d) * N + n) * 2;
   a.agg_h[k] = cr;
