@@ -173,8 +173,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the scan shards over batch and channels with no "
-              "exchange, which a single GPU cannot show); run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the scan shards over batch and channels with no "
+              "exchange; each GPU would run this kernel on its share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
