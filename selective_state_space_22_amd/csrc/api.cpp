@@ -2,6 +2,7 @@
 //
 // Every entry point validates its arguments on the host before it touches
 // the HIP runtime, then enqueues kernels on the caller's stream and returns.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -383,7 +384,8 @@ size_t mamba_ssm_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, 
   const size_t tok = (size_t)batch * seqlen;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   return al(tok * dim * e) + 2 * al(tok * dstate * e) + s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype) +
-         al(s6::plan_scan(batch, seqlen, dim, dstate).ws_bytes);
+         al(std::max(s6::plan_scan(batch, seqlen, dim, dstate).ws_bytes,
+                     s6::plan_scan_fused_dt(batch, seqlen, dim, dstate).ws_bytes));
 }
 
 int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int64_t dt_rank, int io_dtype,
@@ -421,14 +423,15 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
   void* xdbl = w + al(tok * dim * e) + 2 * al(tok * dstate * e);
   void* scan_ws = static_cast<uint8_t*>(xdbl) + s6::selection_ws_bytes(batch, seqlen, dt_rank, dstate, io_dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const s6::ScanPlan plan = s6::plan_scan(batch, seqlen, dim, dstate);
   // Opt-in (MAMBA_MI355X_FUSED_DT=1): the workgroup engine projects dt itself
   // on the matrix cores (no delta tensor).  Off by default: the scan is
   // VALU-bound and the extra per-tile work there costs about what the separate
   // dt projection GEMM does.
   const char* fenv = std::getenv("MAMBA_MI355X_FUSED_DT");
-  const bool fused = tokens && plan.engine == s6::kEngineWg && s6::fused_dt_supported(dstate, dt_rank, io_dtype) &&
+  const bool fused = tokens && s6::wg_supported(dstate) && s6::fused_dt_supported(dstate, dt_rank, io_dtype) &&
                      aligned16(W_dt) && fenv && fenv[0] == '1';
+  const s6::ScanPlan plan = fused ? s6::plan_scan_fused_dt(batch, seqlen, dim, dstate)
+                                  : s6::plan_scan(batch, seqlen, dim, dstate);
   if (tokens) {
     s6::SelArgs sa{x, W_x, W_dt, fused ? nullptr : delta, Bm, Cm, xdbl, batch, seqlen, dim, dstate, dt_rank,
                    s6::selection_ld(dt_rank, dstate)};

@@ -59,6 +59,7 @@ struct StepArgs {
 enum Engine {
   kEngineLane = 0,  // one lane owns all N states of a channel (any supported N)
   kEngineWg = 1,    // a workgroup owns 64 channels, its waves split the N states (N = 8, 16)
+  kEngineWp = 2,    // a workgroup owns 64 channels, each wave whole channels, two states per lane (N = 8, 16)
 };
 
 // Modes of the workgroup engine.
@@ -94,6 +95,8 @@ struct ScanPlan {
 };
 
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N);
+// Plan of a scan whose dt is projected inside the workgroup engine (ScanArgs::dtlow).
+ScanPlan plan_scan_fused_dt(int64_t batch, int64_t L, int64_t D, int64_t N);
 
 // Workgroup engine (scan_wg.hip).
 // cplx: complex A (A, h0, last and the carries hold (re, im) pairs), no fused dt projection.
@@ -102,6 +105,10 @@ hipError_t launch_scan_wg(const ScanArgs& a, const ScanPlan& p, int io, int N, v
 bool wg_supported(int64_t N);
 int wg_waves(int64_t N);
 int wg_tile(int64_t N);
+
+// Wave-private engine (scan_wp.hip): real A, N = 8 or 16, the workgroup engine's plans.
+hipError_t launch_scan_wp(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
+int wp_tile();
 
 bool dstate_supported(int64_t N);
 

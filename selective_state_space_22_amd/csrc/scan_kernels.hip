@@ -271,9 +271,58 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
 
 }  // namespace
 
+// Wave-private engine: one wave per (batch row, CW channels) for the whole
+// sequence; long sequences over few channels are cut into chunks (two passes)
+// until about 2.5 waves per SIMD result.
+constexpr int64_t kWpSplitBelow = 1024;   // waves of the unchunked scan below which L is cut
+constexpr int64_t kWpTargetWaves = 2560;  // waves the chunked scan aims for (2.5 per SIMD)
+
+ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  ScanPlan p{};
+  p.engine = kEngineWp;
+  p.waves = (int32_t)(N / 2);
+  const int64_t T = wp_tile();
+  const int64_t waves = batch * ((D + 63) / 64) * (N / 2);
+  const int64_t tiles = (L + T - 1) / T;
+  // A chunk's token rows (of u, delta, z, out and of B, C), plus the tiles the
+  // pipeline reads past its end (at most five), must span less than 2^31 bytes:
+  // buffer offsets are 32-bit and the out-of-range offset 2^31 must never wrap
+  // back into range.
+  int64_t cap = ((int64_t)0x7fffffff / ((D > N ? D : N) * 4) - 8 * T) / T * T;
+  if (cap < T) cap = T;
+  int64_t g = 1;
+  if (waves < kWpSplitBelow && tiles >= 8) {
+    g = (kWpTargetWaves + waves - 1) / waves;
+    if (g > tiles / 4) g = tiles / 4;
+    if (g < 2) g = 2;
+  }
+  int64_t chunk = (L + g - 1) / g;
+  chunk = ((chunk + T - 1) / T) * T;
+  if (chunk > cap) chunk = cap;
+  if (chunk >= L) chunk = L;
+  p.chunk_len = chunk;
+  p.nchunks = (int32_t)((L + chunk - 1) / chunk);
+  p.split = p.nchunks > 1;
+  p.ws_ctrl = 0;
+  p.ws_bytes = p.split ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) : 0;
+  return p;
+}
+
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
-  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0)
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0) {
+    // Long sequences over few channel blocks (two passes over chunks) run faster
+    // on the workgroup engine, whose waves load whole 128-byte lines of a token row.
+    if (env_int("MAMBA_MI355X_WG_ENGINE", 0) == 0) {
+      const ScanPlan p = plan_wp(batch, L, D, N);
+      if (!p.split) return p;
+    }
     return plan_wg(batch, L, D, N);
+  }
+  return plan_lane(batch, L, D, N);
+}
+
+ScanPlan plan_scan_fused_dt(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0) return plan_wg(batch, L, D, N);
   return plan_lane(batch, L, D, N);
 }
 
@@ -341,6 +390,7 @@ hipError_t launch_scan(const ScanArgs& in, const ScanPlan& p, int io, int N, voi
   ScanArgs a = in;
   a.chunk_len = p.chunk_len;
   a.nchunks = p.nchunks;
+  if (p.engine == kEngineWp) return a.dtlow ? hipErrorInvalidValue : launch_scan_wp(a, p, io, N, workspace, s);
   if (p.engine == kEngineWg) return launch_scan_wg(a, p, io, N, workspace, s);
   a.agg_h = static_cast<float*>(workspace);
   a.agg_s = p.ws_bytes > 0 ? a.agg_h + (size_t)a.batch * p.nchunks * a.D * N : nullptr;

@@ -286,7 +286,10 @@ struct WgScan {
   };
 
   __device__ __forceinline__ void read_tok(Tok& t, int f3, int j) const {
+    // a 16-byte read although the scan uses three components: a 12-byte LDS
+    // read costs about twice the cycles of a 16-byte one on gfx950 (measured)
     t.fv = sm.fr[f3][j][lane];
+    asm volatile("" : "+v"(t.fv.w));
 #pragma unroll
     for (int q = 0; q < BCW; q += 4) {
       const float4 v4 = *reinterpret_cast<const float4*>(&sm.bc[f3][j][w][q]);

@@ -1,0 +1,579 @@
+// scan_wp.hip -- wave-private forward selective scan on gfx950 (real diagonal A).
+//
+// One wave owns CW = 64 / P whole channels of one batch row for a whole
+// sequence (or one chunk of it): the P = N / 2 lanes of a channel hold two of
+// its states each (lane l: channel l / P of the wave, states 2 (l % P) and
+// 2 (l % P) + 1), so the wave never waits for another wave.  Everything it needs
+// for a tile of T tokens goes through its own LDS, in program order:
+//   front    lane l computes dt = softplus(raw + bias), dt^2, x and z for the
+//            T / P tokens l / CW + P i of channel l % CW into the fr slot; the
+//            B_t / C_t elements it loaded (shared by all channels:
+//            "Mamba 状态空间模型原理与 Transformer 对比", section 3.2) go to the bc
+//            slot as (B, B, C, C) per token and state pair;
+//   scan     every lane advances its two states over the tile (section 2.1
+//            eq. (2) discretisation, eq. (3a) recurrence) and writes its partial
+//            readout C_t,2g h_t,2g + C_t,2g+1 h_t,2g+1 (eq. (3b)) to yp;
+//   epilogue lane l sums the P partials of its tokens in state order, adds
+//            Dskip x, multiplies by SiLU(z) and makes one store per (token, channel).
+// The expanded (batch, L, D, N) state never leaves VGPRs (section 4.1).
+//
+// A workgroup is one wave.  Its LDS (12 KB for N = 16) lets about ten waves
+// share a CU, which is what hides the latencies of the per-token chains
+// (exp, select, recurrence FMA) and of LDS.  The P waves of a 64-channel block
+// read and write the same 128-byte lines of every token row; workgroup ids are
+// mapped so that they run on one XCD (ids are dealt to the XCDs in turn) and
+// share its L2.
+//
+// Sequences too long for the number of channel blocks to fill the GPU are cut
+// into chunks processed in two passes (the parallel scan over chunks of
+// section 4.1): chunk end states from zero with the chunk's sum of dt, a carry
+// pass composing them (the chunk's product of Abar is e^{A sum dt} because A
+// does not vary in time), then every chunk again from its exact carry-in.
+// Global loads run two tiles ahead through bounds-checked buffer resources based
+// at the chunk, so tails need no branches.
+#include <utility>
+
+#include "s6_device.h"
+#include "s6_internal.h"
+
+namespace s6 {
+namespace {
+
+#ifndef S6_WP_TILE
+#define S6_WP_TILE 16  // tokens per tile (N = 8)
+#endif
+#ifndef S6_WP_TILE16
+#define S6_WP_TILE16 16  // tokens per tile (N = 16)
+#endif
+#ifndef S6_WP_BATCH
+#define S6_WP_BATCH 2  // tokens whose input terms are computed together in the scan
+#endif
+#ifndef S6_WP_TREE
+#define S6_WP_TREE 0  // 1: pairwise sum of the partial readouts
+#endif
+#ifndef S6_WP_WGW
+#define S6_WP_WGW 1  // waves per workgroup (a divisor of N / 2); each owns its channels
+#endif
+#ifndef S6_WP_LDAUX
+#define S6_WP_LDAUX 0  // cache policy bits of the per-token row loads
+#endif
+#ifndef S6_WP_STAUX
+#define S6_WP_STAUX 0  // cache policy bits of the output stores
+#endif
+#ifndef S6_WP_PD
+#define S6_WP_PD 4  // tiles of global loads in flight per wave (N = 16)
+#endif
+#ifndef S6_WP_WPE
+#define S6_WP_WPE 3  // occupancy hint: waves per SIMD
+#endif
+
+constexpr int32_t kWpBufferDword3 = 0x00020000;  // raw (untyped) buffer access on the gfx9 family
+constexpr uint32_t kWpOutOfRange = 0x80000000u;  // offset beyond every buffer: loads 0, stores dropped
+
+// Passes of the wave-private engine.
+enum WpMode { kWpFull = 0, kWpAgg = 1, kWpOut = 2 };
+
+struct WpArgs {
+  ScanArgs s;
+  int32_t nblk;   // 64-channel blocks per batch row
+  int32_t units;  // (chunk, batch row, block) units of this launch
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wp_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kWpBufferDword3);
+}
+
+// A 16-byte LDS read whose fourth component the caller does not use: the empty
+// asm keeps the compiler from narrowing it to a 12-byte read, which costs about
+// twice the LDS cycles of a 16-byte one on gfx950 (measured).
+#ifndef S6_WP_READ16
+#define S6_WP_READ16 0
+#endif
+__device__ __forceinline__ float4 lds_read16(const float4* p) {
+  float4 v = *p;
+  if (S6_WP_READ16) asm volatile("" : "+v"(v.w));
+  return v;
+}
+
+// Orders this wave's LDS accesses across the phases of a tile: its lanes
+// exchange data through LDS, which serves one wave's accesses in order, so only
+// the compiler has to be kept from moving them.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename IO>
+struct WpIo;
+template <>
+struct WpIo<uint16_t> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, S6_WP_LDAUX);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw << 16); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, S6_WP_STAUX);
+  }
+};
+template <>
+struct WpIo<float> {
+  static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, S6_WP_LDAUX);
+  }
+  static __device__ __forceinline__ float widen(uint32_t raw) { return __uint_as_float(raw); }
+  static __device__ __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, S6_WP_STAUX);
+  }
+};
+
+typedef unsigned int wp_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int wp_u32x4 __attribute__((ext_vector_type(4)));
+
+// K consecutive dwords at byte offset off (buffer loads of 4, 8 or 16 bytes).
+template <int K>
+__device__ __forceinline__ void load_dwords(uint32_t (&w)[K], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (K == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (K == 2) {
+    const wp_u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+    static_assert(K % 4 == 0, "B/C staging width");
+#pragma unroll
+    for (int q = 0; q < K; q += 4) {
+      const wp_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * (q / 4), 0, 0);
+      w[q] = v.x;
+      w[q + 1] = v.y;
+      w[q + 2] = v.z;
+      w[q + 3] = v.w;
+    }
+  }
+}
+
+template <typename IO, int N, int T, int MODE, bool SP>
+struct WpScan {
+  static constexpr int S = 2;            // states per lane
+  static constexpr int P = N / S;        // lanes per channel = waves per 64-channel block
+  static constexpr int CW = 64 / P;      // channels per wave
+  static constexpr int TQ = T / P;       // front-end / epilogue tokens per lane per tile
+  static constexpr int NQ = T * P / 64;  // (token, state pair) B/C chunks staged per lane per tile
+  static constexpr uint32_t kIo = sizeof(IO);
+  static constexpr int DPC = 2 * (int)kIo / 4;  // dwords of B (or C) per chunk: a state pair
+  static_assert(N % S == 0 && T % P == 0 && (T * P) % 64 == 0 && T % 2 == 0, "tile shape");
+  // the phases of a tile need at least two parts: the epilogue of a part reads
+  // partial readouts that the scan of the next part leaves alone
+  static_assert(T / P >= 2, "at least two token slots per lane and tile");
+  static_assert(P == 8 || P == 4, "partial-readout layout");
+  static constexpr bool kOut = MODE != kWpAgg;
+  // Partial readouts of one token: P floats per channel.  For P = 8 the two
+  // 16-byte halves of a channel are swapped for channels 4..7 and rows are 96
+  // floats apart, so that the epilogue's 16-byte reads (lane = channel, eight
+  // or sixteen lanes per LDS cycle) and the scan's 4-byte writes touch distinct
+  // banks.
+  static constexpr int YS = P == 8 ? 96 : 64;
+  static __device__ __forceinline__ int ypos(int c, int g) {
+    if constexpr (P == 8) return 4 * (2 * c + ((g >> 2) ^ ((c >> 2) & 1))) + (g & 3);
+    return 4 * c + g;
+  }
+
+  struct Lds {
+    float4 fr[2][T][CW];             // (dt, dt^2, x, z) per (token, channel)
+    float4 bc[2][T][P];              // (B_2g, B_2g+1, C_2g, C_2g+1) per (token, state pair g)
+    float yp[kOut ? T : 1][YS];      // partial readouts per token (layout: ypos)
+    float sdt[MODE == kWpAgg ? 64 : 1];  // chunk sums of dt per lane
+  };
+
+  struct Regs {  // raw prefetched global data of one tile
+    uint32_t dl[TQ], uu[TQ], zz[TQ];
+    uint32_t bw[NQ][DPC], cw[NQ][DPC];
+  };
+
+  const WpArgs& A;
+  Lds& sm;
+  const int lane;
+  const int sc, sg;  // scan lane: channel within the wave, state pair
+  const int fc, fq;  // front / epilogue lane: channel within the wave, first token in the tile
+  int64_t b, t0, t1;
+  int g;
+  int64_t dscan, dfront;
+  uint32_t chan_off;  // byte offset of the front lane's channel in a token row (out of range if >= D)
+  uint32_t row_bytes, out_off;  // token row in bytes; this lane's offset in the output (out of range if >= D)
+  __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_out, r_B, r_C;
+  float a2[S], ka[S], ah[S], h[S];
+  float bias, dskip;
+  float dsum, dcomp;  // compensated sum of dt (first pass of the split scan)
+
+  __device__ WpScan(const WpArgs& a, Lds& s)
+      : A(a),
+        sm(s),
+        lane(threadIdx.x & 63),
+        sc((threadIdx.x & 63) / P),
+        sg((threadIdx.x & 63) % P),
+        fc((threadIdx.x & 63) % CW),
+        fq((threadIdx.x & 63) / CW) {}
+
+  __device__ __forceinline__ int tile_valid(int k) const {
+    const int64_t tk = t0 + (int64_t)k * T;
+    const int64_t r = t1 - tk;
+    return r <= 0 ? 0 : (r >= T ? T : (int)r);
+  }
+
+  // Global loads of tile k (rows past the chunk and channels past D read zero).
+  // B / C: lane l stages the chunks NQ l + q of the tile, chunk = (token, state
+  // pair), i.e. the state pair's two elements, contiguous in memory.
+  __device__ __forceinline__ void load(Regs& r, int k) const {
+    const uint32_t row = (uint32_t)(A.s.D * kIo);
+    const uint32_t base = chan_off + (uint32_t)(k * T + fq) * row;
+#pragma unroll
+    for (int i = 0; i < TQ; ++i) {
+      const uint32_t off = base + (uint32_t)(P * i) * row;
+      r.dl[i] = WpIo<IO>::load(r_dl, off);
+      r.uu[i] = WpIo<IO>::load(r_u, off);
+      if (kOut) r.zz[i] = WpIo<IO>::load(r_z, off);
+    }
+    // this lane's NQ chunks are consecutive (chunks NQ l .. NQ l + NQ - 1): one load per tensor
+    {
+      uint32_t bw[NQ * DPC], cw[NQ * DPC];
+      const uint32_t boff = (uint32_t)(k * T * N + 2 * NQ * lane) * kIo;
+      load_dwords<NQ * DPC>(bw, r_B, boff);
+      if (kOut) load_dwords<NQ * DPC>(cw, r_C, boff);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) {
+          r.bw[q][e] = bw[q * DPC + e];
+          if (kOut) r.cw[q][e] = cw[q * DPC + e];
+        }
+    }
+  }
+
+  // Front end of token slot i (token fq + P i) of tile k into slot f.
+  __device__ __forceinline__ void front_part(const Regs& r, int k, int f, int i) {
+    const int j = fq + P * i;
+    const float x = WpIo<IO>::widen(r.uu[i]);
+    const float raw = WpIo<IO>::widen(r.dl[i]) + bias;
+    const float dt = SP ? softplus(raw) : raw;
+    sm.fr[f][j][fc] = make_float4(dt, dt * dt, x, kOut ? WpIo<IO>::widen(r.zz[i]) : 0.0f);
+    if (MODE == kWpAgg) {  // Kahan sum of dt over this lane's valid tokens
+      const float yk = (j < tile_valid(k) ? dt : 0.0f) - dcomp;
+      const float tk = dsum + yk;
+      dcomp = (tk - dsum) - yk;
+      dsum = tk;
+    }
+  }
+
+  // B / C of a tile into slot f as (B, B, C, C) per (token, state pair).
+  __device__ __forceinline__ void stage_bc(const Regs& r, int f) {
+    float4* bc = &sm.bc[f][0][0];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float b0, b1, c0 = 0.0f, c1 = 0.0f;
+      if constexpr (kIo == 2) {
+        b0 = bf16_lo(r.bw[q][0]);
+        b1 = bf16_hi(r.bw[q][0]);
+        if (kOut) {
+          c0 = bf16_lo(r.cw[q][0]);
+          c1 = bf16_hi(r.cw[q][0]);
+        }
+      } else {
+        b0 = __uint_as_float(r.bw[q][0]);
+        b1 = __uint_as_float(r.bw[q][1]);
+        if (kOut) {
+          c0 = __uint_as_float(r.cw[q][0]);
+          c1 = __uint_as_float(r.cw[q][1]);
+        }
+      }
+      bc[NQ * lane + q] = make_float4(b0, b1, c0, c1);
+    }
+  }
+
+  // BT tokens at a time: their input terms (Abar, beta B x) first, then the
+  // recurrence steps and partial readouts, so a wave has independent work in flight.
+  template <int BT>
+  __device__ __forceinline__ void stepb(const float4 (&fv)[BT], const float4 (&bv)[BT], int j) {
+    float ab[BT][S], in[BT][S];
+#pragma unroll
+    for (int q = 0; q < BT; ++q)
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const float x2 = fv[q].x * a2[s];
+        ab[q][s] = ex2(x2);
+        const float beta = input_weight(ab[q][s], x2, fv[q].x, fv[q].y, ka[s], ah[s]);
+        in[q][s] = beta * ((s == 0 ? bv[q].x : bv[q].y) * fv[q].z);
+      }
+#pragma unroll
+    for (int q = 0; q < BT; ++q) {
+      h[0] = __builtin_fmaf(ab[q][0], h[0], in[q][0]);
+      h[1] = __builtin_fmaf(ab[q][1], h[1], in[q][1]);
+      if (kOut) sm.yp[j + q][ypos(sc, sg)] = __builtin_fmaf(bv[q].w, h[1], bv[q].z * h[0]);
+    }
+  }
+
+  __device__ __forceinline__ void step1(const float4& fv, const float4& bv, int j) {
+    float y = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float x2 = fv.x * a2[s];
+      const float abar = ex2(x2);
+      const float beta = input_weight(abar, x2, fv.x, fv.y, ka[s], ah[s]);
+      h[s] = __builtin_fmaf(abar, h[s], beta * ((s == 0 ? bv.x : bv.y) * fv.z));
+      y = s == 0 ? bv.z * h[0] : __builtin_fmaf(bv.w, h[1], y);
+    }
+    if (kOut) sm.yp[j][ypos(sc, sg)] = y;
+  }
+
+  // Recurrence over rows [P p, P p + P) of a full tile in slot f; partial readouts to yp.
+  __device__ __forceinline__ void scan_part(int f, int p) {
+    constexpr int BT = S6_WP_BATCH;
+    static_assert(P % BT == 0, "scan batch");
+    const int j0 = P * p;
+    float4 fv[BT], bv[BT], fn[BT], bn[BT];
+#pragma unroll
+    for (int q = 0; q < BT; ++q) {
+      fv[q] = lds_read16(&sm.fr[f][j0 + q][sc]);
+      bv[q] = sm.bc[f][j0 + q][sg];
+    }
+#pragma unroll
+    for (int j = j0; j < j0 + P; j += BT) {
+      if (j + BT < j0 + P) {
+#pragma unroll
+        for (int q = 0; q < BT; ++q) {
+          fn[q] = lds_read16(&sm.fr[f][j + BT + q][sc]);
+          bn[q] = sm.bc[f][j + BT + q][sg];
+        }
+      }
+      stepb<BT>(fv, bv, j);
+      if (j + BT < j0 + P) {
+#pragma unroll
+        for (int q = 0; q < BT; ++q) {
+          fv[q] = fn[q];
+          bv[q] = bn[q];
+        }
+      }
+    }
+  }
+
+  // The same rows of a partial tile with nv valid tokens.
+  __device__ __forceinline__ void scan_part_tail(int f, int p, int nv) {
+    const int j1 = P * p + P < nv ? P * p + P : nv;
+    for (int j = P * p; j < j1; ++j) step1(lds_read16(&sm.fr[f][j][sc]), sm.bc[f][j][sg], j);
+  }
+
+  // Readout sum, skip, gate and store of token slot i (token fq + P i) of tile k
+  // (rows past the chunk and channels past D fall outside the output buffer).
+  __device__ __forceinline__ void epi_part(int k, int f, int i) {
+    if (!kOut) return;
+    const int j = fq + P * i;
+    const float4* row = reinterpret_cast<const float4*>(&sm.yp[j][0]);
+    const float4 lo = row[ypos(fc, 0) / 4];
+    float y = ((lo.x + lo.y) + lo.z) + lo.w;  // the P partials in state order
+    if constexpr (P == 8) {
+      const float4 hi = row[ypos(fc, 4) / 4];
+      y = (((y + hi.x) + hi.y) + hi.z) + hi.w;
+    }
+    const float4 fv = lds_read16(&sm.fr[f][j][fc]);
+    const float o = s6::epilogue(y, fv.z, dskip, A.s.z != nullptr, fv.w);
+    WpIo<IO>::store(o, r_out, out_off + (uint32_t)(k * T + P * i) * row_bytes);
+  }
+
+  // Raw global data of PD tiles is in flight per wave (a ring of registers): the
+  // loads must cover the HBM latency, and a wave's requests are small (16-byte
+  // pieces of token rows), so only many in flight at once keep HBM busy.
+  static constexpr int PD = N == 16 ? S6_WP_PD : 2;
+
+  // One tile k (full when FULL, else nv valid tokens) with the front end of tile
+  // k+1 (raw data in ring slot RS) and the epilogue of tile k-1's last rows,
+  // phased so that every LDS round trip has other work between its write and
+  // its read: for each part p of P rows, scan(k, p); epilogue of the part before
+  // (tile k-1's last part when p = 0); front end of tile k+1's part p.  Then the
+  // slot is refilled with tile k+1+PD.
+  template <bool FULL, int RS>
+  __device__ __forceinline__ void tile(Regs (&ring)[PD], int k, int nv) {
+    const int f = k & 1;
+    Regs& r = ring[RS];
+#pragma unroll
+    for (int p = 0; p < TQ; ++p) {
+      wave_lds_order();
+      if (FULL) scan_part(f, p);
+      else scan_part_tail(f, p, nv);
+      wave_lds_order();
+      if (p == 0) {
+        if (k > 0) epi_part(k - 1, f ^ 1, TQ - 1);
+      } else {
+        epi_part(k, f, p - 1);
+      }
+      wave_lds_order();
+      front_part(r, k + 1, f ^ 1, p);
+      if (p == 0) stage_bc(r, f ^ 1);
+    }
+    load(r, k + 1 + PD);
+  }
+
+  // PD consecutive full tiles from k (a multiple of PD): tile k+i reads ring slot (i+1) % PD.
+  template <int... I>
+  __device__ __forceinline__ void tiles_full(Regs (&ring)[PD], int k, std::integer_sequence<int, I...>) {
+    (tile<true, (I + 1) % PD>(ring, k + I, T), ...);
+  }
+  // The rem <= PD tiles from k, full or not.
+  template <int... I>
+  __device__ __forceinline__ void tiles_tail(Regs (&ring)[PD], int k, int rem, std::integer_sequence<int, I...>) {
+    ((rem > I ? tile<false, (I + 1) % PD>(ring, k + I, tile_valid(k + I)) : void()), ...);
+  }
+
+  // This lane's two states from / to p, the first of them in a state array.
+  __device__ __forceinline__ void get_state(const float* p) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    h[0] = v.x;
+    h[1] = v.y;
+  }
+  __device__ __forceinline__ void put_state(float* p) const {
+    *reinterpret_cast<float2*>(p) = make_float2(h[0], h[1]);
+  }
+
+  // unit: (chunk, batch row, 64-channel block) in that order of significance; kw: wave of the block
+  __device__ void run(int unit, int kw) {
+    const int G = A.s.nchunks;
+    const int nb = A.nblk;
+    g = MODE == kWpFull ? 0 : unit / (int)(A.s.batch * nb);
+    b = (unit / nb) % A.s.batch;
+    const int64_t d0 = (int64_t)(unit % nb) * 64 + CW * kw;
+    dscan = d0 + sc;
+    dfront = d0 + fc;
+    const bool svalid = dscan < A.s.D, fvalid = dfront < A.s.D;
+    t0 = (int64_t)g * A.s.chunk_len;
+    t1 = t0 + A.s.chunk_len < A.s.L ? t0 + A.s.chunk_len : A.s.L;
+    chan_off = fvalid ? (uint32_t)(dfront * kIo) : kWpOutOfRange;
+    row_bytes = (uint32_t)(A.s.D * kIo);
+    out_off = chan_off + (uint32_t)fq * row_bytes;
+    {
+      const size_t row0 = ((size_t)b * A.s.L + t0);
+      const uint32_t span = (uint32_t)((t1 - t0) * A.s.D * kIo);
+      const uint32_t bspan = (uint32_t)((t1 - t0) * N * kIo);
+      r_u = wp_rsrc(static_cast<const IO*>(A.s.u) + row0 * A.s.D, span);
+      r_dl = wp_rsrc(static_cast<const IO*>(A.s.delta) + row0 * A.s.D, span);
+      r_z = wp_rsrc(A.s.z ? static_cast<const IO*>(A.s.z) + row0 * A.s.D : static_cast<const IO*>(A.s.u),
+                    A.s.z ? span : 0u);
+      r_out = wp_rsrc(static_cast<const IO*>(A.s.out) + row0 * A.s.D, kOut ? span : 0u);
+      r_B = wp_rsrc(static_cast<const IO*>(A.s.B) + row0 * N, bspan);
+      r_C = wp_rsrc(static_cast<const IO*>(A.s.C) + row0 * N, bspan);
+    }
+    const int n0 = S * sg;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float a = svalid ? A.s.A[dscan * N + n0 + s] : -1.0f;
+      a2[s] = a * kLog2e;
+      ka[s] = rcp(a);
+      ah[s] = 0.5f * a;
+      h[s] = 0.0f;
+    }
+    bias = (fvalid && A.s.bias) ? A.s.bias[dfront] : 0.0f;
+    dskip = (fvalid && A.s.dskip) ? A.s.dskip[dfront] : 0.0f;
+    dsum = 0.0f;
+    dcomp = 0.0f;
+    // state entering the chunk
+    if (MODE == kWpFull) {
+      if (A.s.h0 && svalid) get_state(A.s.h0 + ((size_t)b * A.s.D + dscan) * N + n0);
+    } else if (MODE == kWpOut) {
+      if (svalid) get_state(A.s.agg_h + (((size_t)b * G + g) * A.s.D + dscan) * N + n0);
+    }
+    // tile pipeline: global loads PD tiles ahead, two fr / bc slots
+    const int ntiles = (int)((t1 - t0 + T - 1) / T);
+    const int nfull = (int)((t1 - t0) / T);
+    Regs ring[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) load(ring[q], q);
+#pragma unroll
+    for (int i = 0; i < TQ; ++i) front_part(ring[0], 0, 0, i);
+    stage_bc(ring[0], 0);
+    load(ring[0], PD);
+    int k = 0;
+    for (; k + PD <= nfull; k += PD) tiles_full(ring, k, std::make_integer_sequence<int, PD>{});
+    tiles_tail(ring, k, ntiles - k, std::make_integer_sequence<int, PD>{});  // the last (up to PD) tiles
+    wave_lds_order();
+    if (ntiles > 0) epi_part(ntiles - 1, (ntiles - 1) & 1, TQ - 1);
+
+    // the chunk's end
+    if (MODE == kWpFull) {
+      if (A.s.last && svalid) put_state(A.s.last + ((size_t)b * A.s.D + dscan) * N + n0);
+    } else if (MODE == kWpAgg) {
+      if (svalid) put_state(A.s.agg_h + (((size_t)b * G + g) * A.s.D + dscan) * N + n0);
+      // dt sum of the front lane's channel over its P lanes (fq = 0 .. P-1), in order
+      sm.sdt[lane] = dsum;
+      wave_lds_order();
+      if (fq == 0 && fvalid) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int q = 0; q < P; ++q) tot += sm.sdt[fc + CW * q];
+        A.s.agg_s[((size_t)b * G + g) * A.s.D + dfront] = tot;
+      }
+    } else {  // kWpOut
+      if (g == G - 1 && A.s.last && svalid) put_state(A.s.last + ((size_t)b * A.s.D + dscan) * N + n0);
+    }
+  }
+};
+
+// WGW waves per workgroup, each on its own channels.  Workgroup ids go to the
+// XCDs in turn (id % 8); the P waves of a unit get workgroup ids that are
+// consecutive among one XCD's ids (for WGW = P, one workgroup is one unit).
+template <typename IO, int N, int T, int MODE, bool SP>
+__global__ __launch_bounds__(64 * S6_WP_WGW, S6_WP_WPE) void scan_wp_kernel(WpArgs a) {
+  using K = WpScan<IO, N, T, MODE, SP>;
+  constexpr int WGW = S6_WP_WGW < K::P ? S6_WP_WGW : K::P;
+  constexpr int WPU = K::P / WGW;  // workgroups per unit
+  static_assert(K::P % WGW == 0, "waves per workgroup");
+  __shared__ typename K::Lds sm[WGW];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int id = blockIdx.x;
+  const int m = id >> 3;
+  const int unit = WPU == 1 ? id : (m / WPU) * 8 + (id & 7);
+  if (unit >= a.units) return;
+  K k(a, sm[wv]);
+  k.run(unit, (WPU == 1 ? 0 : (m % WPU)) * WGW + wv);
+}
+
+template <typename IO, int N, int MODE>
+void launch_wp_pass(const WpArgs& a, hipStream_t st) {
+  constexpr int WGW = S6_WP_WGW < N / 2 ? S6_WP_WGW : N / 2;
+  constexpr int WPU = (N / 2) / WGW;
+  const unsigned grid = WPU == 1 ? (unsigned)a.units : (unsigned)((a.units + 7) / 8 * 8 * WPU);
+  if (a.s.softplus)
+    hipLaunchKernelGGL((scan_wp_kernel<IO, N, (N == 16 ? S6_WP_TILE16 : S6_WP_TILE), MODE, true>), dim3(grid), dim3(64 * WGW), 0, st, a);
+  else
+    hipLaunchKernelGGL((scan_wp_kernel<IO, N, (N == 16 ? S6_WP_TILE16 : S6_WP_TILE), MODE, false>), dim3(grid), dim3(64 * WGW), 0, st, a);
+}
+
+template <typename IO, int N>
+hipError_t launch_wp_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
+  WpArgs a;
+  a.s = s;
+  a.nblk = (int32_t)((s.D + 63) / 64);
+  const int32_t rows = (int32_t)(s.batch * a.nblk);
+  if (!p.split) {
+    a.units = rows;
+    launch_wp_pass<IO, N, kWpFull>(a, st);
+  } else {
+    a.s.agg_h = static_cast<float*>(ws);
+    a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N;
+    a.units = rows * (p.nchunks - 1);
+    launch_wp_pass<IO, N, kWpAgg>(a, st);
+    const hipError_t ce = launch_chunk_carry(a.s, N, st);
+    if (ce != hipSuccess) return ce;
+    a.units = rows * p.nchunks;
+    launch_wp_pass<IO, N, kWpOut>(a, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int wp_tile() { return S6_WP_TILE > S6_WP_TILE16 ? S6_WP_TILE : S6_WP_TILE16; }
+
+hipError_t launch_scan_wp(const ScanArgs& s, const ScanPlan& p, int io, int N, void* ws, hipStream_t st) {
+  const bool bf = io == kIoBF16;
+  if (N == 16) return bf ? launch_wp_t<uint16_t, 16>(s, p, ws, st) : launch_wp_t<float, 16>(s, p, ws, st);
+  if (N == 8) return bf ? launch_wp_t<uint16_t, 8>(s, p, ws, st) : launch_wp_t<float, 8>(s, p, ws, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace s6

@@ -158,16 +158,20 @@ EDGE = [
 ]
 
 
-ENGINES = ["default", "lane"]
+ENGINES = ["default", "wg", "lane"]
 
 
 def _engine(monkeypatch, engine):
     """The library picks its engine from the shape; MAMBA_MI355X_LANE_ENGINE=1 forces the
-    lane-per-channel engine so that both engines are covered on the same cases."""
+    lane-per-channel engine and MAMBA_MI355X_WG_ENGINE=1 the workgroup engine (waves split
+    the states) in place of the wave-private one, so that every engine is covered on the
+    same cases."""
+    monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
+    monkeypatch.delenv("MAMBA_MI355X_WG_ENGINE", raising=False)
     if engine == "lane":
         monkeypatch.setenv("MAMBA_MI355X_LANE_ENGINE", "1")
-    else:
-        monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
+    elif engine == "wg":
+        monkeypatch.setenv("MAMBA_MI355X_WG_ENGINE", "1")
 
 
 @pytest.mark.parametrize("engine", ENGINES)
@@ -196,21 +200,23 @@ WG_CASES = [
 ]
 
 
+@pytest.mark.parametrize("engine", ["default", "wg"])
 @pytest.mark.parametrize("case", WG_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in WG_CASES])
-def test_workgroup_engine_modes(case, monkeypatch):
+def test_workgroup_engine_modes(case, engine, monkeypatch):
     _need_gpu()
-    _engine(monkeypatch, "default")
+    _engine(monkeypatch, engine)
     batch, L, D, N, io = case
-    _announce(f"workgroup engine case {case}")
+    _announce(f"workgroup engine case {case} engine={engine}")
     inp = W.generate(batch, L, D, N, io, seed=900 + L + D + N)
     eo, el = check(inp, label=str(case))
     print(f"{case}: out err {eo:.3e} last err {el:.3e}")
 
 
+@pytest.mark.parametrize("engine", ["default", "wg"])
 @pytest.mark.parametrize("case", [(5, 1100, 4096, 16, "f32"), (1, 4096, 64, 16, "f32")], ids=["chained", "split"])
-def test_workgroup_engine_initial_state(case, monkeypatch):
+def test_workgroup_engine_initial_state(case, engine, monkeypatch):
     _need_gpu()
-    _engine(monkeypatch, "default")
+    _engine(monkeypatch, engine)
     batch, L, D, N, io = case
     inp = W.generate(batch, L, D, N, io, seed=77)
     h0 = np.random.default_rng(78).standard_normal((batch, D, N)).astype(np.float32)
