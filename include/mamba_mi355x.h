@@ -57,7 +57,11 @@ enum mamba_status {
   MAMBA_ERR_DTYPE = 4,       /* io_dtype is not a mamba_io_dtype                     */
   MAMBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size function says */
   MAMBA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                     */
-  MAMBA_ERR_HIP = 7          /* the HIP runtime refused a kernel launch              */
+  MAMBA_ERR_HIP = 7,         /* the HIP runtime refused a kernel launch (or, from
+                                mamba_stream_status, failed to synchronise)        */
+  MAMBA_ERR_TIMEOUT = 8,     /* mamba_stream_status: a wait between sequence chunks
+                                gave up; the outputs after it are NaN              */
+  MAMBA_ERR_OPTION = 9       /* mamba_set_option: unknown option or invalid value  */
 };
 
 enum mamba_io_dtype { MAMBA_IO_F32 = 0, MAMBA_IO_BF16 = 1 };
@@ -69,12 +73,60 @@ int mamba_version(void);
 const char* mamba_status_string(int status);
 
 /*
+ * Tuning options: process-wide settings that the execution plan of every later
+ * call reads, so a workspace size depends on the shape AND on these values
+ * (query the size after setting them).  Each option starts, when the library is
+ * first used, from the environment variable named in brackets; the defaults
+ * are the fastest measured settings.  Setting options is not synchronised with
+ * calls in flight on other threads.  Not part of the method: no option changes
+ * what is computed, only how.
+ */
+enum mamba_option {
+  MAMBA_OPT_ENGINE = 1,       /* forward engine for dstate 8 and 16: 0 automatic, 1 one lane per
+                                 channel, 2 workgroup (waves split the states), 3 wave-private
+                                 [MAMBA_MI355X_ENGINE = lane | wg | wp]                          */
+  MAMBA_OPT_CHUNK = 2,        /* tokens per chunk of the workgroup engine's chained mode, 0: 1024
+                                 [MAMBA_MI355X_CHUNK]                                           */
+  MAMBA_OPT_WG_WAVES = 3,     /* waves per workgroup of the workgroup engine at dstate 16: 0 or 8,
+                                 or 4 [MAMBA_MI355X_WG_WAVES]                                    */
+  MAMBA_OPT_FUSED_DT = 4,     /* 1: mamba_ssm_fwd projects dt inside the scan kernel on the matrix
+                                 cores instead of writing delta [MAMBA_MI355X_FUSED_DT]          */
+  MAMBA_OPT_BWD_CHUNK = 5,    /* tokens per chunk of mamba_scan_bwd, a multiple of 8; 0: chosen
+                                 from the shape [MAMBA_MI355X_BWD_CHUNK]                         */
+  MAMBA_OPT_GEMM_GENERAL = 6, /* 1: the projections use only the general GEMM kernel
+                                 [MAMBA_MI355X_GEMM_GENERAL]                                     */
+  MAMBA_OPT_SPIN_LIMIT = 7    /* polls a chunk makes for its predecessor's end state before it
+                                 gives up (default 2^24, never reached in practice); 0 gives up
+                                 at once, so that the error path can be tested                   */
+};
+
+/* Set an option: MAMBA_OK, or MAMBA_ERR_OPTION for an unknown option or a value
+   out of its range (the option keeps its value). */
+int mamba_set_option(int option, int64_t value);
+
+/* Current value of an option, or -1 for an unknown option. */
+int64_t mamba_get_option(int option);
+
+/*
+ * Synchronises `stream` (a hipStream_t, NULL = default), then reports whether a
+ * wait between sequence chunks has given up on the current device since the
+ * last call: MAMBA_ERR_TIMEOUT if so (and clears the report), else MAMBA_OK;
+ * MAMBA_ERR_HIP if the synchronisation fails.  Chunks of one channel block that
+ * run on different workgroups hand their end state over through the workspace
+ * (mamba_scan_fwd, mamba_scan_fwd_complex, mamba_ssm_fwd, mamba_block_fwd);
+ * a waiting chunk that gives up continues from NaN, so the affected outputs and
+ * last_state are NaN, never silently stale.  The report is per device and
+ * shared by all streams.
+ */
+int mamba_stream_status(void* stream);
+
+/*
  * Bytes of device workspace mamba_scan_fwd needs for this shape: work
  * counters, the state handed between sequence chunks, or per-chunk aggregates
  * (about 4*N bytes per (batch row, channel) and chunk; 0 for some small
- * shapes).  A pure host function of its arguments: it needs no GPU and returns
- * the same value on every call.  Returns 0 for arguments mamba_scan_fwd would
- * reject.
+ * shapes).  A host function of its arguments and the options (mamba_set_option):
+ * it needs no GPU and returns the same value while the options are unchanged.
+ * Returns 0 for arguments mamba_scan_fwd would reject.
  */
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype);
 

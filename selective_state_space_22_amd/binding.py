@@ -16,6 +16,21 @@ LIB_PATH = os.path.join(_HERE, "libmamba_mi355x.so")
 MAMBA_IO_F32 = 0
 MAMBA_IO_BF16 = 1
 
+# statuses that callers test for (the rest: see status_string)
+MAMBA_OK = 0
+MAMBA_ERR_TIMEOUT = 8
+MAMBA_ERR_OPTION = 9
+
+# options (enum mamba_option)
+MAMBA_OPT_ENGINE = 1
+MAMBA_OPT_CHUNK = 2
+MAMBA_OPT_WG_WAVES = 3
+MAMBA_OPT_FUSED_DT = 4
+MAMBA_OPT_BWD_CHUNK = 5
+MAMBA_OPT_GEMM_GENERAL = 6
+MAMBA_OPT_SPIN_LIMIT = 7
+ENGINES = {"auto": 0, "lane": 1, "wg": 2, "wp": 3}
+
 _lib = None
 
 
@@ -69,6 +84,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_block_fwd_workspace_size.restype = ctypes.c_size_t
     lib.mamba_block_fwd.argtypes = [I64] * 6 + [I] + [P] * 8 + [I, P, P, P, P, ctypes.c_size_t, P]
     lib.mamba_block_fwd.restype = I
+    lib.mamba_set_option.argtypes = [I, I64]
+    lib.mamba_set_option.restype = I
+    lib.mamba_get_option.argtypes = [I]
+    lib.mamba_get_option.restype = I64
+    lib.mamba_stream_status.argtypes = [P]
+    lib.mamba_stream_status.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -80,6 +101,33 @@ def status_string(status: int) -> str:
 
 def mamba_version() -> int:
     return int(load_library().mamba_version())
+
+
+def mamba_set_option(option: int, value: int) -> None:
+    """Set a process-wide tuning option (MAMBA_OPT_*); raises on an unknown option or value."""
+    st = load_library().mamba_set_option(int(option), int(value))
+    if st != 0:
+        raise MambaError("mamba_set_option", st)
+
+
+def mamba_get_option(option: int) -> int:
+    return int(load_library().mamba_get_option(int(option)))
+
+
+def mamba_stream_status(device=None) -> int:
+    """Synchronise the current stream of `device` and return the device's wait status
+    (0, or MAMBA_ERR_TIMEOUT = 8 when a wait between sequence chunks gave up since the
+    last query; the report is then cleared)."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    return int(load_library().mamba_stream_status(_stream(dev)))
+
+
+def _check_status(func, device):
+    st = mamba_stream_status(device)
+    if st != 0:
+        raise MambaError(func, st)
 
 
 def _io_dtype(t):
@@ -120,10 +168,12 @@ def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, dim: int, dstate: int
 
 
 def mamba_scan_fwd(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
-                   out=None, last_state=None, workspace=None, return_last_state=True):
+                   out=None, last_state=None, workspace=None, return_last_state=True, check=False):
     """Forward selective scan.  u, delta, z: (batch, L, D); B, C: (batch, L, N); A: (D, N) float32.
 
-    Returns (out, last_state); out has u's dtype, last_state is float32 (batch, D, N)."""
+    Returns (out, last_state); out has u's dtype, last_state is float32 (batch, D, N).
+    check=True synchronises the stream and raises MambaError if a wait between
+    sequence chunks gave up (mamba_stream_status); the default only enqueues."""
     import torch
 
     lib = load_library()
@@ -151,6 +201,8 @@ def mamba_scan_fwd(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta
         ws_ptr, workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
     if st != 0:
         raise MambaError("mamba_scan_fwd", st)
+    if check:
+        _check_status("mamba_scan_fwd", dev)
     return out, last_state
 
 
@@ -172,7 +224,7 @@ def _re_im(t, name):
 
 
 def mamba_scan_fwd_complex(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
-                           out=None, last_state=None, workspace=None, return_last_state=True):
+                           out=None, last_state=None, workspace=None, return_last_state=True, check=False):
     """Forward selective scan with a complex diagonal A; x, dt, B, C and out are real, y = Re(C . h).
 
     A: (D, N) complex64 or (D, N, 2) float32 re/im; h0 likewise (batch, D, N).  Other
@@ -210,6 +262,8 @@ def mamba_scan_fwd_complex(u, delta, A, B, C, delta_bias=None, Dskip=None, z=Non
         ws_ptr, workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
     if st != 0:
         raise MambaError("mamba_scan_fwd_complex", st)
+    if check:
+        _check_status("mamba_scan_fwd_complex", dev)
     return out, (torch.view_as_complex(last_state) if last_state is not None else None)
 
 
@@ -358,7 +412,7 @@ def mamba_ssm_fwd_workspace_size(batch, seqlen, dim, dstate, dt_rank, io_dtype) 
 
 
 def mamba_ssm_fwd(x, W_x, W_dt, A, z=None, dt_bias=None, Dskip=None, delta_softplus=True, h0=None, out=None,
-                  last_state=None, workspace=None, return_last_state=True):
+                  last_state=None, workspace=None, return_last_state=True, check=False):
     """Selection projections followed by the scan (u = x).  Returns (out, last_state)."""
     import torch
 
@@ -384,6 +438,8 @@ def mamba_ssm_fwd(x, W_x, W_dt, A, z=None, dt_bias=None, Dskip=None, delta_softp
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
     if st != 0:
         raise MambaError("mamba_ssm_fwd", st)
+    if check:
+        _check_status("mamba_ssm_fwd", dev)
     return out, last_state
 
 
@@ -392,7 +448,7 @@ def mamba_block_fwd_workspace_size(batch, seqlen, d_model, dim, dstate, dt_rank,
 
 
 def mamba_block_fwd(hidden, W_in, W_x, W_dt, A, W_out, dt_bias=None, Dskip=None, delta_softplus=True, h0=None,
-                    out=None, last_state=None, workspace=None, return_last_state=True):
+                    out=None, last_state=None, workspace=None, return_last_state=True, check=False):
     """One Mamba block: hidden (batch, L, d_model); W_in (2 D, d_model); W_out (d_model, D);
     W_x, W_dt, A, dt_bias, Dskip as for mamba_ssm_fwd.  Returns (out (batch, L, d_model), last_state)."""
     import torch
@@ -422,4 +478,6 @@ def mamba_block_fwd(hidden, W_in, W_x, W_dt, A, W_out, dt_bias=None, Dskip=None,
         workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(dev))
     if st != 0:
         raise MambaError("mamba_block_fwd", st)
+    if check:
+        _check_status("mamba_block_fwd", dev)
     return out, last_state

@@ -3,8 +3,10 @@
 // Every entry point validates its arguments on the host before it touches
 // the HIP runtime, then enqueues kernels on the caller's stream and returns.
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "../../include/mamba_mi355x.h"
 #include "s6_internal.h"
@@ -25,6 +27,59 @@ int fail(int status, const char* where, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------------ options
+
+constexpr int64_t kDefaultSpinLimit = int64_t(1) << 24;
+
+int64_t env_value(const char* name, int64_t dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !v[0]) return dflt;
+  char* end = nullptr;
+  const long long x = std::strtoll(v, &end, 10);
+  return (end && *end == 0 && x >= 0) ? (int64_t)x : dflt;
+}
+
+// The options start from the environment once, when the library is first used.
+struct Options {
+  std::atomic<int64_t> v[s6::kOptCount];
+  Options() {
+    int64_t engine = 0;
+    if (const char* e = std::getenv("MAMBA_MI355X_ENGINE")) {
+      if (!std::strcmp(e, "lane")) engine = 1;
+      else if (!std::strcmp(e, "wg")) engine = 2;
+      else if (!std::strcmp(e, "wp")) engine = 3;
+    }
+    if (env_value("MAMBA_MI355X_LANE_ENGINE", 0) == 1) engine = 1;
+    if (env_value("MAMBA_MI355X_WG_ENGINE", 0) == 1) engine = 2;
+    for (auto& x : v) x.store(0);
+    v[s6::kOptEngine].store(engine);
+    v[s6::kOptChunk].store(env_value("MAMBA_MI355X_CHUNK", 0));
+    v[s6::kOptWgWaves].store(env_value("MAMBA_MI355X_WG_WAVES", 0));
+    v[s6::kOptFusedDt].store(env_value("MAMBA_MI355X_FUSED_DT", 0) == 1 ? 1 : 0);
+    v[s6::kOptBwdChunk].store(env_value("MAMBA_MI355X_BWD_CHUNK", 0));
+    v[s6::kOptGemmGeneral].store(std::getenv("MAMBA_MI355X_GEMM_GENERAL") ? 1 : 0);
+    v[s6::kOptSpinLimit].store(kDefaultSpinLimit);
+  }
+};
+
+Options& options() {
+  static Options o;
+  return o;
+}
+
+bool option_valid(int key, int64_t value) {
+  switch (key) {
+    case s6::kOptEngine: return value >= 0 && value <= 3;
+    case s6::kOptChunk: return value >= 0 && value <= (int64_t(1) << 30);
+    case s6::kOptWgWaves: return value == 0 || value == 4 || value == 8;
+    case s6::kOptFusedDt: return value == 0 || value == 1;
+    case s6::kOptBwdChunk: return value >= 0 && value <= (int64_t(1) << 30);
+    case s6::kOptGemmGeneral: return value == 0 || value == 1;
+    case s6::kOptSpinLimit: return value >= 0 && value <= 0xffffffffll;
+    default: return false;
+  }
+}
 
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t kMaxDim = int64_t(1) << 22;
@@ -97,9 +152,31 @@ int state_update(bool cplx, const char* where, int64_t batch, int64_t dim, int64
 
 }  // namespace
 
+namespace s6 {
+int64_t option(int key) { return key > 0 && key < kOptCount ? options().v[key].load() : 0; }
+}  // namespace s6
+
 extern "C" {
 
-int mamba_version(void) { return 100; }
+int mamba_version(void) { return 200; }
+
+int mamba_set_option(int option, int64_t value) {
+  if (!option_valid(option, value)) return fail(MAMBA_ERR_OPTION, "mamba_set_option", "option or value");
+  options().v[option].store(value);
+  return MAMBA_OK;
+}
+
+int64_t mamba_get_option(int option) {
+  if (option <= 0 || option >= s6::kOptCount) return -1;
+  return options().v[option].load();
+}
+
+int mamba_stream_status(void* stream) {
+  uint32_t v = 0;
+  const hipError_t e = s6::take_wait_status(static_cast<hipStream_t>(stream), &v);
+  if (e != hipSuccess) return fail(MAMBA_ERR_HIP, "mamba_stream_status", hipGetErrorString(e));
+  return v != 0 ? fail(MAMBA_ERR_TIMEOUT, "mamba_stream_status", "a chained-chunk wait gave up") : MAMBA_OK;
+}
 
 const char* mamba_status_string(int status) {
   switch (status) {
@@ -111,6 +188,8 @@ const char* mamba_status_string(int status) {
     case MAMBA_ERR_WORKSPACE: return "workspace missing or too small";
     case MAMBA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MAMBA_ERR_HIP: return "HIP kernel launch failed";
+    case MAMBA_ERR_TIMEOUT: return "a wait between sequence chunks gave up; outputs after it are NaN";
+    case MAMBA_ERR_OPTION: return "unknown option or invalid option value";
     default: return "unknown status";
   }
 }
@@ -427,9 +506,8 @@ int mamba_ssm_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, in
   // on the matrix cores (no delta tensor).  Off by default: the scan is
   // VALU-bound and the extra per-tile work there costs about what the separate
   // dt projection GEMM does.
-  const char* fenv = std::getenv("MAMBA_MI355X_FUSED_DT");
   const bool fused = tokens && s6::wg_supported(dstate) && s6::fused_dt_supported(dstate, dt_rank, io_dtype) &&
-                     aligned16(W_dt) && fenv && fenv[0] == '1';
+                     aligned16(W_dt) && s6::option(s6::kOptFusedDt) == 1;
   const s6::ScanPlan plan = fused ? s6::plan_scan_fused_dt(batch, seqlen, dim, dstate)
                                   : s6::plan_scan(batch, seqlen, dim, dstate);
   if (tokens) {

@@ -10,6 +10,26 @@ namespace s6 {
 
 enum IoType { kIoF32 = 0, kIoBF16 = 1 };
 
+// Process-wide tuning options (the mamba_option values of the C ABI).  They are
+// read by the plans, so a workspace size depends on the shape and on them.
+enum Option {
+  kOptEngine = 1,       // forward engine: 0 automatic, 1 lane, 2 workgroup, 3 wave-private
+  kOptChunk = 2,        // tokens per chunk of the workgroup engine's chained mode (0: 1024)
+  kOptWgWaves = 3,      // waves of the workgroup engine for N = 16 (0: 8, or 4)
+  kOptFusedDt = 4,      // 1: mamba_ssm_fwd projects dt inside the scan
+  kOptBwdChunk = 5,     // tokens per chunk of the backward (0: automatic)
+  kOptGemmGeneral = 6,  // 1: only the general GEMM kernel
+  kOptSpinLimit = 7,    // polls of a chained-mode wait before it gives up (0: give up at once)
+  kOptCount = 8
+};
+int64_t option(int key);
+
+// Sticky per-device status word of the chained-mode waits (nonzero: some wait
+// gave up since the last read); kernels write it through this device address.
+uint32_t* wait_status_ptr();
+// Synchronise the stream, then read and clear the current device's status word.
+hipError_t take_wait_status(hipStream_t stream, uint32_t* value);
+
 // Arguments of one forward scan; pointers are device pointers.
 struct ScanArgs {
   const void* u;
@@ -74,7 +94,8 @@ struct WgArgs {
   ScanArgs s;
   uint32_t* ticket;   // work counter of this launch (zeroed before the launch)
   uint32_t* flags;    // chained mode: chunks finished per channel block (zeroed before the launch)
-  uint32_t* err;      // set nonzero if a wait ever exceeded its bound (never expected)
+  uint32_t* err;      // the device's wait status word: set when a wait gives up (never expected)
+  uint32_t spin_limit;  // polls of a wait before it gives up; 0: give up at once (testing)
   float* carry;       // chained mode: (chains, 64, N) state handed from chunk to chunk
   int32_t chains;     // batch * blocks_per_row: independent (batch row, 64-channel block) pairs
   int32_t blocks_per_row;

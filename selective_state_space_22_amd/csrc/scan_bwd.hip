@@ -804,10 +804,7 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t D, int64_t N) {
   while (K > 64 && units * ((L + K - 1) / K) < 1024) K /= 2;
   const int64_t Lr = (L + T - 1) / T * T;
   if (K > Lr) K = Lr;
-  if (const char* v = std::getenv("MAMBA_MI355X_BWD_CHUNK")) {
-    const long c = std::atol(v);
-    if (c >= T && c % T == 0) K = c;
-  }
+  if (const int64_t c = option(kOptBwdChunk); c >= T && c % T == 0) K = c;
   // every per-chunk buffer (token rows, tile-start states) must span < 2^31 bytes
   const int64_t cap_tok = ((int64_t(1) << 31) - 1) / (D * 4) / T * T;
   const int64_t cap_st = ((int64_t(1) << 31) - 1) / (N * D * 4) * T;

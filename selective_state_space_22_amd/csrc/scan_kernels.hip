@@ -185,13 +185,6 @@ bool dstate_supported(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 |
 
 namespace {
 
-int64_t env_int(const char* name, int64_t dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !v[0]) return dflt;
-  char* end = nullptr;
-  long long x = std::strtoll(v, &end, 10);
-  return (end && *end == 0 && x > 0) ? (int64_t)x : dflt;
-}
 
 size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
@@ -242,7 +235,7 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
     // about 1024 tokens let the persistent grid balance the blocks.
     p.split = 0;
     int64_t chunk = L;
-    if (chains > kCus) chunk = env_int("MAMBA_MI355X_CHUNK", 1024);
+    if (chains > kCus) chunk = option(kOptChunk) > 0 ? option(kOptChunk) : 1024;
     chunk = ((chunk + T - 1) / T) * T;
     if (chunk > cap) chunk = cap;
     if (chunk >= L) chunk = L;
@@ -309,10 +302,12 @@ ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
 }
 
 ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
-  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0) {
+  const int64_t engine = option(kOptEngine);
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && engine != 1) {
+    if (engine == 3) return plan_wp(batch, L, D, N);
     // Long sequences over few channel blocks (two passes over chunks) run faster
     // on the workgroup engine, whose waves load whole 128-byte lines of a token row.
-    if (env_int("MAMBA_MI355X_WG_ENGINE", 0) == 0) {
+    if (engine == 0) {
       const ScanPlan p = plan_wp(batch, L, D, N);
       if (!p.split) return p;
     }
@@ -328,8 +323,7 @@ ScanPlan plan_scan_fused_dt(int64_t batch, int64_t L, int64_t D, int64_t N) {
 
 ScanPlan plan_scan_complex(int64_t batch, int64_t L, int64_t D, int64_t N) {
   // The real scan's plans; carries and chunk aggregates hold N complex states.
-  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && env_int("MAMBA_MI355X_LANE_ENGINE", 0) == 0)
-    return plan_wg(batch, L, D, N, 2);
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && option(kOptEngine) != 1) return plan_wg(batch, L, D, N, 2);
   return plan_lane(batch, L, D, N, 2);
 }
 

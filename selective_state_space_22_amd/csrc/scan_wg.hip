@@ -38,7 +38,6 @@
 namespace s6 {
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 24;
 #ifndef S6_SCAN_AHEAD
 #define S6_SCAN_AHEAD 1
 #endif
@@ -145,6 +144,7 @@ struct WgScan {
     float sdt[W][64];                            // split mode: partial sums of dt
     float raw[FDT ? 2 : 1][T][64];               // fused dt projection: raw dt per (token, channel)
     int item[2];
+    int poison;  // chained mode: the wait for this item's carry-in gave up
   };
 
   struct Regs {  // raw prefetched global data of one tile
@@ -465,19 +465,28 @@ struct WgScan {
         if (A.s.h0 && dvalid) get_state(A.s.h0 + (((size_t)b * A.s.D + d) * N + nstate0) * CF);
       } else {
         if (threadIdx.x == 0) {
+          // Bounded wait for the previous chunk's end state.  Giving up sets the
+          // device's status word and poisons this chunk's state with NaN, so the
+          // rest of the channel block's outputs cannot pass for valid ones.
+          bool ok = A.spin_limit > 0;
           uint32_t spins = 0;
-          while (__hip_atomic_load(A.flags + chain, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)g) {
+          while (ok && __hip_atomic_load(A.flags + chain, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)g) {
             __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-              __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
+            if (++spins >= A.spin_limit) ok = false;
           }
+          if (!ok) __hip_atomic_store(A.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.poison = ok ? 0 : 1;
         }
         // Thread 0's acquire load (which invalidates this CU's caches) is
         // ordered before the other waves' reads of the carry by the barrier.
         __syncthreads();
         get_state(A.carry + (((size_t)chain * 64 + lane) * N + nstate0) * CF);
+        if (sm.poison) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) h[s] = __builtin_nanf("");
+#pragma unroll
+          for (int s = 0; s < CS; ++s) hq[s] = __builtin_nanf("");
+        }
       }
     } else if (MODE == kModeOut) {
       if (dvalid) get_state(A.s.agg_h + ((((size_t)b * G + g) * A.s.D + d) * N + nstate0) * CF);
@@ -601,7 +610,9 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
   a.blocks_per_row = (int32_t)((s.D + 63) / 64);
   a.chains = (int32_t)(s.batch * a.blocks_per_row);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(base);
-  a.err = ctrl + 2;
+  a.err = wait_status_ptr();
+  if (a.err == nullptr) return hipErrorInvalidSymbol;
+  a.spin_limit = (uint32_t)option(kOptSpinLimit);
   a.flags = ctrl + 64;
   const int64_t ctrl_words = (int64_t)(p.ws_ctrl / 4);
   hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((ctrl_words + 255) / 256)), dim3(256), 0, st, ctrl,
@@ -639,10 +650,40 @@ hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, bool cplx, void* 
 
 }  // namespace
 
+// The chained-mode waits' status word of each device (a copy per GPU).
+__device__ uint32_t s6_wait_status;
+
+uint32_t* wait_status_ptr() {
+  constexpr int kMaxDevices = 64;
+  static uint32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(s6_wait_status)) != hipSuccess) return nullptr;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  return addr[dev];
+}
+
+hipError_t take_wait_status(hipStream_t stream, uint32_t* value) {
+  *value = 0;
+  uint32_t* p = wait_status_ptr();
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(value, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  if (*value != 0) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+  }
+  return e;
+}
+
 bool wg_supported(int64_t N) { return N == 16 || N == 8; }
 int wg_waves(int64_t N) {
-  const char* v = std::getenv("MAMBA_MI355X_WG_WAVES");
-  if (N == 16 && v && v[0] == '4') return 4;
+  if (N == 16 && option(kOptWgWaves) == 4) return 4;
   return N == 16 ? 8 : 4;
 }
 int wg_tile(int64_t) { return S6_WG_TILE; }

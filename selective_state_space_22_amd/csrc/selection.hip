@@ -886,7 +886,7 @@ bool big_ok(const GemmArgs& g, size_t out_bytes) {
   const bool second = g.C2 == nullptr ||
                       (g.n2 > 0 && g.n2 < g.N && g.n2 % kBigBM == 0 && reinterpret_cast<uintptr_t>(g.C2) % (4 * out_bytes) == 0);
   return g.M >= 1024 && g.N >= 512 && g.K * e >= 1024 && offsets && segments && second &&
-         std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr;
+         option(kOptGemmGeneral) == 0;
 }
 
 template <typename IN, typename OUT>
@@ -914,7 +914,7 @@ hipError_t gemm_nt(GemmArgs g, hipStream_t st, int parts = 1) {
   }
   if (g.C2 != nullptr) return hipErrorInvalidValue;  // only the large-product kernel routes columns
   const int ks = (int)((g.K * (int64_t)sizeof(IN) + 63) / 64);
-  if (mfma_ok<IN>(g) && parts == 1 && ks <= kShortMaxSlices && std::getenv("MAMBA_MI355X_GEMM_GENERAL") == nullptr)
+  if (mfma_ok<IN>(g) && parts == 1 && ks <= kShortMaxSlices && option(kOptGemmGeneral) == 0)
     return gemm_nt_short<IN, OUT>(g, ks, st);
   if (mfma_ok<IN>(g)) {
     const int all = (int)((g.K * (int64_t)sizeof(IN) + kStageBytes - 1) / kStageBytes);

@@ -2,6 +2,8 @@
 calling the HIP path through the C ABI, and the parity error metric."""
 from __future__ import annotations
 
+import contextlib
+
 import numpy as np
 
 # Max relative error allowed against the fp64 oracle (fp32 state in both cases).
@@ -56,6 +58,31 @@ def gpu_scan(inp, h0=None, device="cuda", softplus=None, dev_inputs=None):
     d = dev_inputs or to_device(inp, device)
     h0t = None if h0 is None else torch.from_numpy(np.ascontiguousarray(h0, np.float32)).to(device)
     out, last = mamba_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["delta_bias"], d["Dskip"], d["z"],
-                               inp.softplus if softplus is None else softplus, h0t)
+                               inp.softplus if softplus is None else softplus, h0t, check=True)
     torch.cuda.synchronize()
     return to_host(out), to_host(last)
+
+
+@contextlib.contextmanager
+def library_option(option, value):
+    """Set a process-wide library option (MAMBA_OPT_*) for the body of a with-block and
+    restore the previous value afterwards; value None leaves the option as it is."""
+    from selective_state_space_22_amd import binding
+
+    old = binding.mamba_get_option(option)
+    if value is not None:
+        binding.mamba_set_option(option, value)
+    try:
+        yield
+    finally:
+        binding.mamba_set_option(option, old)
+
+
+def force_engine(request, engine):
+    """Pin the forward engine for one test ("default" = the library's own choice) and
+    restore it when the test ends."""
+    from selective_state_space_22_amd import binding
+
+    cm = library_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["auto" if engine == "default" else engine])
+    cm.__enter__()
+    request.addfinalizer(lambda: cm.__exit__(None, None, None))

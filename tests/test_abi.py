@@ -31,13 +31,13 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_fwd",
-                                    "mamba_scan_fwd_complex", "mamba_scan_fwd_complex_workspace_size",
-                                    "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
-                                    "mamba_selection_fwd_workspace_size", "mamba_ssm_fwd",
-                                    "mamba_ssm_fwd_workspace_size", "mamba_state_update", "mamba_state_update_complex",
-                                    "mamba_status_string",
-                                    "mamba_version"]
+    assert declared_functions() == sorted([
+        "mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_get_option", "mamba_scan_bwd",
+        "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_complex",
+        "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
+        "mamba_selection_fwd_workspace_size", "mamba_set_option", "mamba_ssm_fwd", "mamba_ssm_fwd_workspace_size",
+        "mamba_state_update", "mamba_state_update_complex", "mamba_status_string", "mamba_stream_status",
+        "mamba_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -47,9 +47,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mamba_version() == 100
+    assert lib.mamba_version() == 200
     seen = set()
-    for st in range(8):
+    for st in range(10):
         s = binding.status_string(st)
         assert s and s not in seen
         seen.add(s)
@@ -74,6 +74,51 @@ def test_workspace_size_is_a_pure_function_of_shape(lib):
     assert ws(1, 16, 64, 16, 7) == 0
     assert ws(-1, 16, 64, 16, 0) == 0
 
+
+
+@pytest.fixture
+def restore_options(lib):
+    keep = {k: binding.mamba_get_option(k) for k in range(1, 8)}
+    yield
+    for k, v in keep.items():
+        binding.mamba_set_option(k, v)
+
+
+def test_options_round_trip_and_validation(lib, restore_options):
+    opts = [binding.MAMBA_OPT_ENGINE, binding.MAMBA_OPT_CHUNK, binding.MAMBA_OPT_WG_WAVES, binding.MAMBA_OPT_FUSED_DT,
+            binding.MAMBA_OPT_BWD_CHUNK, binding.MAMBA_OPT_GEMM_GENERAL, binding.MAMBA_OPT_SPIN_LIMIT]
+    assert opts == list(range(1, 8))
+    # the wait bound starts at 2^24 sleeps (a few seconds) unless the environment set it
+    for k, good, bad in [(binding.MAMBA_OPT_ENGINE, 3, 4), (binding.MAMBA_OPT_WG_WAVES, 4, 5),
+                         (binding.MAMBA_OPT_FUSED_DT, 1, 2), (binding.MAMBA_OPT_GEMM_GENERAL, 1, -1),
+                         (binding.MAMBA_OPT_CHUNK, 2048, -1), (binding.MAMBA_OPT_SPIN_LIMIT, 0, 1 << 32)]:
+        binding.mamba_set_option(k, good)
+        assert binding.mamba_get_option(k) == good
+        with pytest.raises(binding.MambaError) as ex:
+            binding.mamba_set_option(k, bad)
+        assert ex.value.status == 9
+        assert binding.mamba_get_option(k) == good  # a refused value leaves the option alone
+    for k in (0, 8, 99, -1):
+        assert binding.mamba_get_option(k) == -1
+        with pytest.raises(binding.MambaError):
+            binding.mamba_set_option(k, 0)
+
+
+def test_workspace_follows_the_engine_option(lib, restore_options):
+    ws = binding.mamba_scan_fwd_workspace_size
+    shape = (4, 4096, 5120, 16, 1)
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["auto"])
+    auto = ws(*shape)
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["wp"])
+    assert ws(*shape) == auto == 0
+    # the workgroup engine chains sequence chunks through a flag and carry workspace,
+    # the lane engine's chunks store their aggregates
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["wg"])
+    assert ws(*shape) > 0
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["lane"])
+    assert ws(*shape) > 0
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["auto"])
+    assert ws(*shape) == auto
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced
 

@@ -14,13 +14,12 @@ row and channel where that takes seconds, otherwise a subset whose gradients
 it can compute exactly (channels are independent SSMs; dB and dC of a batch
 row need all of its channels, dA, dDskip and dbias of a channel need all of
 its batch rows)."""
-import os
-
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import parity_error, to_device, to_host, torch_io
+from gpu_util import library_option, parity_error, to_device, to_host, torch_io
+from selective_state_space_22_amd import binding
 from selective_state_space_22_amd import workloads as W
 
 torch = pytest.importorskip("torch")
@@ -82,22 +81,9 @@ def compare(got, ref, io, label, keys=None):
     return errs
 
 
-class chunk_len:
-    """Force the backward's chunk length (plan override read at every call)."""
-
-    def __init__(self, k):
-        self.k = k
-
-    def __enter__(self):
-        self.old = os.environ.get("MAMBA_MI355X_BWD_CHUNK")
-        if self.k is not None:
-            os.environ["MAMBA_MI355X_BWD_CHUNK"] = str(self.k)
-
-    def __exit__(self, *a):
-        if self.old is None:
-            os.environ.pop("MAMBA_MI355X_BWD_CHUNK", None)
-        else:
-            os.environ["MAMBA_MI355X_BWD_CHUNK"] = self.old
+def chunk_len(k):
+    """Force the backward's chunk length (None keeps the library's own choice)."""
+    return library_option(binding.MAMBA_OPT_BWD_CHUNK, k)
 
 
 def run_case(batch, L, D, N, io, seed, chunk=None, h0=False, dlast=True, gate=True, skip=True, bias=True,

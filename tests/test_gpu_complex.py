@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, gpu_scan, parity_error, to_device, to_host
+from gpu_util import TOL, force_engine, gpu_scan, parity_error, to_device, to_host
 from selective_state_space_22_amd import workloads as W
 
 torch = pytest.importorskip("torch")
@@ -73,21 +73,18 @@ def check(inp, Ac, h0=None, softplus=None, label=""):
     return eo, el
 
 
-def _engine(monkeypatch, engine):
-    """N = 8 and 16 run on the workgroup engine by default; MAMBA_MI355X_LANE_ENGINE=1
-    forces the lane-per-channel kernels so that both are covered."""
-    if engine == "lane":
-        monkeypatch.setenv("MAMBA_MI355X_LANE_ENGINE", "1")
-    else:
-        monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
+def _engine(request, engine):
+    """N = 8 and 16 run on the workgroup engine by default; the engine option set to
+    "lane" forces the lane-per-channel kernels so that both are covered."""
+    force_engine(request, "lane" if engine == "lane" else "default")
 
 
 @pytest.mark.parametrize("engine", ["default", "lane"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
-def test_small_full(io, N, engine, monkeypatch):
+def test_small_full(io, N, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     _announce(f"complex A: (2, 300, 130, {N}) {io}, with h0, engine={engine}")
     inp, Ac = _cinputs(2, 300, 130, N, io, seed=W.SEED_BASE + 41 + N)
     eo, el = check(inp, Ac, h0=_h0(2, 130, N, 5), label=f"N={N} {io} {engine}")
@@ -108,9 +105,9 @@ WG_CASES = [
 
 
 @pytest.mark.parametrize("case", WG_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in WG_CASES])
-def test_workgroup_engine_modes(case, monkeypatch):
+def test_workgroup_engine_modes(case, request):
     _need_gpu()
-    _engine(monkeypatch, "default")
+    _engine(request, "default")
     batch, L, D, N, io = case
     _announce(f"complex A, workgroup engine case {case}, with h0")
     inp, Ac = _cinputs(batch, L, D, N, io, seed=W.SEED_BASE + 66 + L + N)
@@ -127,11 +124,11 @@ def test_scan_only_no_softplus():
 
 
 @pytest.mark.parametrize("engine", ["default", "lane"])
-def test_long_sequence_is_chunked(engine, monkeypatch):
+def test_long_sequence_is_chunked(engine, request):
     """One row of 8192 tokens over 128 channels: the plan cuts it into chunks whose
     end states are composed through complex carries."""
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     _announce("complex A: (1, 8192, 128, 16) f32, chunked, with h0")
     inp, Ac = _cinputs(1, 8192, 128, 16, "f32", seed=W.SEED_BASE + 62)
     eo, el = check(inp, Ac, h0=_h0(1, 128, 16, 6), label="long")
@@ -247,11 +244,11 @@ def test_decode_continues_the_scan():
 
 
 @pytest.mark.parametrize("engine", ["default", "lane"])
-def test_angles_in_every_sin_cos_range(engine, monkeypatch):
+def test_angles_in_every_sin_cos_range(engine, request):
     """Per-token angles dt Im A_n from below 1/4 rad to ~40 rad, so that waves take the
     short series, the pi/4 series and the reduced evaluation of sin and cos."""
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     rng = np.random.default_rng(12)
     D, N = 128, 16
     Ac = (-rng.uniform(0.2, 3.0, (D, N)) + 1j * rng.uniform(-200.0, 200.0, (D, N))).astype(np.complex64)

@@ -1,15 +1,15 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
 
-Small problems are compared element by element in full; the full-size
-workloads are run whole on the GPU and compared on sampled (batch row,
-channel) pairs, each over the whole sequence, which the oracle computes one
-channel at a time (channels are independent SSMs).  Tolerance: max relative
+Every comparison is element by element over whole tensors: the full-size
+workloads are run whole on the GPU and the oracle covers them in groups of
+channels (channels are independent SSMs), so its host memory stays bounded.
+Tolerance: max relative
 error 1e-4 for fp32 I/O, 2e-2 for bf16 I/O (fp32 state in both cases)."""
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, gpu_scan, parity_error, to_device, to_host
+from gpu_util import TOL, force_engine, gpu_scan, parity_error, to_device, to_host
 from selective_state_space_22_amd import workloads as W
 
 torch = pytest.importorskip("torch")
@@ -65,9 +65,13 @@ def _workload(name):
     return _CACHE[name]
 
 
-def _sampled(name, nchan=24, batches=None, scan_only=False):
+def _full(name, group, scan_only=False):
+    """Run a full-size workload whole on the GPU and compare every output element and
+    every end state with the oracle, which runs over groups of `group` channels
+    (channels are independent SSMs) to bound its host memory."""
     _need_gpu()
-    _announce(f"{name}: full GPU run, sampled oracle channels (scan_only={scan_only})")
+    _announce(f"{name}: full GPU run, whole-tensor oracle comparison in groups of {group} channels "
+              f"(scan_only={scan_only})")
     w = W.WORKLOADS[name]
     inp = _workload(name)
     if scan_only:
@@ -76,38 +80,39 @@ def _sampled(name, nchan=24, batches=None, scan_only=False):
         inp = dataclasses.replace(inp, z=None, Dskip=None)
     go, gl = gpu_scan(inp)
     assert np.isfinite(go).all() and np.isfinite(gl).all()
-    rng = np.random.default_rng(7)
-    chans = np.unique(np.concatenate([[0, 63, 64, w.dim - 1], rng.choice(w.dim, nchan, replace=False)]))
-    bs = batches if batches is not None else sorted({0, w.batch - 1})
-    sub = W.channel_subset(inp, bs, chans)
-    ro, rl = oracle.scan_inputs(sub)
-    eo = parity_error(go[np.ix_(bs, np.arange(w.seqlen), chans)], ro)
-    el = parity_error(gl[np.ix_(bs, chans)], rl)
+    ro = np.empty(go.shape, np.float64)
+    rl = np.empty(gl.shape, np.float64)
+    rows = np.arange(w.batch)
+    for d0 in range(0, w.dim, group):
+        d1 = min(d0 + group, w.dim)
+        ro[:, :, d0:d1], rl[:, d0:d1] = oracle.scan_inputs(W.channel_subset(inp, rows, np.arange(d0, d1)))
+    eo, el = parity_error(go, ro), parity_error(gl, rl)
     tol = TOL[w.io]
-    print(f"{name}: out err {eo:.3e} last err {el:.3e} (tol {tol})")
+    print(f"{name}: out err {eo:.3e} last err {el:.3e} over every element (tol {tol})")
     assert eo <= tol and el <= tol, f"{name}: out {eo:.3e} last {el:.3e}"
 
 
-def test_mamba130m_layer_sampled():
-    _sampled("mamba130m_layer")
+def test_mamba130m_layer_full():
+    _full("mamba130m_layer", group=512)
 
 
-def test_mamba130m_layer_scan_only_sampled():
-    _sampled("mamba130m_layer", scan_only=True)
+def test_mamba130m_layer_scan_only_full():
+    _full("mamba130m_layer", group=512, scan_only=True)
 
 
-def test_mamba3b_layer_sampled():
-    _sampled("mamba3b_layer")
+def test_mamba3b_layer_full():
+    _full("mamba3b_layer", group=512)
 
 
-def test_million_tokens_sampled():
-    _sampled("million_tokens", nchan=6)
+def test_million_tokens_full():
+    _full("million_tokens", group=32)
 
 
 def test_decode_64_steps():
-    """64 one-token steps from a zero state == the scan over the same 64 tokens == the oracle."""
+    """64 one-token steps from a zero state == the scan over the same 64 tokens == the
+    oracle, on every output of every step and every end state."""
     _need_gpu()
-    _announce("decode: 64 steps of (256, 5120, 16) bf16")
+    _announce("decode: 64 steps of (256, 5120, 16) bf16, whole-tensor comparison")
     from selective_state_space_22_amd import mamba_state_update
 
     inp = W.generate_workload("decode")
@@ -126,17 +131,13 @@ def test_decode_64_steps():
     so, sl = gpu_scan(inp, dev_inputs=d)
     # the two GPU entry points agree
     assert parity_error(dec, so) <= TOL["bf16"] and parity_error(st, sl) <= 1e-5
-    # and both agree with the oracle on sampled channels
-    rng = np.random.default_rng(3)
-    chans = np.unique(np.concatenate([[0, D - 1], rng.choice(D, 16, replace=False)]))
-    bs = [0, 97, batch - 1]
-    sub = W.channel_subset(inp, bs, chans)
-    ro, rl = oracle.scan_inputs(sub)
-    eo = parity_error(dec[np.ix_(bs, np.arange(L), chans)], ro)
-    el = parity_error(st[np.ix_(bs, chans)], rl)
-    print(f"decode: out err {eo:.3e} state err {el:.3e}; decode vs scan identical: "
+    # and both agree with the oracle everywhere
+    ro, rl = oracle.scan_inputs(inp)
+    eo, el = parity_error(dec, ro), parity_error(st, rl)
+    eso = parity_error(so, ro)
+    print(f"decode: out err {eo:.3e} state err {el:.3e} scan out err {eso:.3e}; decode vs scan identical: "
           f"{np.array_equal(dec, so)} / {np.array_equal(st, sl)}")
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and eso <= TOL["bf16"]
 
 
 EDGE = [
@@ -161,24 +162,19 @@ EDGE = [
 ENGINES = ["default", "wg", "lane"]
 
 
-def _engine(monkeypatch, engine):
-    """The library picks its engine from the shape; MAMBA_MI355X_LANE_ENGINE=1 forces the
-    lane-per-channel engine and MAMBA_MI355X_WG_ENGINE=1 the workgroup engine (waves split
-    the states) in place of the wave-private one, so that every engine is covered on the
-    same cases."""
-    monkeypatch.delenv("MAMBA_MI355X_LANE_ENGINE", raising=False)
-    monkeypatch.delenv("MAMBA_MI355X_WG_ENGINE", raising=False)
-    if engine == "lane":
-        monkeypatch.setenv("MAMBA_MI355X_LANE_ENGINE", "1")
-    elif engine == "wg":
-        monkeypatch.setenv("MAMBA_MI355X_WG_ENGINE", "1")
+def _engine(request, engine):
+    """The library picks its engine from the shape; the engine option forces the
+    lane-per-channel engine ("lane"), the workgroup engine whose waves split the states
+    ("wg") or leaves the choice to the library ("default", the wave-private engine for
+    N = 8 and 16), so that every engine is covered on the same cases."""
+    force_engine(request, engine)
 
 
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("case", EDGE, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}_{i}" for i, c in enumerate(EDGE)])
-def test_edge_cases(case, engine, monkeypatch):
+def test_edge_cases(case, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     batch, L, D, N, io, kw = case
     _announce(f"edge case {case} engine={engine}")
     inp = W.generate(batch, L, D, N, io, seed=500 + L + D + N, **kw)
@@ -202,9 +198,9 @@ WG_CASES = [
 
 @pytest.mark.parametrize("engine", ["default", "wg"])
 @pytest.mark.parametrize("case", WG_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in WG_CASES])
-def test_workgroup_engine_modes(case, engine, monkeypatch):
+def test_workgroup_engine_modes(case, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     batch, L, D, N, io = case
     _announce(f"workgroup engine case {case} engine={engine}")
     inp = W.generate(batch, L, D, N, io, seed=900 + L + D + N)
@@ -214,20 +210,56 @@ def test_workgroup_engine_modes(case, engine, monkeypatch):
 
 @pytest.mark.parametrize("engine", ["default", "wg"])
 @pytest.mark.parametrize("case", [(5, 1100, 4096, 16, "f32"), (1, 4096, 64, 16, "f32")], ids=["chained", "split"])
-def test_workgroup_engine_initial_state(case, engine, monkeypatch):
+def test_workgroup_engine_initial_state(case, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     batch, L, D, N, io = case
     inp = W.generate(batch, L, D, N, io, seed=77)
     h0 = np.random.default_rng(78).standard_normal((batch, D, N)).astype(np.float32)
     check(inp, h0=h0, label=f"h0 {case}")
 
 
+def test_chained_wait_timeout_is_reported(request):
+    """A chained chunk whose wait for its predecessor's end state gives up must say so:
+    with the wait bound set to 0 every chunk after the first gives up at once, the
+    stream status reports MAMBA_ERR_TIMEOUT (and the binding raises), those chunks'
+    outputs and the end states are NaN, and the first chunk's outputs still match the
+    oracle.  The status is cleared by the query, and the next call with the default
+    bound is clean and correct."""
+    _need_gpu()
+    from gpu_util import library_option
+    from selective_state_space_22_amd import binding, mamba_scan_fwd
+
+    force_engine(request, "wg")
+    batch, L, D, N, io = 5, 1100, 4096, 16, "f32"   # 320 channel blocks: chained, chunks of 256
+    _announce(f"chained wait with bound 0 on {(batch, L, D, N, io)}")
+    inp = W.generate(batch, L, D, N, io, seed=31)
+    d = to_device(inp)
+    assert binding.mamba_stream_status() == 0
+    with library_option(binding.MAMBA_OPT_CHUNK, 256), library_option(binding.MAMBA_OPT_SPIN_LIMIT, 0):
+        with pytest.raises(binding.MambaError) as ex:
+            mamba_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["delta_bias"], d["Dskip"], d["z"], True,
+                           check=True)
+        assert ex.value.status == binding.MAMBA_ERR_TIMEOUT
+        assert binding.mamba_stream_status() == 0  # reported once
+        out, last = mamba_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["delta_bias"], d["Dskip"], d["z"],
+                                   True)
+        assert binding.mamba_stream_status() == binding.MAMBA_ERR_TIMEOUT
+        go, gl = to_host(out), to_host(last)
+    ro, _ = oracle.scan_inputs(inp)
+    assert np.isnan(go[:, 256:]).all() and np.isnan(gl).all()
+    assert parity_error(go[:, :256], ro[:, :256]) <= TOL[io]
+    # the default bound: every wait ends, the status stays clear
+    with library_option(binding.MAMBA_OPT_CHUNK, 256):
+        check(inp, label="chained after a timeout")
+    assert binding.mamba_stream_status() == 0
+
+
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("chunked", [False, True])
-def test_initial_state(chunked, engine, monkeypatch):
+def test_initial_state(chunked, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     L = 4096 if chunked else 200
     inp = W.generate(2, L, 64, 16, "f32", seed=71)
     h0 = np.random.default_rng(72).standard_normal((2, 64, 16)).astype(np.float32)
@@ -266,9 +298,9 @@ def _run(inp, **kw):
 
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("L", [300, 3000])
-def test_causality_bit_exact(L, engine, monkeypatch):
+def test_causality_bit_exact(L, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     inp = W.generate(2, L, 128, 16, "f32", seed=80)
     o1, _ = _run(inp)
     t0 = L // 2 + 3
@@ -283,10 +315,10 @@ def test_causality_bit_exact(L, engine, monkeypatch):
 
 
 @pytest.mark.parametrize("engine", ENGINES)
-def test_hold_is_exact(engine, monkeypatch):
+def test_hold_is_exact(engine, request):
     """dt = 0 (no softplus, raw = -bias) keeps the state bit-exactly."""
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     inp = W.generate(2, 400, 64, 16, "f32", seed=81)
     inp.delta = np.broadcast_to(-inp.delta_bias, inp.u.shape).astype(np.float32).copy()
     h0 = np.random.default_rng(82).standard_normal((2, 64, 16)).astype(np.float32)
@@ -298,9 +330,9 @@ def test_hold_is_exact(engine, monkeypatch):
 
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("L", [200, 3000])
-def test_reset_forgets_the_prefix_exactly(L, engine, monkeypatch):
+def test_reset_forgets_the_prefix_exactly(L, engine, request):
     _need_gpu()
-    _engine(monkeypatch, engine)
+    _engine(request, engine)
     inp = W.generate(1, L, 64, 16, "f32", seed=83)
     tr = L // 2 + 11
     inp.delta[:, tr] = 60.0  # dt*A <= -60 * log2(e): Abar underflows to exactly 0

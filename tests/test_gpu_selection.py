@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, parity_error, to_device, to_host, torch_io
+from gpu_util import TOL, library_option, parity_error, to_device, to_host, torch_io
+from selective_state_space_22_amd import binding
 from selective_state_space_22_amd import workloads as W
 
 torch = pytest.importorskip("torch")
@@ -104,13 +105,15 @@ SSM_CASES = [
 
 @pytest.mark.parametrize("fused", ["on", "off"])
 @pytest.mark.parametrize("case", SSM_CASES, ids=str)
-def test_ssm_matches_selection_then_scan_oracle(case, fused, monkeypatch):
+def test_ssm_matches_selection_then_scan_oracle(case, fused, request):
     _need_gpu()
     from selective_state_space_22_amd import mamba_ssm_fwd
 
     batch, L, D, N, io, R = case
     R = R or W.dt_rank_for(D)
-    monkeypatch.setenv("MAMBA_MI355X_FUSED_DT", "1" if fused == "on" else "0")
+    cm = library_option(binding.MAMBA_OPT_FUSED_DT, 1 if fused == "on" else 0)
+    cm.__enter__()
+    request.addfinalizer(lambda: cm.__exit__(None, None, None))
     _announce(f"ssm (selection + scan) {case} R {R} fused={fused}")
     inp, sw = _inputs(batch, L, D, N, R, io, seed=400 + L)
     d = to_device(inp)
