@@ -152,6 +152,29 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward selective scan for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and errors as for mamba_scan_fwd, without
+ * the workspace: the scratch it needs comes from a fixed array of
+ * MAMBA_SCAN_FWD_NOALLOC_MAX_WORKSPACE bytes in the library's device image,
+ * one copy per GPU, held by each GPU the library runs on until the process
+ * ends.  The call allocates nothing.
+ *   Returns MAMBA_ERR_WORKSPACE, before anything is enqueued, when
+ *   mamba_scan_fwd_workspace_size(...) exceeds that size.
+ *   stream must belong to the current device; the copy of that device is used.
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind (the kernels clear what must start at zero): calls whose work can
+ *   overlap on one GPU (other streams, other host threads) race on it and must
+ *   be serialised by the caller.
+ */
+#define MAMBA_SCAN_FWD_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+int mamba_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, int io_dtype,
+                           const void* u, const void* delta, const float* delta_bias, const float* A,
+                           const void* B, const void* C, const float* Dskip, const void* z,
+                           int delta_softplus, const float* h0,
+                           void* out, float* last_state, void* stream);
+
+/*
  * Forward selective scan with a complex diagonal A: the complex row
  * A_n = -1/2 + n i of the A-initialisation ablation (section 6.5).  dt, u,
  * B, C, z and out stay real; eq. (2) and (3a) are taken over the complex

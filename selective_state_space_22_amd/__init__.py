@@ -10,7 +10,7 @@ from .binding import (MAMBA_IO_BF16, MAMBA_IO_F32, MambaError, load_library, mam
                       mamba_get_option, mamba_set_option, mamba_stream_status,
                       mamba_block_fwd_workspace_size, mamba_scan_bwd,
                       mamba_scan_bwd_workspace_size, mamba_scan_fwd, mamba_scan_fwd_complex,
-                      mamba_scan_fwd_complex_workspace_size, mamba_scan_fwd_workspace_size,
+                      mamba_scan_fwd_complex_workspace_size, mamba_scan_fwd_noalloc, mamba_scan_fwd_workspace_size,
                       mamba_selection_fwd, mamba_selection_fwd_workspace_size, mamba_ssm_fwd,
                       mamba_ssm_fwd_workspace_size, mamba_state_update, mamba_state_update_complex, mamba_version,
                       status_string)
@@ -19,4 +19,5 @@ __all__ = ["mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_scan_fwd"
            "mamba_state_update", "mamba_state_update_complex", "mamba_scan_fwd_workspace_size",
            "mamba_scan_bwd_workspace_size", "mamba_selection_fwd", "mamba_selection_fwd_workspace_size",
            "mamba_ssm_fwd", "mamba_ssm_fwd_workspace_size", "mamba_version", "status_string", "load_library", "MambaError",
-           "MAMBA_IO_F32", "MAMBA_IO_BF16", "mamba_set_option", "mamba_get_option", "mamba_stream_status"]
+           "MAMBA_IO_F32", "MAMBA_IO_BF16", "mamba_set_option", "mamba_get_option", "mamba_stream_status",
+           "mamba_scan_fwd_noalloc"]

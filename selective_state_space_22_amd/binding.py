@@ -84,6 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_block_fwd_workspace_size.restype = ctypes.c_size_t
     lib.mamba_block_fwd.argtypes = [I64] * 6 + [I] + [P] * 8 + [I, P, P, P, P, ctypes.c_size_t, P]
     lib.mamba_block_fwd.restype = I
+    lib.mamba_scan_fwd_noalloc.argtypes = [I64, I64, I64, I64, I, P, P, P, P, P, P, P, P, I, P, P, P, P]
+    lib.mamba_scan_fwd_noalloc.restype = I
     lib.mamba_set_option.argtypes = [I, I64]
     lib.mamba_set_option.restype = I
     lib.mamba_get_option.argtypes = [I]
@@ -203,6 +205,42 @@ def mamba_scan_fwd(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta
         raise MambaError("mamba_scan_fwd", st)
     if check:
         _check_status("mamba_scan_fwd", dev)
+    return out, last_state
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20  # MAMBA_SCAN_FWD_NOALLOC_MAX_WORKSPACE
+
+
+def mamba_scan_fwd_noalloc(u, delta, A, B, C, delta_bias=None, Dskip=None, z=None, delta_softplus=True, h0=None,
+                           out=None, last_state=None, check=False):
+    """mamba_scan_fwd through the entry point that allocates no device memory: its
+    workspace is the library's fixed per-GPU scratch array.  Pass `out` (and
+    `last_state`, or None to skip it) to allocate nothing here either; raises
+    MambaError (MAMBA_ERR_WORKSPACE) when the shape needs more scratch than the
+    array holds.  Calls that overlap on one GPU share that array and race."""
+    import torch
+
+    lib = load_library()
+    batch, L, D = u.shape
+    N = A.shape[1]
+    io = _io_dtype(u)
+    dev = u.device
+    f32 = torch.float32
+    if out is None:
+        out = torch.empty_like(u)
+    st = lib.mamba_scan_fwd_noalloc(
+        batch, L, D, N, io,
+        _ptr(u, "u", u.dtype, (batch, L, D), dev), _ptr(delta, "delta", u.dtype, (batch, L, D), dev),
+        _ptr(delta_bias, "delta_bias", f32, (D,), dev), _ptr(A, "A", f32, (D, N), dev),
+        _ptr(B, "B", u.dtype, (batch, L, N), dev), _ptr(C, "C", u.dtype, (batch, L, N), dev),
+        _ptr(Dskip, "Dskip", f32, (D,), dev), _ptr(z, "z", u.dtype, (batch, L, D), dev),
+        int(bool(delta_softplus)), _ptr(h0, "h0", f32, (batch, D, N), dev),
+        _ptr(out, "out", u.dtype, (batch, L, D), dev), _ptr(last_state, "last_state", f32, (batch, D, N), dev),
+        _stream(dev))
+    if st != 0:
+        raise MambaError("mamba_scan_fwd_noalloc", st)
+    if check:
+        _check_status("mamba_scan_fwd_noalloc", dev)
     return out, last_state
 
 

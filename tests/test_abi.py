@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_get_option", "mamba_scan_bwd",
         "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_complex",
-        "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_workspace_size", "mamba_selection_fwd",
+        "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_workspace_size",
+        "mamba_selection_fwd",
         "mamba_selection_fwd_workspace_size", "mamba_set_option", "mamba_ssm_fwd", "mamba_ssm_fwd_workspace_size",
         "mamba_state_update", "mamba_state_update_complex", "mamba_status_string", "mamba_stream_status",
         "mamba_version"])
@@ -119,6 +120,21 @@ def test_workspace_follows_the_engine_option(lib, restore_options):
     assert ws(*shape) > 0
     binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["auto"])
     assert ws(*shape) == auto
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib, restore_options):
+    """The no-allocation scan checks the workspace the shape needs against its fixed
+    scratch array on the host, before the HIP runtime is touched."""
+    assert binding.NOALLOC_MAX_WORKSPACE == 32 << 20
+    binding.mamba_set_option(binding.MAMBA_OPT_ENGINE, binding.ENGINES["wg"])
+    batch, L, D, N = 64, 1, 16384, 16   # 16 k chained channel blocks: 64 MiB of flags and carries
+    assert binding.mamba_scan_fwd_workspace_size(batch, L, D, N, 0) > binding.NOALLOC_MAX_WORKSPACE
+    st = lib.mamba_scan_fwd_noalloc(batch, L, D, N, 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 1, None,
+                                    FAKE, None, None)
+    assert st == ERR_WORKSPACE
+    # shapes that mamba_scan_fwd rejects keep their own status
+    assert lib.mamba_scan_fwd_noalloc(1, 8, 64, 3, 0, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 1, None,
+                                      FAKE, None, None) == ERR_UNSUPPORTED
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced
 
