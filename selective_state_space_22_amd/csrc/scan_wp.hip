@@ -63,6 +63,9 @@ namespace {
 #ifndef S6_WP_PD
 #define S6_WP_PD 4  // tiles of global loads in flight per wave (N = 16)
 #endif
+#ifndef S6_WP_YPSINGLE
+#define S6_WP_YPSINGLE 1  // partial readouts stored one token at a time
+#endif
 #ifndef S6_WP_WPE
 #define S6_WP_WPE 3  // occupancy hint: waves per SIMD
 #endif
@@ -78,6 +81,16 @@ struct WpArgs {
   int32_t nblk;   // 64-channel blocks per batch row
   int32_t units;  // (chunk, batch row, block) units of this launch
 };
+
+// Values that are the same in every lane, kept in scalar registers (the
+// compiler cannot always prove it, and a buffer resource in vector registers
+// costs a loop over the lanes at every access).
+__device__ __forceinline__ uint32_t wp_uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ const char* wp_uniform(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = wp_uniform((uint32_t)v), hi = wp_uniform((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(lo | (hi << 32));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wp_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kWpBufferDword3);
@@ -197,9 +210,16 @@ struct WpScan {
   int64_t b, t0, t1;
   int g;
   int64_t dscan, dfront;
-  uint32_t chan_off;  // byte offset of the front lane's channel in a token row (out of range if >= D)
-  uint32_t row_bytes, out_off;  // token row in bytes; this lane's offset in the output (out of range if >= D)
-  __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_out, r_B, r_C;
+  uint32_t row_bytes;  // one token row of u, delta, z, out in bytes
+  // Byte offset of token slot i of a tile (token fq + P i, the front lane's
+  // channel) from the tile's first row; out of range for channels >= D.
+  uint32_t voff[TQ];
+  uint32_t bc_off;  // this lane's B / C chunks from the tile's first row
+  // Chunk bases and spans in bytes; each tile gets buffer resources based at its
+  // first row, so that the tile's position costs scalar instructions only and
+  // rows past the chunk still fall outside the resource.
+  const char *p_u, *p_dl, *p_z, *p_out, *p_B, *p_C;
+  uint32_t span, zspan, ospan, bspan;
   float a2[S], ka[S], ah[S], h[S];
   float bias, dskip;
   float dsum, dcomp;  // compensated sum of dt (first pass of the split scan)
@@ -222,22 +242,30 @@ struct WpScan {
   // Global loads of tile k (rows past the chunk and channels past D read zero).
   // B / C: lane l stages the chunks NQ l + q of the tile, chunk = (token, state
   // pair), i.e. the state pair's two elements, contiguous in memory.
+  // Buffer resource of tile k of a tensor whose chunk starts at base and spans span bytes.
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t span, uint32_t off) {
+    // spans are below 2^31: a signed difference clamped at zero (scalar max, where
+    // an unsigned saturating subtraction would be a vector instruction)
+    const int32_t left = (int32_t)span - (int32_t)off;
+    return wp_rsrc(base + off, (uint32_t)(left > 0 ? left : 0));
+  }
+
   __device__ __forceinline__ void load(Regs& r, int k) const {
-    const uint32_t row = (uint32_t)(A.s.D * kIo);
-    const uint32_t base = chan_off + (uint32_t)(k * T + fq) * row;
+    const uint32_t toff = (uint32_t)(k * T) * row_bytes;
+    const __amdgpu_buffer_rsrc_t r_dl = tile_rsrc(p_dl, span, toff), r_u = tile_rsrc(p_u, span, toff);
+    const __amdgpu_buffer_rsrc_t r_z = tile_rsrc(p_z, zspan, toff);
 #pragma unroll
     for (int i = 0; i < TQ; ++i) {
-      const uint32_t off = base + (uint32_t)(P * i) * row;
-      r.dl[i] = WpIo<IO>::load(r_dl, off);
-      r.uu[i] = WpIo<IO>::load(r_u, off);
-      if (kOut) r.zz[i] = WpIo<IO>::load(r_z, off);
+      r.dl[i] = WpIo<IO>::load(r_dl, voff[i]);
+      r.uu[i] = WpIo<IO>::load(r_u, voff[i]);
+      if (kOut) r.zz[i] = WpIo<IO>::load(r_z, voff[i]);
     }
     // this lane's NQ chunks are consecutive (chunks NQ l .. NQ l + NQ - 1): one load per tensor
     {
       uint32_t bw[NQ * DPC], cw[NQ * DPC];
-      const uint32_t boff = (uint32_t)(k * T * N + 2 * NQ * lane) * kIo;
-      load_dwords<NQ * DPC>(bw, r_B, boff);
-      if (kOut) load_dwords<NQ * DPC>(cw, r_C, boff);
+      const uint32_t bt = (uint32_t)(k * T * N) * kIo;
+      load_dwords<NQ * DPC>(bw, tile_rsrc(p_B, bspan, bt), bc_off);
+      if (kOut) load_dwords<NQ * DPC>(cw, tile_rsrc(p_C, bspan, bt), bc_off);
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -288,6 +316,17 @@ struct WpScan {
     }
   }
 
+  // Partial readout of token row j.  One 4-byte store per token: the row's
+  // position is then an immediate offset (paired stores of two rows would need
+  // an address computed per pair).
+  __device__ __forceinline__ void yp_store(int j, float v) {
+#if S6_WP_YPSINGLE
+    *(volatile __attribute__((address_space(3))) float*)(&sm.yp[j][ypos(sc, sg)]) = v;
+#else
+    sm.yp[j][ypos(sc, sg)] = v;
+#endif
+  }
+
   // BT tokens at a time: their input terms (Abar, beta B x) first, then the
   // recurrence steps and partial readouts, so a wave has independent work in flight.
   template <int BT>
@@ -306,7 +345,7 @@ struct WpScan {
     for (int q = 0; q < BT; ++q) {
       h[0] = __builtin_fmaf(ab[q][0], h[0], in[q][0]);
       h[1] = __builtin_fmaf(ab[q][1], h[1], in[q][1]);
-      if (kOut) sm.yp[j + q][ypos(sc, sg)] = __builtin_fmaf(bv[q].w, h[1], bv[q].z * h[0]);
+      if (kOut) yp_store(j + q, __builtin_fmaf(bv[q].w, h[1], bv[q].z * h[0]));
     }
   }
 
@@ -320,7 +359,7 @@ struct WpScan {
       h[s] = __builtin_fmaf(abar, h[s], beta * ((s == 0 ? bv.x : bv.y) * fv.z));
       y = s == 0 ? bv.z * h[0] : __builtin_fmaf(bv.w, h[1], y);
     }
-    if (kOut) sm.yp[j][ypos(sc, sg)] = y;
+    if (kOut) yp_store(j, y);
   }
 
   // Recurrence over rows [P p, P p + P) of a full tile in slot f; partial readouts to yp.
@@ -374,7 +413,7 @@ struct WpScan {
     }
     const float4 fv = lds_read16(&sm.fr[f][j][fc]);
     const float o = s6::epilogue(y, fv.z, dskip, A.s.z != nullptr, fv.w);
-    WpIo<IO>::store(o, r_out, out_off + (uint32_t)(k * T + P * i) * row_bytes);
+    WpIo<IO>::store(o, tile_rsrc(p_out, ospan, (uint32_t)(k * T) * row_bytes), voff[i]);
   }
 
   // Raw global data of PD tiles is in flight per wave (a ring of registers): the
@@ -443,20 +482,27 @@ struct WpScan {
     const bool svalid = dscan < A.s.D, fvalid = dfront < A.s.D;
     t0 = (int64_t)g * A.s.chunk_len;
     t1 = t0 + A.s.chunk_len < A.s.L ? t0 + A.s.chunk_len : A.s.L;
-    chan_off = fvalid ? (uint32_t)(dfront * kIo) : kWpOutOfRange;
-    row_bytes = (uint32_t)(A.s.D * kIo);
-    out_off = chan_off + (uint32_t)fq * row_bytes;
+    row_bytes = wp_uniform((uint32_t)(A.s.D * kIo));
     {
+      const uint32_t chan_off = fvalid ? (uint32_t)(dfront * kIo) : kWpOutOfRange;
+#pragma unroll
+      for (int i = 0; i < TQ; ++i) voff[i] = chan_off + (uint32_t)(fq + P * i) * row_bytes;
+      bc_off = (uint32_t)(2 * NQ * lane) * kIo;
       const size_t row0 = ((size_t)b * A.s.L + t0);
-      const uint32_t span = (uint32_t)((t1 - t0) * A.s.D * kIo);
-      const uint32_t bspan = (uint32_t)((t1 - t0) * N * kIo);
-      r_u = wp_rsrc(static_cast<const IO*>(A.s.u) + row0 * A.s.D, span);
-      r_dl = wp_rsrc(static_cast<const IO*>(A.s.delta) + row0 * A.s.D, span);
-      r_z = wp_rsrc(A.s.z ? static_cast<const IO*>(A.s.z) + row0 * A.s.D : static_cast<const IO*>(A.s.u),
-                    A.s.z ? span : 0u);
-      r_out = wp_rsrc(static_cast<const IO*>(A.s.out) + row0 * A.s.D, kOut ? span : 0u);
-      r_B = wp_rsrc(static_cast<const IO*>(A.s.B) + row0 * N, bspan);
-      r_C = wp_rsrc(static_cast<const IO*>(A.s.C) + row0 * N, bspan);
+      span = (uint32_t)((t1 - t0) * A.s.D * kIo);
+      bspan = (uint32_t)((t1 - t0) * N * kIo);
+      zspan = A.s.z ? span : 0u;
+      ospan = kOut ? span : 0u;
+      p_u = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.u) + row0 * A.s.D));
+      p_dl = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.delta) + row0 * A.s.D));
+      p_z = A.s.z ? wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.z) + row0 * A.s.D)) : p_u;
+      p_out = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.out) + row0 * A.s.D));
+      p_B = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.B) + row0 * N));
+      p_C = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.C) + row0 * N));
+      span = wp_uniform(span);
+      bspan = wp_uniform(bspan);
+      zspan = wp_uniform(zspan);
+      ospan = wp_uniform(ospan);
     }
     const int n0 = S * sg;
 #pragma unroll
