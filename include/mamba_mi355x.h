@@ -152,6 +152,22 @@ int mamba_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate, i
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement utility, not part of the scan: a plain streaming copy of `bytes`
+ * bytes (a multiple of 16, both pointers 16-byte aligned, device memory),
+ * enqueued on `stream`.  It is the measured HBM read+write reference against
+ * which the memory-bound decode step is compared.
+ *   blocks > 0 : that many workgroups of 256 threads in a grid-stride loop
+ *   blocks = 0 : one pass, each workgroup over 16 KB contiguous
+ *   blocks = -1: the same with non-temporal loads and stores
+ *   blocks = -2: in place, dst read and written back (src unused; the access
+ *                pattern of the decode step's state)
+ *   blocks = -3: the same with non-temporal loads and stores
+ * Returns MAMBA_ERR_NULL, MAMBA_ERR_ALIGN or MAMBA_ERR_DIM (blocks above 2^20 or
+ * below -3) before enqueueing anything, MAMBA_ERR_HIP if the launch fails.
+ */
+int mamba_calibrate_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream);
+
+/*
  * Forward selective scan for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  Arguments, results and errors as for mamba_scan_fwd, without

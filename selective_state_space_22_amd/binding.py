@@ -86,6 +86,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mamba_block_fwd.restype = I
     lib.mamba_scan_fwd_noalloc.argtypes = [I64, I64, I64, I64, I, P, P, P, P, P, P, P, P, I, P, P, P, P]
     lib.mamba_scan_fwd_noalloc.restype = I
+    lib.mamba_calibrate_copy.argtypes = [P, P, ctypes.c_size_t, I, P]
+    lib.mamba_calibrate_copy.restype = I
     lib.mamba_set_option.argtypes = [I, I64]
     lib.mamba_set_option.restype = I
     lib.mamba_get_option.argtypes = [I]
@@ -124,6 +126,17 @@ def mamba_stream_status(device=None) -> int:
 
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
     return int(load_library().mamba_stream_status(_stream(dev)))
+
+
+def mamba_calibrate_copy(src, dst, blocks=2048):
+    """Streaming copy of src into dst (same size, device tensors) with the library's
+    hand-written copy kernel: the HBM reference of the memory-bound kernels."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_cuda or not dst.is_cuda:
+        raise ValueError("src and dst must be device tensors of one size")
+    st = load_library().mamba_calibrate_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(blocks), _stream(src.device))
+    if st != 0:
+        raise MambaError("mamba_calibrate_copy", st)
 
 
 def _check_status(func, device):

@@ -393,8 +393,8 @@ hipError_t launch_scan(const ScanArgs& in, const ScanPlan& p, int io, int N, voi
 
 // ----------------------------------------------------------------- decode
 
-// One token for every (batch, channel): lane = channel d of batch row
-// blockIdx.y, all N states read and written in place as float4.  B_t and C_t
+// One token for every (batch, channel), N = 1 and 2: lane = channel d of batch
+// row blockIdx.y, all N states read and written in place.  B_t and C_t
 // of the row are shared by the row's channels (page section 3.2): they are read
 // once per wave through the scalar cache (whole dwords through the constant
 // address space: the kernel never writes them), A as float4.
@@ -471,15 +471,112 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
   }
 }
 
+// The same step with four states per lane (N = 4, 8, 16): the N / 4 lanes of a
+// channel are adjacent, so a wave's state loads and stores cover one
+// contiguous 1 KB run per instruction (a lane that owned all N states would
+// read them as N / 4 float4s at a 4 N-byte lane stride).  Each lane evaluates
+// the channel's front end itself (dt, x and z are per channel, read by all its
+// lanes at one address); the readout is summed over the channel's lanes with
+// quad lane swaps.
+#ifndef S6_DECODE_ROUNDS
+#define S6_DECODE_ROUNDS 2  // channel groups per lane (their loads are issued together)
+#endif
+#ifndef S6_DECODE_NT
+#define S6_DECODE_NT 3  // non-temporal state loads (bit 0) and stores (bit 1)
+#endif
+typedef float dec_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 dec_load_state(const float* p) {
+  const dec_f32x4 v = (S6_DECODE_NT & 1) ? __builtin_nontemporal_load(reinterpret_cast<const dec_f32x4*>(p))
+                                   : *reinterpret_cast<const dec_f32x4*>(p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void dec_store_state(float* p, float a, float b, float c, float d) {
+  const dec_f32x4 v = {a, b, c, d};
+  if (S6_DECODE_NT & 2) __builtin_nontemporal_store(v, reinterpret_cast<dec_f32x4*>(p));
+  else *reinterpret_cast<dec_f32x4*>(p) = v;
+}
+
+template <typename IO, int N>
+__global__ __launch_bounds__(256) void state_update_vec_kernel(StepArgs a) {
+  constexpr int LPC = N / 4;      // lanes per channel
+  constexpr int CPB = 256 / LPC;  // channels per block and round
+  constexpr int R = S6_DECODE_ROUNDS;
+  static_assert(N % 4 == 0 && LPC <= 4, "four states per lane");
+  const int q = threadIdx.x % LPC;
+  const int64_t b = blockIdx.y;
+  const int n0 = 4 * q;
+  float Bt[4], Ct[4];
+  if constexpr (sizeof(IO) == 2) {
+    const uint2 wb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.B) + b * N + n0);
+    const uint2 wc = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.C) + b * N + n0);
+    Bt[0] = bf16_lo(wb.x); Bt[1] = bf16_hi(wb.x); Bt[2] = bf16_lo(wb.y); Bt[3] = bf16_hi(wb.y);
+    Ct[0] = bf16_lo(wc.x); Ct[1] = bf16_hi(wc.x); Ct[2] = bf16_lo(wc.y); Ct[3] = bf16_hi(wc.y);
+  } else {
+    const float4 vb = *reinterpret_cast<const float4*>(static_cast<const float*>(a.B) + b * N + n0);
+    const float4 vc = *reinterpret_cast<const float4*>(static_cast<const float*>(a.C) + b * N + n0);
+    Bt[0] = vb.x; Bt[1] = vb.y; Bt[2] = vb.z; Bt[3] = vb.w;
+    Ct[0] = vc.x; Ct[1] = vc.y; Ct[2] = vc.z; Ct[3] = vc.w;
+  }
+  // every round's loads first
+  int64_t d[R];
+  bool ok[R];
+  float4 hv[R], qa[R];
+  float xr[R], dr[R], zr[R];
+  const bool has_z = a.z != nullptr;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    d[r] = ((int64_t)blockIdx.x * R + r) * CPB + threadIdx.x / LPC;
+    ok[r] = d[r] < a.D;  // whole channels (all LPC lanes of a channel) agree
+    const int64_t dd = ok[r] ? d[r] : 0;
+    const int64_t idx = b * a.D + dd;
+    hv[r] = ok[r] ? dec_load_state(a.state + (size_t)idx * N + n0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    qa[r] = *reinterpret_cast<const float4*>(a.A + dd * N + n0);
+    xr[r] = load_io(static_cast<const IO*>(a.u), idx);
+    dr[r] = load_io(static_cast<const IO*>(a.delta), idx);
+    zr[r] = has_z ? load_io(static_cast<const IO*>(a.z), idx) : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t dd = ok[r] ? d[r] : 0;
+    const int64_t idx = b * a.D + dd;
+    float h[4] = {hv[r].x, hv[r].y, hv[r].z, hv[r].w};
+    const float av[4] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w};
+    ChanConst<4> cc;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      cc.a2[n] = av[n] * kLog2e;
+      cc.ka[n] = rcp(av[n]);
+      cc.ah[n] = 0.5f * av[n];
+    }
+    const TokenFront f = make_front(dr[r], a.bias ? a.bias[dd] : 0.0f, a.softplus != 0);
+    float y = token_step<4>(cc, f, xr[r], Bt, Ct, h);
+    // sum over the channel's lanes: (q0 + q1) + (q2 + q3), the same in every lane
+    if constexpr (LPC >= 2) y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, false));
+    if constexpr (LPC == 4) y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, false));
+    if (ok[r]) {
+      dec_store_state(a.state + (size_t)idx * N + n0, h[0], h[1], h[2], h[3]);
+      if (q == 0)
+        store_io(static_cast<IO*>(a.out), idx, epilogue(y, xr[r], a.dskip ? a.dskip[dd] : 0.0f, has_z, zr[r]));
+    }
+  }
+}
+
+template <typename IO, int N>
+static void launch_step_vec(const StepArgs& a, hipStream_t s) {
+  constexpr int CPB = 256 / (N / 4) * S6_DECODE_ROUNDS;  // channels per block
+  const dim3 grid((unsigned)((a.D + CPB - 1) / CPB), (unsigned)a.batch);
+  hipLaunchKernelGGL((state_update_vec_kernel<IO, N>), grid, dim3(256), 0, s, a);
+}
+
 template <typename IO>
 static hipError_t launch_step_io(const StepArgs& a, int N, hipStream_t s) {
   const dim3 grid((unsigned)((a.D + 255) / 256), (unsigned)a.batch);
   switch (N) {
     case 1: hipLaunchKernelGGL((state_update_kernel<IO, 1>), grid, dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((state_update_kernel<IO, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((state_update_kernel<IO, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((state_update_kernel<IO, 8>), grid, dim3(256), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((state_update_kernel<IO, 16>), grid, dim3(256), 0, s, a); break;
+    case 4: launch_step_vec<IO, 4>(a, s); break;
+    case 8: launch_step_vec<IO, 8>(a, s); break;
+    case 16: launch_step_vec<IO, 16>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

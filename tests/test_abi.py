@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_get_option", "mamba_scan_bwd",
+        "mamba_block_fwd", "mamba_block_fwd_workspace_size", "mamba_calibrate_copy", "mamba_get_option", "mamba_scan_bwd",
         "mamba_scan_bwd_workspace_size", "mamba_scan_fwd", "mamba_scan_fwd_complex",
         "mamba_scan_fwd_complex_workspace_size", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_workspace_size",
         "mamba_selection_fwd",
