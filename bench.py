@@ -148,7 +148,7 @@ def measured_traffic(workload, which="fwd"):
         return None
 
 
-def calibrate_copy(torch, dev, mib, steps, flush):
+def calibrate_copy(torch, dev, mib, steps, flush, settle_ms):
     """HBM reference for the memory-bound kernels: the library's hand-written
     streaming copy (and torch's copy_) of mib MiB, each launch reading and writing
     mib MiB, warm or with the Infinity Cache evicted before every launch; one JSON
@@ -171,7 +171,7 @@ def calibrate_copy(torch, dev, mib, steps, flush):
         for _ in range(3):
             fn()
         # settle the clock as for the scan
-        t_end = time.perf_counter() + 0.1
+        t_end = time.perf_counter() + settle_ms / 1e3
         while time.perf_counter() < t_end:
             fn()
         torch.cuda.synchronize()
@@ -233,7 +233,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
-        calibrate_copy(torch, dev, args.calibrate_copy, args.steps, args.flush)
+        calibrate_copy(torch, dev, args.calibrate_copy, args.steps, args.flush, args.settle_ms)
         return
     w = W.WORKLOADS[args.workload]
     if args.which != "fwd" and w.decode_steps > 0:
