@@ -59,7 +59,8 @@ struct Options {
     v[s6::kOptFusedDt].store(env_value("MAMBA_MI355X_FUSED_DT", 0) == 1 ? 1 : 0);
     v[s6::kOptBwdChunk].store(env_value("MAMBA_MI355X_BWD_CHUNK", 0));
     v[s6::kOptGemmGeneral].store(std::getenv("MAMBA_MI355X_GEMM_GENERAL") ? 1 : 0);
-    v[s6::kOptSpinLimit].store(kDefaultSpinLimit);
+    const int64_t spin = env_value("MAMBA_MI355X_SPIN_LIMIT", kDefaultSpinLimit);
+    v[s6::kOptSpinLimit].store(spin <= 0xffffffffll ? spin : kDefaultSpinLimit);
   }
 };
 
