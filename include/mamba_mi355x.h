@@ -79,7 +79,7 @@ const char* mamba_status_string(int status);
  * first used, from the environment variable named in brackets; the defaults
  * are the fastest measured settings.  Setting options is not synchronised with
  * calls in flight on other threads.  Not part of the method: no option changes
- * what is computed, only how.
+ * what is computed beyond fp32 rounding, only how.
  */
 enum mamba_option {
   MAMBA_OPT_ENGINE = 1,       /* forward engine for dstate 8 and 16: 0 automatic, 1 one lane per
@@ -95,9 +95,14 @@ enum mamba_option {
                                  from the shape [MAMBA_MI355X_BWD_CHUNK]                         */
   MAMBA_OPT_GEMM_GENERAL = 6, /* 1: the projections use only the general GEMM kernel
                                  [MAMBA_MI355X_GEMM_GENERAL]                                     */
-  MAMBA_OPT_SPIN_LIMIT = 7    /* polls a chunk makes for its predecessor's end state before it
+  MAMBA_OPT_SPIN_LIMIT = 7,   /* polls a chunk makes for its predecessor's end state before it
                                  gives up (default 2^24, never reached in practice); 0 gives up
                                  at once, so that the error path can be tested                   */
+  MAMBA_OPT_AGG_SKIP = 8      /* two-pass scans with softplus: 1 (default) starts each chunk's
+                                 end-state pass where the rest of the chunk decays the state
+                                 entering it below 2^-200 (e^{A_n sum dt} for every state of a
+                                 64-channel block), 0 always from the chunk's first token; the
+                                 two agree to fp32 rounding [MAMBA_MI355X_AGG_SKIP=0]            */
 };
 
 /* Set an option: MAMBA_OK, or MAMBA_ERR_OPTION for an unknown option or a value

@@ -29,6 +29,7 @@ MAMBA_OPT_FUSED_DT = 4
 MAMBA_OPT_BWD_CHUNK = 5
 MAMBA_OPT_GEMM_GENERAL = 6
 MAMBA_OPT_SPIN_LIMIT = 7
+MAMBA_OPT_AGG_SKIP = 8
 ENGINES = {"auto": 0, "lane": 1, "wg": 2, "wp": 3}
 
 _lib = None

@@ -61,6 +61,7 @@ struct Options {
     v[s6::kOptGemmGeneral].store(std::getenv("MAMBA_MI355X_GEMM_GENERAL") ? 1 : 0);
     const int64_t spin = env_value("MAMBA_MI355X_SPIN_LIMIT", kDefaultSpinLimit);
     v[s6::kOptSpinLimit].store(spin <= 0xffffffffll ? spin : kDefaultSpinLimit);
+    v[s6::kOptAggSkip].store(env_value("MAMBA_MI355X_AGG_SKIP", 1) == 0 ? 0 : 1);
   }
 };
 
@@ -78,6 +79,7 @@ bool option_valid(int key, int64_t value) {
     case s6::kOptBwdChunk: return value >= 0 && value <= (int64_t(1) << 30);
     case s6::kOptGemmGeneral: return value == 0 || value == 1;
     case s6::kOptSpinLimit: return value >= 0 && value <= 0xffffffffll;
+    case s6::kOptAggSkip: return value == 0 || value == 1;
     default: return false;
   }
 }

@@ -20,7 +20,8 @@ enum Option {
   kOptBwdChunk = 5,     // tokens per chunk of the backward (0: automatic)
   kOptGemmGeneral = 6,  // 1: only the general GEMM kernel
   kOptSpinLimit = 7,    // polls of a chained-mode wait before it gives up (0: give up at once)
-  kOptCount = 8
+  kOptAggSkip = 8,      // 1: chunk aggregates skip what decays below 2^-200 before the chunk end
+  kOptCount = 9
 };
 int64_t option(int key);
 
@@ -55,6 +56,10 @@ struct ScanArgs {
   const void* dtlow = nullptr;
   const void* Wdt = nullptr;
   int64_t R = 0, ldr = 0;
+  // Two-pass scans: first token of each chunk aggregate, relative to the
+  // chunk's first token, per (batch, chunk, 64-channel block); null: every
+  // aggregate starts at its chunk's first token.
+  const int32_t* agg_start = nullptr;
 };
 
 // Largest dt rank the fused projection keeps in registers (eight 64-byte K slices).
@@ -111,6 +116,8 @@ struct ScanPlan {
   int64_t chunk_len;
   int32_t block;      // lane engine: threads per workgroup (64 channels per wave)
   int32_t grid;       // workgroup engine: persistent workgroups
+  int32_t tile_out;   // workgroup engine, two passes: tokens per tile of the output pass
+  int32_t grid_out;   // workgroup engine, two passes: persistent workgroups of the output pass
   size_t ws_ctrl;     // bytes of counters and flags at the start of the workspace
   size_t ws_bytes;    // workspace the plan needs in total (0 when nothing is needed)
 };
@@ -230,6 +237,11 @@ hipError_t launch_gemm_nt_pair(const void* A, const void* B, void* C, void* C2, 
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& p, int io, int N, void* workspace, hipStream_t stream);
 // Carry pass over (batch, chunk, D, N) chunk aggregates (both engines' split modes).
 hipError_t launch_chunk_carry(const ScanArgs& a, int N, hipStream_t stream);
+// Start tokens of the chunk aggregates of a two-pass scan (ScanArgs::agg_start):
+// (batch, nchunks, ceil(D / 64)) int32 in `start`.  Returns false (and launches
+// nothing) where every aggregate must start at its chunk's first token.
+size_t agg_start_bytes(int64_t batch, int64_t nchunks, int64_t D);
+bool launch_agg_start(const ScanArgs& a, int io, int N, int32_t* start, hipStream_t stream);
 hipError_t launch_step(const StepArgs& a, int io, int N, hipStream_t stream);
 
 }  // namespace s6

@@ -130,6 +130,101 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanArgs a) {
   a.agg_h[(((size_t)b * G + (G - 1)) * D + d) * N + n] = carry;
 }
 
+// ---------------------------------------------------------------- aggregate starts
+//
+// A state entering token t of chunk g reaches the chunk's end multiplied by the
+// product of Abar over tokens t..end, e^{A_n S(t)} with S(t) the sum of dt over
+// those tokens (eq. (2); A does not vary in time).  With dt >= 0 (softplus) and
+// A_n log2(e) S(t) <= -200 for every state of every channel of a 64-channel
+// block, that factor is below 2^-200: whatever the chunk holds before t moves
+// its end state by less than 2^-200 of that state's size, far below fp32
+// rounding.  The aggregate pass then starts at t from zero, and its sum of dt
+// (over t..end) makes the carry pass's factor e^{A_n sum dt} underflow to zero,
+// so the state entering the chunk is dropped as well, by the same bound.  Only
+// with softplus: dt >= 0 keeps the aggregate's own sum of dt (which the carry
+// uses) at or above the sum tested here, up to rounding; without it nothing is
+// skipped.
+// One wave per (batch row, chunk, block) walks back from the chunk's end a tile
+// of 16 tokens at a time and records the latest tile start where the bound holds
+// for the whole block (0 if it never does).  The walk sums max(raw + bias, 0),
+// a lower bound of dt = softplus(raw + bias), so the bound it tests is the
+// stronger one, at a few instructions per token; the loads of eight tiles are
+// issued together (one wave per SIMD at most: the walk is latency-bound).
+constexpr float kAggSkipExp2 = -200.0f;
+constexpr int kAggStartTile = 16;
+constexpr int kAggStartGroup = 8;  // tiles whose loads are in flight together
+
+template <typename IO>
+__global__ __launch_bounds__(64) void agg_start_kernel(ScanArgs a, int32_t N, int32_t nblk, int32_t* start) {
+  constexpr int T = kAggStartTile;
+  constexpr int GT = kAggStartGroup;
+  const int G = a.nchunks;
+  const int64_t unit = blockIdx.x;  // (batch row, chunk < G - 1, block), block fastest
+  const int64_t blk = unit % nblk;
+  const int64_t g = (unit / nblk) % (G - 1);
+  const int64_t b = unit / ((int64_t)nblk * (G - 1));
+  const int64_t d = blk * 64 + threadIdx.x;
+  const bool dv = d < a.D;
+  // the channel's slowest decay: the largest A_n log2(e)
+  float amax = -__builtin_inff();
+  if (dv)
+    for (int n = 0; n < N; ++n) amax = fmaxf(amax, a.A[d * N + n] * kLog2e);
+  const float bias = (dv && a.bias) ? a.bias[d] : 0.0f;
+  // chunks before the last hold chunk_len tokens, a multiple of the tile (checked
+  // at the launch): every tile is whole
+  const int ntiles = (int)(a.chunk_len / T);
+  const IO* chunk = static_cast<const IO*>(a.delta) + ((size_t)b * a.L + (size_t)g * a.chunk_len) * a.D;
+  // element offsets of the tile's 16 rows in this lane's channel (lanes past D read channel 0)
+  uint32_t off[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) off[j] = (uint32_t)(j * a.D + (dv ? d : 0));
+  float S = 0.0f;  // lower bound of the sum of dt from the current tile's start to the chunk's end
+  int32_t s0 = 0;
+  // tiles kg, kg - 1, ..., kg - GT + 1 (those >= 1: a start at tile 0 skips nothing)
+  for (int kg = ntiles - 1; kg >= 1 && s0 == 0; kg -= GT) {
+    float v[GT][T];
+#pragma unroll
+    for (int q = 0; q < GT; ++q) {
+      const IO* rows = chunk + (size_t)(kg - q > 0 ? kg - q : 0) * T * a.D;
+#pragma unroll
+      for (int j = 0; j < T; ++j) v[q][j] = load_io(rows, off[j]);
+    }
+#pragma unroll
+    for (int q = 0; q < GT; ++q) {
+      const int k = kg - q;
+      if (k < 1) break;
+      float ts = 0.0f;
+#pragma unroll
+      for (int j = 0; j < T; ++j) ts += fmaxf(v[q][j] + bias, 0.0f);
+      S += ts;
+      if (__all(!dv || amax * S <= kAggSkipExp2)) {
+        s0 = k * T;
+        break;
+      }
+    }
+  }
+  if (threadIdx.x == 0) start[((size_t)b * G + g) * nblk + blk] = s0;
+}
+
+size_t agg_start_bytes(int64_t batch, int64_t nchunks, int64_t D) {
+  return (size_t)batch * nchunks * ((D + 63) / 64) * sizeof(int32_t);
+}
+
+bool launch_agg_start(const ScanArgs& a, int io, int N, int32_t* start, hipStream_t s) {
+  // dt >= 0 only with softplus; the fused dt projection has no delta to read
+  if (option(kOptAggSkip) == 0 || a.softplus == 0 || a.dtlow != nullptr || start == nullptr || a.nchunks < 2 ||
+      a.chunk_len % kAggStartTile != 0 || a.chunk_len * a.D > 0x7fffffff)
+    return false;
+  const int32_t nblk = (int32_t)((a.D + 63) / 64);
+  const int64_t units = a.batch * (int64_t)(a.nchunks - 1) * nblk;
+  if (units <= 0 || units > 0x7fffffff) return false;
+  if (io == kIoBF16)
+    hipLaunchKernelGGL(agg_start_kernel<uint16_t>, dim3((unsigned)units), dim3(64), 0, s, a, (int32_t)N, nblk, start);
+  else
+    hipLaunchKernelGGL(agg_start_kernel<float>, dim3((unsigned)units), dim3(64), 0, s, a, (int32_t)N, nblk, start);
+  return true;
+}
+
 // Output pass: every chunk from its carry-in (or h0 / zero when unchunked).
 template <typename IO, int N>
 __global__ __launch_bounds__(256) void scan_output_kernel(ScanArgs a) {
@@ -218,7 +313,11 @@ ScanPlan plan_lane(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
   return p;
 }
 
-ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
+#ifndef S6_WG_SPLIT_ITEMS
+#define S6_WG_SPLIT_ITEMS 512
+#endif
+
+ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1, bool fdt = false) {
   ScanPlan p{};
   p.engine = kEngineWg;
   p.waves = wg_waves(N);
@@ -242,12 +341,14 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
     p.chunk_len = chunk;
     p.nchunks = (int32_t)((L + chunk - 1) / chunk);
     p.grid = (int32_t)(chains < kGridMax ? chains : kGridMax);
+    p.tile_out = (int32_t)T;
+    p.grid_out = p.grid;
     p.ws_ctrl = round_up(256 + 4 * (size_t)chains, 256);
     p.ws_bytes = p.ws_ctrl + (size_t)chains * 64 * N * cf * sizeof(float);
   } else {
-    // Two passes over independent chunks: about 1024 work items.
+    // Two passes over independent chunks: about S6_WG_SPLIT_ITEMS work items.
     p.split = 1;
-    int64_t g = (1024 + chains - 1) / chains;
+    int64_t g = (S6_WG_SPLIT_ITEMS + chains - 1) / chains;
     if (g > tiles / 4) g = tiles / 4;
     if (g < 2) g = 2;
     int64_t chunk = (L + g - 1) / g;
@@ -256,8 +357,14 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
     p.chunk_len = chunk;
     p.nchunks = (int32_t)((L + chunk - 1) / chunk);
     p.grid = (int32_t)kGridMax;
+    // The output pass of a real scan runs on 8-token tiles: half the LDS, so two
+    // workgroups share a CU (the projected-dt front end needs 16-token tiles).
+    p.tile_out = (cf == 1 && !fdt && T == 16) ? 8 : (int32_t)T;
+    p.grid_out = p.tile_out < T ? 2 * p.grid : p.grid;
     p.ws_ctrl = 256;
-    p.ws_bytes = p.ws_ctrl + (size_t)batch * p.nchunks * D * (N * cf + 1) * sizeof(float);
+    // then the aggregate starts (real A only)
+    p.ws_bytes = p.ws_ctrl + (size_t)batch * p.nchunks * D * (N * cf + 1) * sizeof(float) +
+                 (cf == 1 ? agg_start_bytes(batch, p.nchunks, D) : 0);
   }
   return p;
 }
@@ -267,8 +374,11 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1) {
 // Wave-private engine: one wave per (batch row, CW channels) for the whole
 // sequence; long sequences over few channels are cut into chunks (two passes)
 // until about 2.5 waves per SIMD result.
-constexpr int64_t kWpSplitBelow = 1024;   // waves of the unchunked scan below which L is cut
-constexpr int64_t kWpTargetWaves = 2560;  // waves the chunked scan aims for (2.5 per SIMD)
+#ifndef S6_WP_SPLIT_WAVES
+#define S6_WP_SPLIT_WAVES 2560  // waves the chunked scan aims for (2.5 per SIMD)
+#endif
+constexpr int64_t kWpSplitBelow = 1024;  // waves of the unchunked scan below which L is cut
+constexpr int64_t kWpTargetWaves = S6_WP_SPLIT_WAVES;
 
 ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
   ScanPlan p{};
@@ -297,7 +407,8 @@ ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
   p.nchunks = (int32_t)((L + chunk - 1) / chunk);
   p.split = p.nchunks > 1;
   p.ws_ctrl = 0;
-  p.ws_bytes = p.split ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) : 0;
+  p.ws_bytes = p.split ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) + agg_start_bytes(batch, p.nchunks, D)
+                       : 0;
   return p;
 }
 
@@ -317,7 +428,7 @@ ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
 }
 
 ScanPlan plan_scan_fused_dt(int64_t batch, int64_t L, int64_t D, int64_t N) {
-  if (wg_supported(N) && batch > 0 && L > 0 && D > 0) return plan_wg(batch, L, D, N);
+  if (wg_supported(N) && batch > 0 && L > 0 && D > 0) return plan_wg(batch, L, D, N, 1, true);
   return plan_lane(batch, L, D, N);
 }
 

@@ -403,6 +403,9 @@ struct WgScan {
     dvalid = d < A.s.D;
     t0 = (int64_t)g * A.s.chunk_len;
     t1 = t0 + A.s.chunk_len < A.s.L ? t0 + A.s.chunk_len : A.s.L;
+    // an aggregate may skip the part of its chunk that cannot reach the chunk's end
+    if (MODE == kModeAgg && A.s.agg_start)
+      t0 += A.s.agg_start[((size_t)b * G + g) * A.blocks_per_row + chain % A.blocks_per_row];
     chan_off = dvalid ? (uint32_t)(d * kIo) : kOutOfRange;
     {
       const size_t row0 = ((size_t)b * A.s.L + t0);
@@ -582,8 +585,14 @@ struct WgScan {
   }
 };
 
+// Workgroups per CU the kernel is compiled for: two on 8-token tiles.
+template <int T>
+constexpr int wg_per_cu() {
+  return T < 16 ? 2 * S6_WG_PER_CU : S6_WG_PER_CU;
+}
+
 template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
-__global__ __launch_bounds__(64 * W, S6_WG_PER_CU) void scan_wg_kernel(WgArgs a) {
+__global__ __launch_bounds__(64 * W, wg_per_cu<T>()) void scan_wg_kernel(WgArgs a) {
   using K = WgScan<IO, N, W, T, MODE, FDT, CPLX>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
@@ -601,7 +610,9 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-template <typename IO, int N, int W, int T, bool FDT, bool CPLX>
+// T: tokens per tile of the chained mode and of the split mode's first pass;
+// TO: of the split mode's output pass.
+template <typename IO, int N, int W, int T, int TO, bool FDT, bool CPLX>
 hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
   constexpr int CF = CPLX ? 2 : 1;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -626,6 +637,8 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
   } else {
     a.s.agg_h = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N * CF;
+    int32_t* start = reinterpret_cast<int32_t*>(a.s.agg_s + (size_t)s.batch * p.nchunks * s.D);
+    if (!CPLX && launch_agg_start(a.s, sizeof(IO) == 2 ? kIoBF16 : kIoF32, N, start, st)) a.s.agg_start = start;
     a.carry = nullptr;
     a.ticket = ctrl;
     a.nitems = a.chains * (p.nchunks - 1);
@@ -635,17 +648,24 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     if (ce != hipSuccess) return ce;
     a.ticket = ctrl + 1;
     a.nitems = a.chains * p.nchunks;
-    const unsigned g2 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeOut, FDT, CPLX>), dim3(g2), block, 0, st, a);
+    const unsigned g2 = (unsigned)(a.nitems < p.grid_out ? a.nitems : p.grid_out);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, TO, kModeOut, FDT, CPLX>), dim3(g2), block, 0, st, a);
   }
   return hipGetLastError();
 }
 
 template <typename IO, int N, int W, int T>
 hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, bool cplx, void* ws, hipStream_t st) {
-  if (cplx) return s.dtlow ? hipErrorInvalidValue : launch_wg_t<IO, N, W, T, false, true>(s, p, ws, st);
-  if (s.dtlow) return launch_wg_t<IO, N, W, T, true, false>(s, p, ws, st);
-  return launch_wg_t<IO, N, W, T, false, false>(s, p, ws, st);
+  if (p.tile_out != T && (p.tile_out != 8 || !p.split || cplx || s.dtlow)) return hipErrorInvalidValue;
+  if (cplx) return s.dtlow ? hipErrorInvalidValue : launch_wg_t<IO, N, W, T, T, false, true>(s, p, ws, st);
+  if (s.dtlow) {
+    if constexpr (T == 16) return launch_wg_t<IO, N, W, T, T, true, false>(s, p, ws, st);
+    return hipErrorInvalidValue;
+  }
+  if constexpr (T != 8) {
+    if (p.tile_out == 8) return launch_wg_t<IO, N, W, T, 8, false, false>(s, p, ws, st);
+  }
+  return launch_wg_t<IO, N, W, T, T, false, false>(s, p, ws, st);
 }
 
 }  // namespace

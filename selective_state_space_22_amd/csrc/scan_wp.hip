@@ -482,6 +482,8 @@ struct WpScan {
     const bool svalid = dscan < A.s.D, fvalid = dfront < A.s.D;
     t0 = (int64_t)g * A.s.chunk_len;
     t1 = t0 + A.s.chunk_len < A.s.L ? t0 + A.s.chunk_len : A.s.L;
+    // an aggregate may skip the part of its chunk that cannot reach the chunk's end
+    if (MODE == kWpAgg && A.s.agg_start) t0 += A.s.agg_start[((size_t)b * G + g) * nb + unit % nb];
     row_bytes = wp_uniform((uint32_t)(A.s.D * kIo));
     {
       const uint32_t chan_off = fvalid ? (uint32_t)(dfront * kIo) : kWpOutOfRange;
@@ -601,6 +603,8 @@ hipError_t launch_wp_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
   } else {
     a.s.agg_h = static_cast<float*>(ws);
     a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N;
+    int32_t* start = reinterpret_cast<int32_t*>(a.s.agg_s + (size_t)s.batch * p.nchunks * s.D);
+    if (launch_agg_start(a.s, sizeof(IO) == 2 ? kIoBF16 : kIoF32, N, start, st)) a.s.agg_start = start;
     a.units = rows * (p.nchunks - 1);
     launch_wp_pass<IO, N, kWpAgg>(a, st);
     const hipError_t ce = launch_chunk_carry(a.s, N, st);

@@ -41,6 +41,7 @@ int main(void) {
   CHECK(mamba_set_option(MAMBA_OPT_ENGINE, keep) == MAMBA_OK);
   CHECK(mamba_set_option(99, 0) == MAMBA_ERR_OPTION && mamba_get_option(99) == -1);
   CHECK(mamba_set_option(MAMBA_OPT_SPIN_LIMIT, (int64_t)1 << 33) == MAMBA_ERR_OPTION);
+  CHECK(mamba_set_option(MAMBA_OPT_AGG_SKIP, 2) == MAMBA_ERR_OPTION);
   /* forward scan validation */
   CHECK(mamba_scan_fwd(1, 8, 64, 16, 7, F, F, NULL, F, F, F, NULL, NULL, 1, NULL, F, NULL, NULL, 0, NULL) ==
         MAMBA_ERR_DTYPE);

@@ -67,9 +67,10 @@ def test_workspace_size_is_a_pure_function_of_shape(lib):
     # the lane engine (other N) runs short sequences in one piece: no workspace
     assert ws(1, 256, 64, 4, 0) == 0
     # few channel blocks and a long sequence: two passes over chunks, the workspace
-    # holds the (batch, chunks, D, N+1) chunk aggregates after a 256-byte header
+    # holds the (batch, chunks, D, N+1) chunk aggregates after a 256-byte header, then
+    # one int32 aggregate start per (batch, chunk, 64-channel block)
     w = ws(1, 1 << 20, 256, 16, 0)
-    assert w > 256 and (w - 256) % (256 * 17 * 4) == 0
+    assert w > 256 and (w - 256) % (256 * 17 * 4 + 4 * 4) == 0
     # rejected shapes report 0
     assert ws(1, 16, 64, 3, 0) == 0
     assert ws(1, 16, 64, 16, 7) == 0
@@ -79,7 +80,7 @@ def test_workspace_size_is_a_pure_function_of_shape(lib):
 
 @pytest.fixture
 def restore_options(lib):
-    keep = {k: binding.mamba_get_option(k) for k in range(1, 8)}
+    keep = {k: binding.mamba_get_option(k) for k in range(1, 9)}
     yield
     for k, v in keep.items():
         binding.mamba_set_option(k, v)
@@ -87,19 +88,21 @@ def restore_options(lib):
 
 def test_options_round_trip_and_validation(lib, restore_options):
     opts = [binding.MAMBA_OPT_ENGINE, binding.MAMBA_OPT_CHUNK, binding.MAMBA_OPT_WG_WAVES, binding.MAMBA_OPT_FUSED_DT,
-            binding.MAMBA_OPT_BWD_CHUNK, binding.MAMBA_OPT_GEMM_GENERAL, binding.MAMBA_OPT_SPIN_LIMIT]
-    assert opts == list(range(1, 8))
+            binding.MAMBA_OPT_BWD_CHUNK, binding.MAMBA_OPT_GEMM_GENERAL, binding.MAMBA_OPT_SPIN_LIMIT,
+            binding.MAMBA_OPT_AGG_SKIP]
+    assert opts == list(range(1, 9))
     # the wait bound starts at 2^24 sleeps (a few seconds) unless the environment set it
     for k, good, bad in [(binding.MAMBA_OPT_ENGINE, 3, 4), (binding.MAMBA_OPT_WG_WAVES, 4, 5),
                          (binding.MAMBA_OPT_FUSED_DT, 1, 2), (binding.MAMBA_OPT_GEMM_GENERAL, 1, -1),
-                         (binding.MAMBA_OPT_CHUNK, 2048, -1), (binding.MAMBA_OPT_SPIN_LIMIT, 0, 1 << 32)]:
+                         (binding.MAMBA_OPT_CHUNK, 2048, -1), (binding.MAMBA_OPT_SPIN_LIMIT, 0, 1 << 32),
+                         (binding.MAMBA_OPT_AGG_SKIP, 0, 2)]:
         binding.mamba_set_option(k, good)
         assert binding.mamba_get_option(k) == good
         with pytest.raises(binding.MambaError) as ex:
             binding.mamba_set_option(k, bad)
         assert ex.value.status == 9
         assert binding.mamba_get_option(k) == good  # a refused value leaves the option alone
-    for k in (0, 8, 99, -1):
+    for k in (0, 9, 99, -1):
         assert binding.mamba_get_option(k) == -1
         with pytest.raises(binding.MambaError):
             binding.mamba_set_option(k, 0)

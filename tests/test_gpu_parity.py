@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, force_engine, gpu_scan, parity_error, to_device, to_host
-from selective_state_space_22_amd import workloads as W
+from gpu_util import TOL, force_engine, gpu_scan, library_option, parity_error, to_device, to_host
+from selective_state_space_22_amd import binding, workloads as W
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -287,6 +287,69 @@ def test_empty_sequence_returns_initial_state():
     out, last = mamba_scan_fwd(u, u, A, B, B)
     torch.cuda.synchronize()
     assert torch.count_nonzero(last) == 0
+
+
+# Two-pass scans with reset tokens: each chunk's end-state pass may start where the
+# rest of the chunk decays the state before it below 2^-200 (MAMBA_OPT_AGG_SKIP).
+SKIP_CASES = [
+    (1, 65536, 64, 16, "f32"),
+    (2, 20000, 200, 16, "bf16"),
+    (1, 30000, 128, 8, "f32"),
+]
+
+
+@pytest.mark.parametrize("engine", ["default", "wg"])
+@pytest.mark.parametrize("case", SKIP_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in SKIP_CASES])
+def test_split_scan_with_reset_tokens(case, engine, request):
+    """Against the oracle with the skip on and off, and the two runs against each other."""
+    _need_gpu()
+    _engine(request, engine)
+    batch, L, D, N, io = case
+    _announce(f"split scan with reset tokens {case} engine={engine}")
+    inp = W.generate(batch, L, D, N, io, seed=610 + L + D, reset_frac=0.01)
+    ro, rl = oracle.scan_inputs(inp)
+    runs = {}
+    for skip in (1, 0):
+        with library_option(binding.MAMBA_OPT_AGG_SKIP, skip):
+            go, gl = gpu_scan(inp)
+        eo, el = parity_error(go, ro), parity_error(gl, rl)
+        print(f"{case} skip={skip}: out err {eo:.3e} last err {el:.3e}")
+        assert eo <= TOL[io] and el <= TOL[io], f"skip={skip}: out {eo:.3e} last {el:.3e}"
+        runs[skip] = (go, gl)
+    # the skipped terms are below 2^-200 of the state: the runs differ by rounding only
+    agree = 1e-5 if io == "f32" else 2e-2
+    assert parity_error(runs[1][0], runs[0][0]) <= agree and parity_error(runs[1][1], runs[0][1]) <= agree
+
+
+@pytest.mark.parametrize("engine", ["default", "wg"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_aggregate_skip_keeps_what_reaches_the_chunk_end(io, engine, request):
+    """dt is set token by token (bias 0): a period of five 16-token tiles holds a mild
+    reset (dt = softplus(2) at the start of tile 1) and a strong one (three tokens of
+    dt = softplus(50) at the start of tile 3).  A_0 = -1 decays slowly and the other
+    states fast (A_n = -100), so a start taken from the fastest decay would drop the
+    state 0 that survives the mild reset (2^-3 of it), a start one tile late would drop
+    the tokens after the strong reset, and a start from the wrong chunk or block would
+    drop whole chunks: each shows up against the oracle."""
+    _need_gpu()
+    _engine(request, engine)
+    batch, L, D, N = 2, 8000, 96, 16
+    _announce(f"aggregate start bound case {(batch, L, D, N, io)} engine={engine}")
+    inp = W.generate(batch, L, D, N, io, seed=640)
+    inp.delta_bias = np.zeros(D, np.float32)
+    A = np.full((D, N), -100.0, np.float32)
+    A[:, 0] = -1.0
+    inp.A = A
+    raw = np.full((batch, L), -5.0, np.float32)
+    for p0 in range(0, L, 80):
+        raw[:, p0 + 16:p0 + 17] = 2.0
+        raw[:, p0 + 48:p0 + 51] = 50.0
+    raw[1] = np.roll(raw[1], 37)  # the second row's resets fall elsewhere in the chunks
+    inp.delta = np.repeat(raw[:, :, None], D, axis=2).astype(np.float32)
+    inp.z = None  # the scan alone: skip and gate would dilute the states' share of the output
+    inp.Dskip = None
+    with library_option(binding.MAMBA_OPT_AGG_SKIP, 1):
+        check(inp, label=f"aggregate start {io} {engine}")
 
 
 # ------------------------------------------------------------ invariants
