@@ -298,7 +298,7 @@ SKIP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("engine", ["default", "wg"])
+@pytest.mark.parametrize("engine", ["default", "wg", "wp"])
 @pytest.mark.parametrize("case", SKIP_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_N{c[3]}_{c[4]}" for c in SKIP_CASES])
 def test_split_scan_with_reset_tokens(case, engine, request):
     """Against the oracle with the skip on and off, and the two runs against each other."""
@@ -321,7 +321,7 @@ def test_split_scan_with_reset_tokens(case, engine, request):
     assert parity_error(runs[1][0], runs[0][0]) <= agree and parity_error(runs[1][1], runs[0][1]) <= agree
 
 
-@pytest.mark.parametrize("engine", ["default", "wg"])
+@pytest.mark.parametrize("engine", ["default", "wg", "wp"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_aggregate_skip_keeps_what_reaches_the_chunk_end(io, engine, request):
     """dt is set token by token (bias 0): a period of five 16-token tiles holds a mild
