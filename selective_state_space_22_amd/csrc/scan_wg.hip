@@ -585,14 +585,17 @@ struct WgScan {
   }
 };
 
-// Workgroups per CU the kernel is compiled for: two on 8-token tiles.
-template <int T>
-constexpr int wg_per_cu() {
-  return T < 16 ? 2 * S6_WG_PER_CU : S6_WG_PER_CU;
+// The launch bound's second value is the waves per SIMD the registers must
+// allow: the workgroups per CU that LDS admits (S6_WG_PER_CU on 16-token tiles,
+// twice that on 8-token tiles) times W waves, over the CU's 4 SIMDs.
+template <int W, int T>
+constexpr int wg_waves_per_simd() {
+  constexpr int v = (T < 16 ? 2 : 1) * S6_WG_PER_CU * W / 4;
+  return v > 1 ? v : 1;
 }
 
 template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
-__global__ __launch_bounds__(64 * W, wg_per_cu<T>()) void scan_wg_kernel(WgArgs a) {
+__global__ __launch_bounds__(64 * W, (wg_waves_per_simd<W, T>())) void scan_wg_kernel(WgArgs a) {
   using K = WgScan<IO, N, W, T, MODE, FDT, CPLX>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
