@@ -118,6 +118,8 @@ struct ScanPlan {
   int32_t grid;       // workgroup engine: persistent workgroups
   int32_t tile_out;   // workgroup engine, two passes: tokens per tile of the output pass
   int32_t grid_out;   // workgroup engine, two passes: persistent workgroups of the output pass
+  int32_t wp1_units;  // wave-private engine, unchunked N = 16: the last wp1_units (batch row, 64-channel
+                      // block) units run with one state per lane in the same launch (0: none)
   size_t ws_ctrl;     // bytes of counters and flags at the start of the workspace
   size_t ws_bytes;    // workspace the plan needs in total (0 when nothing is needed)
 };

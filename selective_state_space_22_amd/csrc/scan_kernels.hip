@@ -374,6 +374,9 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1, boo
 // Wave-private engine: one wave per (batch row, CW channels) for the whole
 // sequence; long sequences over few channels are cut into chunks (two passes)
 // until about 2.5 waves per SIMD result.
+#ifndef S6_WP_MIXED
+#define S6_WP_MIXED 1  // 0: no mixed launches of two- and one-state-per-lane waves
+#endif
 #ifndef S6_WP_SPLIT_WAVES
 #define S6_WP_SPLIT_WAVES 2560  // waves the chunked scan aims for (2.5 per SIMD)
 #endif
@@ -406,6 +409,14 @@ ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
   p.chunk_len = chunk;
   p.nchunks = (int32_t)((L + chunk - 1) / chunk);
   p.split = p.nchunks > 1;
+  // Unchunked N = 16 with more than 1024 but fewer than 3072 waves: part of the
+  // (batch row, block) units run with one state per lane (twice the waves, half
+  // the work each), so that the launch has 2 or 3 waves on every SIMD.
+  const int64_t units = batch * ((D + 63) / 64);
+  if (S6_WP_MIXED && !p.split && N == 16) {
+    if (units > 128 && units < 256) p.wp1_units = (int32_t)(256 - units);
+    else if (units > 256 && units < 384) p.wp1_units = (int32_t)(384 - units);
+  }
   p.ws_ctrl = 0;
   p.ws_bytes = p.split ? (size_t)batch * p.nchunks * D * (N + 1) * sizeof(float) + agg_start_bytes(batch, p.nchunks, D)
                        : 0;

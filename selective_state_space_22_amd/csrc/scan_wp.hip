@@ -17,8 +17,8 @@
 //            Dskip x, multiplies by SiLU(z) and makes one store per (token, channel).
 // The expanded (batch, L, D, N) state never leaves VGPRs (section 4.1).
 //
-// A workgroup is one wave.  Its LDS (12 KB for N = 16) lets about ten waves
-// share a CU, which is what hides the latencies of the per-token chains
+// A workgroup is one wave.  Its LDS (12 KB for N = 16) lets twelve waves, three
+// per SIMD, share a CU, which is what hides the latencies of the per-token chains
 // (exp, select, recurrence FMA) and of LDS.  The P waves of a 64-channel block
 // read and write the same 128-byte lines of every token row; workgroup ids are
 // mapped so that they run on one XCD (ids are dealt to the XCDs in turn) and
@@ -179,12 +179,13 @@ struct WpScan {
   static_assert(T / P >= 2, "at least two token slots per lane and tile");
   static_assert(P == 8 || P == 4, "partial-readout layout");
   static constexpr bool kOut = MODE != kWpAgg;
-  // Partial readouts of one token: P floats per channel.  For P = 8 the two
-  // 16-byte halves of a channel are swapped for channels 4..7 and rows are 96
-  // floats apart, so that the epilogue's 16-byte reads (lane = channel, eight
-  // or sixteen lanes per LDS cycle) and the scan's 4-byte writes touch distinct
-  // banks.
-  static constexpr int YS = P == 8 ? 96 : 64;
+  // Partial readouts of one token: P floats per channel, 64 per row.  For P = 8
+  // the two 16-byte halves of a channel are swapped for channels 4..7, and odd
+  // rows are rotated by half a row (position ^ 32), so that the epilogue's
+  // 16-byte reads (lane = channel, eight or sixteen lanes of two consecutive
+  // rows per LDS cycle) and the scan's 4-byte writes touch distinct banks
+  // without padding: 12 KB of LDS per wave, so that twelve waves fit a CU.
+  static constexpr int YS = 64;
   static __device__ __forceinline__ int ypos(int c, int g) {
     if constexpr (P == 8) return 4 * (2 * c + ((g >> 2) ^ ((c >> 2) & 1))) + (g & 3);
     return 4 * c + g;
@@ -215,6 +216,7 @@ struct WpScan {
   // channel) from the tile's first row; out of range for channels >= D.
   uint32_t voff[TQ];
   uint32_t bc_off;  // this lane's B / C chunks from the tile's first row
+  int yo0, yo1;     // this lane's partial-readout position in even / odd token rows
   // Chunk bases and spans in bytes; each tile gets buffer resources based at its
   // first row, so that the tile's position costs scalar instructions only and
   // rows past the chunk still fall outside the resource.
@@ -231,7 +233,10 @@ struct WpScan {
         sc((threadIdx.x & 63) / P),
         sg((threadIdx.x & 63) % P),
         fc((threadIdx.x & 63) % CW),
-        fq((threadIdx.x & 63) / CW) {}
+        fq((threadIdx.x & 63) / CW) {
+    yo0 = ypos(sc, sg);
+    yo1 = P == 8 ? yo0 ^ 32 : yo0;
+  }
 
   __device__ __forceinline__ int tile_valid(int k) const {
     const int64_t tk = t0 + (int64_t)k * T;
@@ -321,9 +326,9 @@ struct WpScan {
   // an address computed per pair).
   __device__ __forceinline__ void yp_store(int j, float v) {
 #if S6_WP_YPSINGLE
-    *(volatile __attribute__((address_space(3))) float*)(&sm.yp[j][ypos(sc, sg)]) = v;
+    *(volatile __attribute__((address_space(3))) float*)(&sm.yp[j][(j & 1) ? yo1 : yo0]) = v;
 #else
-    sm.yp[j][ypos(sc, sg)] = v;
+    sm.yp[j][(j & 1) ? yo1 : yo0] = v;
 #endif
   }
 
@@ -405,10 +410,11 @@ struct WpScan {
     if (!kOut) return;
     const int j = fq + P * i;
     const float4* row = reinterpret_cast<const float4*>(&sm.yp[j][0]);
-    const float4 lo = row[ypos(fc, 0) / 4];
+    const int sw = P == 8 ? 32 * (j & 1) : 0;
+    const float4 lo = row[(ypos(fc, 0) ^ sw) / 4];
     float y = ((lo.x + lo.y) + lo.z) + lo.w;  // the P partials in state order
     if constexpr (P == 8) {
-      const float4 hi = row[ypos(fc, 4) / 4];
+      const float4 hi = row[(ypos(fc, 4) ^ sw) / 4];
       y = (((y + hi.x) + hi.y) + hi.z) + hi.w;
     }
     const float4 fv = lds_read16(&sm.fr[f][j][fc]);
@@ -591,8 +597,12 @@ void launch_wp_pass(const WpArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((scan_wp_kernel<IO, N, (N == 16 ? S6_WP_TILE16 : S6_WP_TILE), MODE, false>), dim3(grid), dim3(64 * WGW), 0, st, a);
 }
 
+template <typename IO>
+hipError_t launch_wp_mixed(const ScanArgs& s, int32_t wp1_units, hipStream_t st);
+
 template <typename IO, int N>
 hipError_t launch_wp_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
+  if (p.wp1_units > 0) return (N == 16 && !p.split) ? launch_wp_mixed<IO>(s, p.wp1_units, st) : hipErrorInvalidValue;
   WpArgs a;
   a.s = s;
   a.nblk = (int32_t)((s.D + 63) / 64);
@@ -612,6 +622,279 @@ hipError_t launch_wp_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.units = rows * p.nchunks;
     launch_wp_pass<IO, N, kWpOut>(a, st);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- one state per lane (N = 16)
+//
+// A second layout for mixed launches.  A wave owns 4 channels of one batch row
+// for the whole sequence: the 16 lanes of row r (lanes 16r .. 16r+15, one DPP
+// row) hold the 16 states of channel r, one each, so its work is half a
+// two-states-per-lane wave's.  Lane 16r + j also owns token j of every 16-token
+// tile of channel r: it loads delta, u and z, computes dt, and after the scan
+// sums the row's 16 partial readouts of that token (eq. (3b)) in state order,
+// adds Dskip x, multiplies by SiLU(z) and makes the store.  The scan of token j
+// reads dt and x from lane 16r + j of its own row with a DPP row broadcast
+// (row_newbcast:j), which the compiler folds into the multiplies that use them;
+// B_t and C_t (shared by all channels, section 3.2) are staged once per tile in
+// LDS as (B, C) pairs per state.  The series branch of the input weight is
+// written dt (1 + x ln2 / 2) with x = dt A log2(e), the same value as
+// dt + dt^2 A / 2, so that dt enters it only through a multiply.
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + J, 0xf, 0xf,
+                                                               false));
+}
+
+template <typename IO, bool SP>
+struct Wp1Scan {
+  static constexpr int N = 16, T = 16, CW1 = 4;
+  static constexpr int PD = 3;  // tiles of global loads in flight
+  static constexpr uint32_t kIo = sizeof(IO);
+  static constexpr int KB = (int)kIo;  // dwords of B (or C) a lane stages per tile: four elements
+  // Partial readouts: 64 floats per token (channel-major), rows 68 floats apart so
+  // that the epilogue's 16-byte reads of consecutive tokens touch distinct banks.
+  static constexpr int YS = 68;
+  static constexpr float kHalfLn2 = 0.5f * kLn2;
+
+  struct Lds {
+    float2 bc[T][N];  // (B, C) per (token, state)
+    float yp[T][YS];  // partial readouts per (token, channel * 16 + state)
+  };
+  struct Regs {  // raw prefetched global data of one tile: this lane's token, its four B / C elements
+    uint32_t dl, uu, zz;
+    uint32_t bw[KB], cw[KB];
+  };
+
+  const WpArgs& A;
+  Lds& sm;
+  const int lane, r, n;  // channel within the wave (row), state = token of the row's front lane
+  int64_t L;
+  uint32_t row_bytes, voff, bc_off;
+  const char *p_u, *p_dl, *p_z, *p_out, *p_B, *p_C;
+  uint32_t span, zspan, bspan;
+  float a2, ka, h, bias, dskip;
+  float fdt, fx, fz;  // front end of this lane's token of the current tile
+
+  __device__ Wp1Scan(const WpArgs& a, Lds& s)
+      : A(a), sm(s), lane(threadIdx.x & 63), r((threadIdx.x & 63) >> 4), n(threadIdx.x & 15) {}
+
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t span, uint32_t off) {
+    const int32_t left = (int32_t)span - (int32_t)off;
+    return wp_rsrc(base + off, (uint32_t)(left > 0 ? left : 0));
+  }
+
+  __device__ __forceinline__ void load(Regs& g, int k) const {
+    const uint32_t toff = (uint32_t)(k * T) * row_bytes;
+    g.dl = WpIo<IO>::load(tile_rsrc(p_dl, span, toff), voff);
+    g.uu = WpIo<IO>::load(tile_rsrc(p_u, span, toff), voff);
+    g.zz = WpIo<IO>::load(tile_rsrc(p_z, zspan, toff), voff);
+    const uint32_t bt = (uint32_t)(k * T * N) * kIo;
+    load_dwords<KB>(g.bw, tile_rsrc(p_B, bspan, bt), bc_off);
+    load_dwords<KB>(g.cw, tile_rsrc(p_C, bspan, bt), bc_off);
+  }
+
+  __device__ __forceinline__ void front(const Regs& g) {
+    fx = WpIo<IO>::widen(g.uu);
+    fz = WpIo<IO>::widen(g.zz);
+    const float raw = WpIo<IO>::widen(g.dl) + bias;
+    fdt = SP ? softplus(raw) : raw;
+  }
+
+  // B / C of a tile: lane l stages elements 4l .. 4l+3 of the (token, state)
+  // block, i.e. token l / 4, states 4 (l % 4) .. 4 (l % 4) + 3.
+  __device__ __forceinline__ void stage_bc(const Regs& g) {
+    float bv[4], cv[4];
+    if constexpr (kIo == 2) {
+      bv[0] = bf16_lo(g.bw[0]);
+      bv[1] = bf16_hi(g.bw[0]);
+      bv[2] = bf16_lo(g.bw[1]);
+      bv[3] = bf16_hi(g.bw[1]);
+      cv[0] = bf16_lo(g.cw[0]);
+      cv[1] = bf16_hi(g.cw[0]);
+      cv[2] = bf16_lo(g.cw[1]);
+      cv[3] = bf16_hi(g.cw[1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bv[q] = __uint_as_float(g.bw[q]);
+        cv[q] = __uint_as_float(g.cw[q]);
+      }
+    }
+    float4* dst = reinterpret_cast<float4*>(&sm.bc[lane >> 2][4 * (lane & 3)]);
+    dst[0] = make_float4(bv[0], cv[0], bv[1], cv[1]);
+    dst[1] = make_float4(bv[2], cv[2], bv[3], cv[3]);
+  }
+
+  // Input terms of token J (eq. (2)): Abar and beta B x for this lane's state.
+  template <int J>
+  __device__ __forceinline__ void input_terms(const float2 v, float& ab, float& in) const {
+    const float x2 = row_bcast<J>(fdt) * a2;
+    ab = ex2(x2);
+    const float big = __builtin_fmaf(ab, ka, -ka);
+    const float small = row_bcast<J>(fdt) * __builtin_fmaf(x2, kHalfLn2, 1.0f);
+    const float beta = fabsf(x2) < kPhiSeriesX2 ? small : big;
+    in = beta * (row_bcast<J>(fx) * v.x);
+  }
+  // Tokens J and J+1: both tokens' input terms, then the two recurrence steps
+  // (eq. (3a)) and partial readouts C h (eq. (3b)) to LDS.
+  template <int J>
+  __device__ __forceinline__ void pair(const float2 (&v)[T]) {
+    float ab0, in0, ab1, in1;
+    input_terms<J>(v[J], ab0, in0);
+    input_terms<J + 1>(v[J + 1], ab1, in1);
+    h = __builtin_fmaf(ab0, h, in0);
+    sm.yp[J][lane] = v[J].y * h;
+    h = __builtin_fmaf(ab1, h, in1);
+    sm.yp[J + 1][lane] = v[J + 1].y * h;
+  }
+  template <int J>
+  __device__ __forceinline__ void single(const float2 (&v)[T]) {
+    float ab, in;
+    input_terms<J>(v[J], ab, in);
+    h = __builtin_fmaf(ab, h, in);
+    sm.yp[J][lane] = v[J].y * h;
+  }
+  template <int... P>
+  __device__ __forceinline__ void pairs(const float2 (&v)[T], std::integer_sequence<int, P...>) {
+    (pair<2 * P>(v), ...);
+  }
+  template <int... J>
+  __device__ __forceinline__ void singles(const float2 (&v)[T], int nv, std::integer_sequence<int, J...>) {
+    ((J < nv ? single<J>(v) : void()), ...);
+  }
+  // The tile's 16 tokens (the first nv of them when not FULL); the (B, C) pairs
+  // of all 16 are read from LDS first, so the reads' latency is paid once.
+  template <bool FULL>
+  __device__ __forceinline__ void scan(int nv) {
+    float2 v[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) v[j] = sm.bc[j][n];
+    if (FULL) pairs(v, std::make_integer_sequence<int, T / 2>{});
+    else singles(v, nv, std::make_integer_sequence<int, T>{});
+  }
+
+  // This lane's token of tile k: the 16 partials in state order, skip, gate, store.
+  __device__ __forceinline__ void epilogue(int k) {
+    const float4* row = reinterpret_cast<const float4*>(&sm.yp[n][16 * r]);
+    const float4 p0 = row[0], p1 = row[1], p2 = row[2], p3 = row[3];
+    float y = ((p0.x + p0.y) + p0.z) + p0.w;
+    y = (((y + p1.x) + p1.y) + p1.z) + p1.w;
+    y = (((y + p2.x) + p2.y) + p2.z) + p2.w;
+    y = (((y + p3.x) + p3.y) + p3.z) + p3.w;
+    const float o = s6::epilogue(y, fx, dskip, A.s.z != nullptr, fz);
+    WpIo<IO>::store(o, tile_rsrc(p_out, span, (uint32_t)(k * T) * row_bytes), voff);
+  }
+
+  // Tile k (full when FULL) from ring slot RS, then that slot refilled with tile k + PD.
+  template <bool FULL, int RS>
+  __device__ __forceinline__ void tile(Regs (&ring)[PD], int k, int nv) {
+    front(ring[RS]);
+    stage_bc(ring[RS]);
+    load(ring[RS], k + PD);
+    wave_lds_order();
+    scan<FULL>(nv);
+    wave_lds_order();
+    epilogue(k);
+    wave_lds_order();
+  }
+  template <int... I>
+  __device__ __forceinline__ void tiles_full(Regs (&ring)[PD], int k, std::integer_sequence<int, I...>) {
+    (tile<true, I>(ring, k + I, T), ...);
+  }
+  template <int... I>
+  __device__ __forceinline__ void tiles_tail(Regs (&ring)[PD], int k, int ntiles, std::integer_sequence<int, I...>) {
+    ((k + I < ntiles ? tile<false, I>(ring, k + I, (int)(L - (int64_t)(k + I) * T < T ? L - (int64_t)(k + I) * T : T))
+                     : void()),
+     ...);
+  }
+
+  // unit: (batch row, 64-channel block); kw: the wave's group of 4 channels in the block
+  __device__ void run(int unit, int kw) {
+    const int nb = A.nblk;
+    const int64_t b = unit / nb;
+    L = A.s.L;
+    const int64_t d = (int64_t)(unit % nb) * 64 + CW1 * kw + r;
+    const bool valid = d < A.s.D;
+    row_bytes = wp_uniform((uint32_t)(A.s.D * kIo));
+    voff = valid ? (uint32_t)(d * kIo) + (uint32_t)n * row_bytes : kWpOutOfRange;
+    bc_off = (uint32_t)(4 * lane) * kIo;
+    const size_t row0 = (size_t)b * A.s.L;
+    span = wp_uniform((uint32_t)(A.s.L * A.s.D * kIo));
+    bspan = wp_uniform((uint32_t)(A.s.L * N * kIo));
+    zspan = A.s.z ? span : 0u;
+    p_u = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.u) + row0 * A.s.D));
+    p_dl = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.delta) + row0 * A.s.D));
+    p_z = A.s.z ? wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.z) + row0 * A.s.D)) : p_u;
+    p_out = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.out) + row0 * A.s.D));
+    p_B = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.B) + row0 * N));
+    p_C = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.C) + row0 * N));
+    const float a = valid ? A.s.A[d * N + n] : -1.0f;
+    a2 = a * kLog2e;
+    ka = rcp(a);
+    bias = (valid && A.s.bias) ? A.s.bias[d] : 0.0f;
+    dskip = (valid && A.s.dskip) ? A.s.dskip[d] : 0.0f;
+    h = (A.s.h0 && valid) ? A.s.h0[((size_t)b * A.s.D + d) * N + n] : 0.0f;
+    const int ntiles = (int)((L + T - 1) / T);
+    const int nfull = (int)(L / T);
+    Regs ring[PD];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) load(ring[q], q);
+    int k = 0;
+    for (; k + PD <= nfull; k += PD) tiles_full(ring, k, std::make_integer_sequence<int, PD>{});
+    tiles_tail(ring, k, ntiles, std::make_integer_sequence<int, PD>{});
+    if (A.s.last && valid) A.s.last[((size_t)b * A.s.D + d) * N + n] = h;
+  }
+};
+
+// Mixed launch (N = 16, unchunked): the first units2 (batch row, block) units run
+// with two states per lane (8 waves each), the rest with one state per lane (16
+// waves of half the work each).  With the split chosen so that the launch has 2
+// or 3 waves per SIMD (1024 SIMDs), the workgroups dealt last, the one-state
+// waves, fill the SIMDs that a launch of two-state waves alone leaves a wave
+// short.  Workgroup ids of both parts are mapped XCD by XCD as in scan_wp_kernel.
+template <typename IO, bool SP>
+__global__ __launch_bounds__(64, 3) void scan_wp_mixed_kernel(WpArgs a, int32_t units2, int32_t grid2) {
+  using K2 = WpScan<IO, 16, S6_WP_TILE16, kWpFull, SP>;
+  using K1 = Wp1Scan<IO, SP>;
+  __shared__ union {
+    typename K2::Lds two;
+    typename K1::Lds one;
+  } sm;
+  const int id = blockIdx.x;
+  if (id < grid2) {
+    const int m = id >> 3;
+    const int unit = (m / K2::P) * 8 + (id & 7);
+    if (unit >= units2) return;
+    K2 k(a, sm.two);
+    k.run(unit, m % K2::P);
+  } else {
+    const int i1 = id - grid2;
+    const int m = i1 >> 3;
+    const int unit = units2 + (m / 16) * 8 + (i1 & 7);
+    if (unit >= a.units) return;
+    K1 k(a, sm.one);
+    k.run(unit, m % 16);
+  }
+}
+
+template <typename IO>
+hipError_t launch_wp_mixed(const ScanArgs& s, int32_t wp1_units, hipStream_t st) {
+  WpArgs a;
+  a.s = s;
+  a.nblk = (int32_t)((s.D + 63) / 64);
+  a.units = (int32_t)(s.batch * a.nblk);
+  const int32_t units2 = a.units - wp1_units;
+  if (units2 < 0 || wp1_units < 0) return hipErrorInvalidValue;
+  // both parts' grids are whole multiples of 8 (one id per XCD in turn)
+  const int32_t grid2 = (units2 + 7) / 8 * 8 * 8;
+  const int32_t grid1 = (wp1_units + 7) / 8 * 8 * 16;
+  if (s.softplus)
+    hipLaunchKernelGGL((scan_wp_mixed_kernel<IO, true>), dim3((unsigned)(grid2 + grid1)), dim3(64), 0, st, a, units2,
+                       grid2);
+  else
+    hipLaunchKernelGGL((scan_wp_mixed_kernel<IO, false>), dim3((unsigned)(grid2 + grid1)), dim3(64), 0, st, a, units2,
+                       grid2);
   return hipGetLastError();
 }
 

@@ -289,6 +289,39 @@ def test_empty_sequence_returns_initial_state():
     assert torch.count_nonzero(last) == 0
 
 
+# Mixed launches (N = 16, unchunked, 128-256 or 256-384 (batch row, 64-channel
+# block) units): the last units run with one state per lane in the same launch.
+MIXED_CASES = [
+    (1, 300, 20480, 16, "bf16"),   # 320 units: 256 two-state + 64 one-state, ragged L
+    (3, 777, 4100, 16, "bf16"),    # 195 units, ragged channel tail in the one-state part
+    (2, 500, 6000, 16, "f32"),     # 188 units, fp32
+]
+
+
+@pytest.mark.parametrize("variant", ["plain", "h0", "no_gate_skip", "no_softplus"])
+@pytest.mark.parametrize("case", MIXED_CASES, ids=[f"b{c[0]}_L{c[1]}_D{c[2]}_{c[4]}" for c in MIXED_CASES])
+def test_mixed_launch(case, variant):
+    _need_gpu()
+    batch, L, D, N, io = case
+    _announce(f"mixed launch {case} {variant}")
+    inp = W.generate(batch, L, D, N, io, seed=700 + L + D)
+    h0 = None
+    softplus = None
+    if variant == "h0":
+        h0 = np.random.default_rng(701).standard_normal((batch, D, N)).astype(np.float32)
+    elif variant == "no_gate_skip":
+        inp.z = None
+        inp.Dskip = None
+    elif variant == "no_softplus":
+        softplus = False
+        inp.delta_bias = np.zeros(D, np.float32)
+        inp.delta = np.abs(inp.delta) * 0.01  # dt = delta itself: positive without softplus
+        if io == "bf16":
+            inp.delta = W.bf16_round(inp.delta)[1].reshape(inp.delta.shape)
+    eo, el = check(inp, h0=h0, softplus=softplus, label=f"mixed {case} {variant}")
+    print(f"{case} {variant}: out err {eo:.3e} last err {el:.3e}")
+
+
 # Two-pass scans with reset tokens: each chunk's end-state pass may start where the
 # rest of the chunk decays the state before it below 2^-200 (MAMBA_OPT_AGG_SKIP).
 SKIP_CASES = [
