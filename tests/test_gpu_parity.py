@@ -156,6 +156,10 @@ EDGE = [
     (1, 256, 64, 16, "f32", {"with_z": False, "with_dskip": False, "with_bias": False}),
     (1, 256, 320, 16, "f32", {"with_z": False}),
     (1, 4096, 32, 16, "f32", {}),           # fewer channels than a wave, many chunks
+    # mixed launches of the default engine (one state per lane for the last blocks)
+    (1, 1, 12288, 16, "f32", {}),           # a single token, 192 blocks
+    (2, 17, 10240, 16, "bf16", {}),         # one whole tile and one token, 320 blocks
+    (1, 100, 12288, 16, "f32", {"a_kind": "exp_normal"}),
 ]
 
 
