@@ -58,37 +58,6 @@ __device__ __forceinline__ float softplus(float v) {
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^{-z}); saturates without NaN.
 __device__ __forceinline__ float silu(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }
 
-// Per-(channel, state) constants derived from A once per launch.
-template <int N>
-struct ChanConst {
-  float a2[N];  // A_n * log2(e): exponent of Abar in base 2 per unit dt
-  float ka[N];  // 1 / A_n
-  float ah[N];  // A_n / 2: second series term of (e^x - 1)/x times dt
-  __device__ __forceinline__ void load(const float* A_row) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      float a = A_row[n];
-      a2[n] = a * kLog2e;
-      ka[n] = rcp(a);  // v_rcp_f32 (<1 ulp); inf for A_n = 0, never selected (see input_weight)
-      ah[n] = 0.5f * a;
-    }
-  }
-};
-
-// Per-token, per-channel front end: dt and the quantities shared by all N states.
-struct TokenFront {
-  float dt;   // discretisation step
-  float dt2;  // dt^2, for the series branch of the input weight
-};
-
-__device__ __forceinline__ TokenFront make_front(float raw, float bias, bool do_softplus) {
-  TokenFront f;
-  float v = raw + bias;
-  f.dt = do_softplus ? softplus(v) : v;
-  f.dt2 = f.dt * f.dt;
-  return f;
-}
-
 // Input weight of eq. (2) for one state: beta = dt * (e^x - 1)/x with x = dt*A_n,
 // returned together with Abar = e^x.  x2 = x*log2(e).
 //   |x2| <  kPhiSeriesX2 : beta = dt + dt^2 * A_n / 2       (series, error <= x^2/6)
@@ -98,6 +67,81 @@ __device__ __forceinline__ float input_weight(float abar, float x2, float dt, fl
   float big = __builtin_fmaf(abar, ka, -ka);
   float small = __builtin_fmaf(dt2, ah, dt);
   return fabsf(x2) < kPhiSeriesX2 ? small : big;
+}
+
+// Input weight for dt >= 0 (dt from softplus), in three instructions and no
+// branch.  With x = dt*A_n, beta = dt * f(x), f(x) = (e^x - 1)/x = integral over
+// s in [0, 1] of e^{s x}.  The integrand is convex in s, so the trapezoid rule
+// bounds the integral from above: f(x) <= (1 + e^x)/2 for every x, and
+//     U = dt * (1 + Abar) / 2 >= beta,   U - beta = dt * (x^2/12 + O(x^3)).
+// The quotient (Abar - 1)/A_n is accurate for large |x| but not near 0, where
+// the rounding error of Abar becomes a relative error ~ulp/|x|.  Adding a margin
+// m that covers that error, q = (Abar - 1)/A_n + m (formed with one rounding as
+// Abar * ka + kc, kc = -ka + m), makes q >= beta as well, so the smaller of the
+// two upper bounds is the closer one:
+//     beta ~= min(q, U),  relative error <= min(x^2/12, 2 m |A_n| / |x|).
+// v_exp_f32 is within 1 ulp (0.74 measured), so for A_n < 0 (Abar <= 1) one ulp
+// of ka, at least 2^-24 |ka|, covers it; for A_n > 0 (Abar >= 1, where the ulp
+// doubles) two ulps do.  In an fp32 emulation with Abar anywhere within 1 ulp of
+// 2^x2, the error stays below 1.4e-5 for A_n < 0 (2e-5 for A_n > 0), the same
+// bound as the guarded form, with a mean upward bias near 1e-6 where |x| > 1e-3.
+// For dt < 0 the trapezoid bound turns into a lower bound, so callers that cannot
+// rule out a negative dt use input_weight above.
+// 1/A_n for the bracket form, finite for every A_n (an A_n of 0 takes U, which is
+// then dt exactly, because q = ka + kc is huge).
+__device__ __forceinline__ float bracket_ka(float a) {
+  const float r = a == 0.0f ? 3.4028235e38f : rcp(a);
+  return fminf(fmaxf(r, -3.4028235e38f), 3.4028235e38f);
+}
+// -ka moved toward +infinity by one ulp (ka < 0) or two (ka > 0).
+__device__ __forceinline__ float bracket_kc(float ka) {
+  const float v = -ka;
+  return __uint_as_float(v > 0.0f ? __float_as_uint(v) + 1u : __float_as_uint(v) - 2u);
+}
+__device__ __forceinline__ float input_weight_pos(float abar, float dth, float ka, float kc) {
+  return fminf(__builtin_fmaf(abar, ka, kc), __builtin_fmaf(abar, dth, dth));
+}
+
+// Per-(channel, state) constants derived from A once per launch.
+template <int N>
+struct ChanConst {
+  float a2[N];  // A_n * log2(e): exponent of Abar in base 2 per unit dt
+  float ka[N];  // 1 / A_n (finite: bracket_ka)
+  float ah[N];  // A_n / 2: second series term of (e^x - 1)/x times dt (guarded form)
+  float kc[N];  // offset of the bracket form's quotient
+  __device__ __forceinline__ void set(int n, float a) {
+    a2[n] = a * kLog2e;
+    ka[n] = bracket_ka(a);  // the guarded form never selects its quotient for A_n = 0
+    ah[n] = 0.5f * a;
+    kc[n] = bracket_kc(ka[n]);
+  }
+  __device__ __forceinline__ void load(const float* A_row) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) set(n, A_row[n]);
+  }
+};
+
+// Per-token, per-channel front end: dt and the quantities shared by all N states.
+struct TokenFront {
+  float dt;   // discretisation step
+  float dt2;  // dt^2, for the series branch of the guarded input weight
+  float dth;  // dt / 2, for the bracket form
+  bool pos;   // dt comes from softplus (never negative): the bracket form applies
+};
+
+__device__ __forceinline__ TokenFront make_front(float raw, float bias, bool do_softplus) {
+  TokenFront f;
+  float v = raw + bias;
+  f.dt = do_softplus ? softplus(v) : v;
+  f.dt2 = f.dt * f.dt;
+  f.dth = 0.5f * f.dt;
+  f.pos = do_softplus;
+  return f;
+}
+
+__device__ __forceinline__ float input_weight_of(const TokenFront& f, float abar, float x2, float ka, float ah,
+                                                 float kc) {
+  return f.pos ? input_weight_pos(abar, f.dth, ka, kc) : input_weight(abar, x2, f.dt, f.dt2, ka, ah);
 }
 
 // One token of eq. (3a) for all N states of one channel, followed by the
@@ -110,7 +154,7 @@ __device__ __forceinline__ float token_step(const ChanConst<N>& cc, const TokenF
   for (int n = 0; n < N; ++n) {
     float x2 = f.dt * cc.a2[n];
     float abar = ex2(x2);
-    float beta = input_weight(abar, x2, f.dt, f.dt2, cc.ka[n], cc.ah[n]);
+    float beta = input_weight_of(f, abar, x2, cc.ka[n], cc.ah[n], cc.kc[n]);
     h[n] = __builtin_fmaf(abar, h[n], beta * (Bt[n] * x));
     y = __builtin_fmaf(Ct[n], h[n], y);
   }
@@ -125,7 +169,7 @@ __device__ __forceinline__ void token_step_state(const ChanConst<N>& cc, const T
   for (int n = 0; n < N; ++n) {
     float x2 = f.dt * cc.a2[n];
     float abar = ex2(x2);
-    float beta = input_weight(abar, x2, f.dt, f.dt2, cc.ka[n], cc.ah[n]);
+    float beta = input_weight_of(f, abar, x2, cc.ka[n], cc.ah[n], cc.kc[n]);
     h[n] = __builtin_fmaf(abar, h[n], beta * (Bt[n] * x));
   }
 }

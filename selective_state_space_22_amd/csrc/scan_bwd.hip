@@ -216,7 +216,9 @@ struct BwdTile {
   bool dvalid;
   uint32_t chan_off;
   __amdgpu_buffer_rsrc_t r_u, r_dl, r_z, r_go, r_B, r_C;
-  float a2[S], ka[S], ah[S], av[S];
+  // per-state constants: A_n log2(e), 1/A_n, A_n / 2 (guarded input weight),
+  // the bracket form's offset, A_n
+  float a2[S], ka[S], ah[S], kc[S], av[S];
   float bias, dskip;
 
   __device__ BwdTile(const BwdArgs& a)
@@ -245,8 +247,9 @@ struct BwdTile {
     for (int s = 0; s < S; ++s) {
       const float a = dvalid ? A.A[d * N + w * S + s] : -1.0f;
       a2[s] = a * kLog2e;
-      ka[s] = rcp(a);
+      ka[s] = bracket_ka(a);  // finite for every A_n; the series branches take A_n = 0
       ah[s] = 0.5f * a;
+      kc[s] = bracket_kc(ka[s]);
       av[s] = a;
     }
     bias = (dvalid && A.bias) ? A.bias[d] : 0.0f;
@@ -324,11 +327,12 @@ struct BwdTile {
 
 // ---------------------------------------------------------------- pass 1: chunk aggregates
 
-template <typename IO, int N, int W, int T>
+// SP: softplus on, so dt >= 0 and the input weight takes the bracket form.
+template <typename IO, int N, int W, int T, bool SP>
 __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
   using K = BwdTile<IO, N, W, T>;
   constexpr int S = K::S, TW = K::TW, BCW = K::BCW;
-  __shared__ float4 fr[2][T][64];  // dt, dt^2, x, dy
+  __shared__ float4 fr[2][T][64];  // dt, dt / 2 (SP) or dt^2, x, dy
   __shared__ __attribute__((aligned(16))) float bc[2][T][W][BCW];
   K k(a);
   k.setup(blockIdx.x);
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
     for (int i = 0; i < TW; ++i) {
       const int j = k.w + W * i;
       const typename K::Front f = k.front_one(r, i, j < nv);
-      fr[slot][j][k.lane] = make_float4(f.dt, f.dt2, f.x, f.dy);
+      fr[slot][j][k.lane] = make_float4(f.dt, SP ? 0.5f * f.dt : f.dt2, f.x, f.dy);
     }
     k.stage_bc(r, bc[slot]);
   };
@@ -389,7 +393,8 @@ __global__ __launch_bounds__(64 * W) void bwd_aggregate_kernel(BwdArgs a) {
       for (int s = 0; s < S; ++s) {
         const float x2 = fv.x * k.a2[s];
         const float ab = ex2(x2);
-        const float be = input_weight(ab, x2, fv.x, fv.y, k.ka[s], k.ah[s]);
+        const float be = SP ? input_weight_pos(ab, fv.y, k.ka[s], k.kc[s])
+                            : input_weight(ab, x2, fv.x, fv.y, k.ka[s], k.ah[s]);
         h[s] = __builtin_fmaf(ab, h[s], be * (bcs[s] * fv.z));
         p[s] *= ab;
         q[s] = __builtin_fmaf(p[s], fv.w * bcs[S + s], q[s]);
@@ -480,6 +485,9 @@ struct MainLds {
   float ex[2][3][T][W][64];                  // per-wave partial sums over states: readout, du, ddt
 };
 
+// The recompute keeps the guarded input weight: the bracket form's dt / 2 would
+// need a fifth per-token value in LDS, which measured slower than the compare and
+// select it saves.
 template <typename IO, int N, int W, int T>
 __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
   using K = BwdTile<IO, N, W, T>;
@@ -769,7 +777,10 @@ hipError_t launch_bwd_t(const BwdArgs& a0, hipStream_t st) {
     return hipGetLastError();
   }
   const unsigned items = (unsigned)(a.batch * a.nchunks * a.nblk);
-  hipLaunchKernelGGL((bwd_aggregate_kernel<IO, N, W, T>), dim3(items), dim3(64 * W), 0, st, a);
+  if (a.softplus)
+    hipLaunchKernelGGL((bwd_aggregate_kernel<IO, N, W, T, true>), dim3(items), dim3(64 * W), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_aggregate_kernel<IO, N, W, T, false>), dim3(items), dim3(64 * W), 0, st, a);
   hipLaunchKernelGGL((bwd_carry_kernel<N>), dim3(blocks_for(a.batch * N * a.D, 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL((bwd_main_kernel<IO, N, W, T>), dim3(items), dim3(64 * W), 0, st, a);
   hipLaunchKernelGGL((bwd_reduce_bc_kernel<IO, N>), dim3(blocks_for(a.batch * a.L * 2 * N, 256)), dim3(256), 0, st,

@@ -567,11 +567,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(StepArgs a) {
       av[4 * j] = q.x; av[4 * j + 1] = q.y; av[4 * j + 2] = q.z; av[4 * j + 3] = q.w;
     }
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-      cc.a2[n] = av[n] * kLog2e;
-      cc.ka[n] = rcp(av[n]);
-      cc.ah[n] = 0.5f * av[n];
-    }
+    for (int n = 0; n < N; ++n) cc.set(n, av[n]);
   } else {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = st[n];
@@ -618,7 +614,8 @@ __device__ __forceinline__ void dec_store_state(float* p, float a, float b, floa
   else *reinterpret_cast<dec_f32x4*>(p) = v;
 }
 
-template <typename IO, int N>
+// SP: softplus on (a compile-time flag, so that only one input-weight form is built).
+template <typename IO, int N, bool SP>
 __global__ __launch_bounds__(256) void state_update_vec_kernel(StepArgs a) {
   constexpr int LPC = N / 4;      // lanes per channel
   constexpr int CPB = 256 / LPC;  // channels per block and round
@@ -665,12 +662,8 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(StepArgs a) {
     const float av[4] = {qa[r].x, qa[r].y, qa[r].z, qa[r].w};
     ChanConst<4> cc;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      cc.a2[n] = av[n] * kLog2e;
-      cc.ka[n] = rcp(av[n]);
-      cc.ah[n] = 0.5f * av[n];
-    }
-    const TokenFront f = make_front(dr[r], a.bias ? a.bias[dd] : 0.0f, a.softplus != 0);
+    for (int n = 0; n < 4; ++n) cc.set(n, av[n]);
+    const TokenFront f = make_front(dr[r], a.bias ? a.bias[dd] : 0.0f, SP);
     float y = token_step<4>(cc, f, xr[r], Bt, Ct, h);
     // sum over the channel's lanes: (q0 + q1) + (q2 + q3), the same in every lane
     if constexpr (LPC >= 2) y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, false));
@@ -687,7 +680,10 @@ template <typename IO, int N>
 static void launch_step_vec(const StepArgs& a, hipStream_t s) {
   constexpr int CPB = 256 / (N / 4) * S6_DECODE_ROUNDS;  // channels per block
   const dim3 grid((unsigned)((a.D + CPB - 1) / CPB), (unsigned)a.batch);
-  hipLaunchKernelGGL((state_update_vec_kernel<IO, N>), grid, dim3(256), 0, s, a);
+  if (a.softplus)
+    hipLaunchKernelGGL((state_update_vec_kernel<IO, N, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((state_update_vec_kernel<IO, N, false>), grid, dim3(256), 0, s, a);
 }
 
 template <typename IO>

@@ -110,7 +110,9 @@ __device__ __forceinline__ f32x4 dt_mfma<float>(u32x4 a, u32x4 b, f32x4 c) {
   return c;
 }
 
-template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
+// POS: dt is known to be non-negative (it comes from softplus), so the input
+// weight takes the bracket form (input_weight_pos); otherwise the guarded form.
+template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX, bool POS>
 struct WgScan {
   static constexpr int S = N / W;                 // states per wave
   static constexpr int CF = CPLX ? 2 : 1;         // floats per state (complex A: re, im)
@@ -138,7 +140,7 @@ struct WgScan {
   static constexpr int BCW = (2 * S + 3) / 4 * 4;  // bc row per (token, wave), padded to float4
 
   struct Lds {
-    float4 fr[kSlots][T][64];                    // (dt, dt^2, x, z) per (token, channel)
+    float4 fr[kSlots][T][64];                    // (dt, dt / 2 (POS) or dt^2, x, z) per (token, channel)
     __attribute__((aligned(16))) float bc[kSlots][T][W][BCW];  // per token and wave: B of its states, then C
     float yp[kOut ? 2 : 1][T][W][64];            // partial readouts
     float sdt[W][64];                            // split mode: partial sums of dt
@@ -165,7 +167,9 @@ struct WgScan {
   __amdgpu_buffer_rsrc_t r_dtl, r_wdt;
   u32x4 wdt[kDtSlices], dta[kDtSlices];
   int nks;
-  float a2[S], ka[S], ah[S], h[S];
+  // per-state constants of the input weight: A_n log2(e), then 1/A_n and the
+  // bracket form's offset (POS) or 1/A_n and A_n / 2
+  float a2[S], ka[S], k2[S], h[S];
   CplxA ca[CS];  // complex A: per-state constants; h holds Re h, hq Im h
   float hq[CS];
   float maxim;   // complex A: largest |Im A_n| of this wave's states
@@ -254,7 +258,7 @@ struct WgScan {
       const float x = BufIo<IO>::widen(r.uu[i]);
       const float raw = FDT ? sm.raw[k & 1][j][lane] : BufIo<IO>::widen(r.dl[i]);
       TokenFront f = make_front(raw, bias, sp);
-      sm.fr[f3][j][lane] = make_float4(f.dt, f.dt2, x, kOut ? BufIo<IO>::widen(r.zz[i]) : 0.0f);
+      sm.fr[f3][j][lane] = make_float4(f.dt, POS ? 0.5f * f.dt : f.dt2, x, kOut ? BufIo<IO>::widen(r.zz[i]) : 0.0f);
       if (MODE == kModeAgg) {  // Kahan sum of dt over this wave's valid tokens
         const float yk = (j < nv ? f.dt : 0.0f) - dcomp;
         const float tk = dsum + yk;
@@ -328,7 +332,8 @@ struct WgScan {
     for (int s = 0; s < S; ++s) {
       const float x2 = t.fv.x * a2[s];
       const float abar = ex2(x2);
-      const float beta = input_weight(abar, x2, t.fv.x, t.fv.y, ka[s], ah[s]);
+      const float beta = POS ? input_weight_pos(abar, t.fv.y, ka[s], k2[s])
+                             : input_weight(abar, x2, t.fv.x, t.fv.y, ka[s], k2[s]);
       h[s] = __builtin_fmaf(abar, h[s], beta * (t.bc[s] * t.fv.z));
       if (kOut) y = __builtin_fmaf(t.bc[S + s], h[s], y);
     }
@@ -449,8 +454,8 @@ struct WgScan {
       for (int s = 0; s < S; ++s) {
         const float a = dvalid ? A.s.A[d * N + nstate0 + s] : -1.0f;
         a2[s] = a * kLog2e;
-        ka[s] = rcp(a);
-        ah[s] = 0.5f * a;
+        ka[s] = POS ? bracket_ka(a) : rcp(a);
+        k2[s] = POS ? bracket_kc(ka[s]) : 0.5f * a;
       }
     }
     bias = (dvalid && A.s.bias) ? A.s.bias[d] : 0.0f;
@@ -594,9 +599,9 @@ constexpr int wg_waves_per_simd() {
   return v > 1 ? v : 1;
 }
 
-template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX>
+template <typename IO, int N, int W, int T, int MODE, bool FDT, bool CPLX, bool POS>
 __global__ __launch_bounds__(64 * W, (wg_waves_per_simd<W, T>())) void scan_wg_kernel(WgArgs a) {
-  using K = WgScan<IO, N, W, T, MODE, FDT, CPLX>;
+  using K = WgScan<IO, N, W, T, MODE, FDT, CPLX, POS>;
   __shared__ typename K::Lds sm;
   K k(a, sm);
   for (int round = 0;; ++round) {
@@ -615,7 +620,7 @@ __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
 
 // T: tokens per tile of the chained mode and of the split mode's first pass;
 // TO: of the split mode's output pass.
-template <typename IO, int N, int W, int T, int TO, bool FDT, bool CPLX>
+template <typename IO, int N, int W, int T, int TO, bool FDT, bool CPLX, bool POS>
 hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream_t st) {
   constexpr int CF = CPLX ? 2 : 1;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -636,7 +641,7 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.ticket = ctrl;
     a.carry = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.nitems = a.chains * p.nchunks;
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained, FDT, CPLX>), dim3(p.grid), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeChained, FDT, CPLX, POS>), dim3(p.grid), block, 0, st, a);
   } else {
     a.s.agg_h = reinterpret_cast<float*>(base + p.ws_ctrl);
     a.s.agg_s = a.s.agg_h + (size_t)s.batch * p.nchunks * s.D * N * CF;
@@ -646,13 +651,13 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
     a.ticket = ctrl;
     a.nitems = a.chains * (p.nchunks - 1);
     const unsigned g1 = (unsigned)(a.nitems < p.grid ? a.nitems : p.grid);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg, FDT, CPLX>), dim3(g1), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, T, kModeAgg, FDT, CPLX, POS>), dim3(g1), block, 0, st, a);
     const hipError_t ce = CPLX ? launch_cplx_carry(a.s, N, st) : launch_chunk_carry(a.s, N, st);
     if (ce != hipSuccess) return ce;
     a.ticket = ctrl + 1;
     a.nitems = a.chains * p.nchunks;
     const unsigned g2 = (unsigned)(a.nitems < p.grid_out ? a.nitems : p.grid_out);
-    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, TO, kModeOut, FDT, CPLX>), dim3(g2), block, 0, st, a);
+    hipLaunchKernelGGL((scan_wg_kernel<IO, N, W, TO, kModeOut, FDT, CPLX, POS>), dim3(g2), block, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -660,15 +665,23 @@ hipError_t launch_wg_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
 template <typename IO, int N, int W, int T>
 hipError_t launch_wg_fdt(const ScanArgs& s, const ScanPlan& p, bool cplx, void* ws, hipStream_t st) {
   if (p.tile_out != T && (p.tile_out != 8 || !p.split || cplx || s.dtlow)) return hipErrorInvalidValue;
-  if (cplx) return s.dtlow ? hipErrorInvalidValue : launch_wg_t<IO, N, W, T, T, false, true>(s, p, ws, st);
+  if (cplx) return s.dtlow ? hipErrorInvalidValue : launch_wg_t<IO, N, W, T, T, false, true, false>(s, p, ws, st);
+  const bool pos = s.softplus != 0;
   if (s.dtlow) {
-    if constexpr (T == 16) return launch_wg_t<IO, N, W, T, T, true, false>(s, p, ws, st);
+    if constexpr (T == 16) {
+      return pos ? launch_wg_t<IO, N, W, T, T, true, false, true>(s, p, ws, st)
+                 : launch_wg_t<IO, N, W, T, T, true, false, false>(s, p, ws, st);
+    }
     return hipErrorInvalidValue;
   }
   if constexpr (T != 8) {
-    if (p.tile_out == 8) return launch_wg_t<IO, N, W, T, 8, false, false>(s, p, ws, st);
+    if (p.tile_out == 8) {
+      return pos ? launch_wg_t<IO, N, W, T, 8, false, false, true>(s, p, ws, st)
+                 : launch_wg_t<IO, N, W, T, 8, false, false, false>(s, p, ws, st);
+    }
   }
-  return launch_wg_t<IO, N, W, T, T, false, false>(s, p, ws, st);
+  return pos ? launch_wg_t<IO, N, W, T, T, false, false, true>(s, p, ws, st)
+             : launch_wg_t<IO, N, W, T, T, false, false, false>(s, p, ws, st);
 }
 
 }  // namespace

@@ -192,7 +192,7 @@ struct WpScan {
   }
 
   struct Lds {
-    float4 fr[2][T][CW];             // (dt, dt^2, x, z) per (token, channel)
+    float4 fr[2][T][CW];             // (dt, dt / 2 (softplus) or dt^2, x, z) per (token, channel)
     float4 bc[2][T][P];              // (B_2g, B_2g+1, C_2g, C_2g+1) per (token, state pair g)
     float yp[kOut ? T : 1][YS];      // partial readouts per token (layout: ypos)
     float sdt[MODE == kWpAgg ? 64 : 1];  // chunk sums of dt per lane
@@ -222,7 +222,9 @@ struct WpScan {
   // rows past the chunk still fall outside the resource.
   const char *p_u, *p_dl, *p_z, *p_out, *p_B, *p_C;
   uint32_t span, zspan, ospan, bspan;
-  float a2[S], ka[S], ah[S], h[S];
+  // per-state constants of the input weight: A_n log2(e), then (dt from softplus,
+  // never negative) the bracket form's 1/A_n and offset, else 1/A_n and A_n / 2
+  float a2[S], ka[S], k2[S], h[S];
   float bias, dskip;
   float dsum, dcomp;  // compensated sum of dt (first pass of the split scan)
 
@@ -287,7 +289,7 @@ struct WpScan {
     const float x = WpIo<IO>::widen(r.uu[i]);
     const float raw = WpIo<IO>::widen(r.dl[i]) + bias;
     const float dt = SP ? softplus(raw) : raw;
-    sm.fr[f][j][fc] = make_float4(dt, dt * dt, x, kOut ? WpIo<IO>::widen(r.zz[i]) : 0.0f);
+    sm.fr[f][j][fc] = make_float4(dt, SP ? 0.5f * dt : dt * dt, x, kOut ? WpIo<IO>::widen(r.zz[i]) : 0.0f);
     if (MODE == kWpAgg) {  // Kahan sum of dt over this lane's valid tokens
       const float yk = (j < tile_valid(k) ? dt : 0.0f) - dcomp;
       const float tk = dsum + yk;
@@ -343,7 +345,8 @@ struct WpScan {
       for (int s = 0; s < S; ++s) {
         const float x2 = fv[q].x * a2[s];
         ab[q][s] = ex2(x2);
-        const float beta = input_weight(ab[q][s], x2, fv[q].x, fv[q].y, ka[s], ah[s]);
+        const float beta = SP ? input_weight_pos(ab[q][s], fv[q].y, ka[s], k2[s])
+                              : input_weight(ab[q][s], x2, fv[q].x, fv[q].y, ka[s], k2[s]);
         in[q][s] = beta * ((s == 0 ? bv[q].x : bv[q].y) * fv[q].z);
       }
 #pragma unroll
@@ -360,7 +363,8 @@ struct WpScan {
     for (int s = 0; s < S; ++s) {
       const float x2 = fv.x * a2[s];
       const float abar = ex2(x2);
-      const float beta = input_weight(abar, x2, fv.x, fv.y, ka[s], ah[s]);
+      const float beta = SP ? input_weight_pos(abar, fv.y, ka[s], k2[s])
+                            : input_weight(abar, x2, fv.x, fv.y, ka[s], k2[s]);
       h[s] = __builtin_fmaf(abar, h[s], beta * ((s == 0 ? bv.x : bv.y) * fv.z));
       y = s == 0 ? bv.z * h[0] : __builtin_fmaf(bv.w, h[1], y);
     }
@@ -517,8 +521,8 @@ struct WpScan {
     for (int s = 0; s < S; ++s) {
       const float a = svalid ? A.s.A[dscan * N + n0 + s] : -1.0f;
       a2[s] = a * kLog2e;
-      ka[s] = rcp(a);
-      ah[s] = 0.5f * a;
+      ka[s] = SP ? bracket_ka(a) : rcp(a);
+      k2[s] = SP ? bracket_kc(ka[s]) : 0.5f * a;
       h[s] = 0.0f;
     }
     bias = (fvalid && A.s.bias) ? A.s.bias[dfront] : 0.0f;
@@ -637,7 +641,7 @@ hipError_t launch_wp_t(const ScanArgs& s, const ScanPlan& p, void* ws, hipStream
 // reads dt and x from lane 16r + j of its own row with a DPP row broadcast
 // (row_newbcast:j), which the compiler folds into the multiplies that use them;
 // B_t and C_t (shared by all channels, section 3.2) are staged once per tile in
-// LDS as (B, C) pairs per state.  The series branch of the input weight is
+// LDS as (B, C) pairs per state.  The guarded input weight's series branch is
 // written dt (1 + x ln2 / 2) with x = dt A log2(e), the same value as
 // dt + dt^2 A / 2, so that dt enters it only through a multiply.
 template <int J>
@@ -673,8 +677,8 @@ struct Wp1Scan {
   uint32_t row_bytes, voff, bc_off;
   const char *p_u, *p_dl, *p_z, *p_out, *p_B, *p_C;
   uint32_t span, zspan, bspan;
-  float a2, ka, h, bias, dskip;
-  float fdt, fx, fz;  // front end of this lane's token of the current tile
+  float a2, ka, kc, h, bias, dskip;
+  float fdt, fdh, fx, fz;  // front end of this lane's token of the current tile (fdh = dt / 2)
 
   __device__ Wp1Scan(const WpArgs& a, Lds& s)
       : A(a), sm(s), lane(threadIdx.x & 63), r((threadIdx.x & 63) >> 4), n(threadIdx.x & 15) {}
@@ -699,6 +703,7 @@ struct Wp1Scan {
     fz = WpIo<IO>::widen(g.zz);
     const float raw = WpIo<IO>::widen(g.dl) + bias;
     fdt = SP ? softplus(raw) : raw;
+    fdh = 0.5f * fdt;
   }
 
   // B / C of a tile: lane l stages elements 4l .. 4l+3 of the (token, state)
@@ -731,9 +736,14 @@ struct Wp1Scan {
   __device__ __forceinline__ void input_terms(const float2 v, float& ab, float& in) const {
     const float x2 = row_bcast<J>(fdt) * a2;
     ab = ex2(x2);
-    const float big = __builtin_fmaf(ab, ka, -ka);
-    const float small = row_bcast<J>(fdt) * __builtin_fmaf(x2, kHalfLn2, 1.0f);
-    const float beta = fabsf(x2) < kPhiSeriesX2 ? small : big;
+    float beta;
+    if constexpr (SP) {  // bracket form (dt >= 0), its bound written (dt / 2)(1 + Abar): dt through a multiply
+      beta = fminf(__builtin_fmaf(ab, ka, kc), row_bcast<J>(fdh) * (1.0f + ab));
+    } else {
+      const float big = __builtin_fmaf(ab, ka, -ka);
+      const float small = row_bcast<J>(fdt) * __builtin_fmaf(x2, kHalfLn2, 1.0f);
+      beta = fabsf(x2) < kPhiSeriesX2 ? small : big;
+    }
     in = beta * (row_bcast<J>(fx) * v.x);
   }
   // Tokens J and J+1: both tokens' input terms, then the two recurrence steps
@@ -831,7 +841,8 @@ struct Wp1Scan {
     p_C = wp_uniform(reinterpret_cast<const char*>(static_cast<const IO*>(A.s.C) + row0 * N));
     const float a = valid ? A.s.A[d * N + n] : -1.0f;
     a2 = a * kLog2e;
-    ka = rcp(a);
+    ka = SP ? bracket_ka(a) : rcp(a);
+    kc = bracket_kc(ka);
     bias = (valid && A.s.bias) ? A.s.bias[d] : 0.0f;
     dskip = (valid && A.s.dskip) ? A.s.dskip[d] : 0.0f;
     h = (A.s.h0 && valid) ? A.s.h0[((size_t)b * A.s.D + d) * N + n] : 0.0f;
