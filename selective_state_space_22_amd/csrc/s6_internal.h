@@ -124,7 +124,11 @@ struct ScanPlan {
   size_t ws_bytes;    // workspace the plan needs in total (0 when nothing is needed)
 };
 
-ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N);
+// mixed: whether an unchunked N = 16 scan may use the mixed launch (two- and
+// one-state-per-lane waves).  It is the faster launch when scans run back to back,
+// and the slower one right after the selection GEMMs (mamba_ssm_fwd and the block
+// pass false).
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, bool mixed = true);
 // Plan of a scan whose dt is projected inside the workgroup engine (ScanArgs::dtlow).
 ScanPlan plan_scan_fused_dt(int64_t batch, int64_t L, int64_t D, int64_t N);
 

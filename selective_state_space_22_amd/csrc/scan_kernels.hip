@@ -383,7 +383,7 @@ ScanPlan plan_wg(int64_t batch, int64_t L, int64_t D, int64_t N, int cf = 1, boo
 constexpr int64_t kWpSplitBelow = 1024;  // waves of the unchunked scan below which L is cut
 constexpr int64_t kWpTargetWaves = S6_WP_SPLIT_WAVES;
 
-ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
+ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N, bool mixed) {
   ScanPlan p{};
   p.engine = kEngineWp;
   p.waves = (int32_t)(N / 2);
@@ -413,7 +413,7 @@ ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
   // (batch row, block) units run with one state per lane (twice the waves, half
   // the work each), so that the launch has 2 or 3 waves on every SIMD.
   const int64_t units = batch * ((D + 63) / 64);
-  if (S6_WP_MIXED && !p.split && N == 16) {
+  if (S6_WP_MIXED && mixed && !p.split && N == 16) {
     if (units > 128 && units < 256) p.wp1_units = (int32_t)(256 - units);
     else if (units > 256 && units < 384) p.wp1_units = (int32_t)(384 - units);
   }
@@ -423,14 +423,14 @@ ScanPlan plan_wp(int64_t batch, int64_t L, int64_t D, int64_t N) {
   return p;
 }
 
-ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N) {
+ScanPlan plan_scan(int64_t batch, int64_t L, int64_t D, int64_t N, bool mixed) {
   const int64_t engine = option(kOptEngine);
   if (wg_supported(N) && batch > 0 && L > 0 && D > 0 && engine != 1) {
-    if (engine == 3) return plan_wp(batch, L, D, N);
+    if (engine == 3) return plan_wp(batch, L, D, N, mixed);
     // Long sequences over few channel blocks (two passes over chunks) run faster
     // on the workgroup engine, whose waves load whole 128-byte lines of a token row.
     if (engine == 0) {
-      const ScanPlan p = plan_wp(batch, L, D, N);
+      const ScanPlan p = plan_wp(batch, L, D, N, mixed);
       if (!p.split) return p;
     }
     return plan_wg(batch, L, D, N);
