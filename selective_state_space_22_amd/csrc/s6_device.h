@@ -93,10 +93,13 @@ __device__ __forceinline__ float bracket_ka(float a) {
   const float r = a == 0.0f ? 3.4028235e38f : rcp(a);
   return fminf(fmaxf(r, -3.4028235e38f), 3.4028235e38f);
 }
-// -ka moved toward +infinity by one ulp (ka < 0) or two (ka > 0).
+// -ka moved toward +infinity by one ulp (ka < 0) or two (ka > 0).  A ka too small
+// to matter (|A_n| beyond 1e37, where dt A_n overflows anyway) keeps no margin, so
+// that the bit step never crosses zero.
 __device__ __forceinline__ float bracket_kc(float ka) {
   const float v = -ka;
-  return __uint_as_float(v > 0.0f ? __float_as_uint(v) + 1u : __float_as_uint(v) - 2u);
+  const uint32_t b = __float_as_uint(v);
+  return v > 0.0f ? __uint_as_float(b + 1u) : (v < -1.0e-37f ? __uint_as_float(b - 2u) : v);
 }
 __device__ __forceinline__ float input_weight_pos(float abar, float dth, float ka, float kc) {
   return fminf(__builtin_fmaf(abar, ka, kc), __builtin_fmaf(abar, dth, dth));

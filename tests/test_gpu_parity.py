@@ -277,6 +277,49 @@ def test_no_softplus_positive_dt():
     check(inp, softplus=False, label="no softplus")
 
 
+def _input_weight_stress(L, D, N, seed):
+    """Inputs that sweep dt * A_n over the whole range the input weight must cover:
+    per channel a bias putting softplus(delta + bias) anywhere in [1e-7, 3], and per
+    state an A_n among 0, tiny and large magnitudes of either sign (A_n = 0, tiny or
+    positive only where dt is small, so that every state stays O(1)).  States that do
+    not decay, driven with a large dt, grow to hundreds over 300 tokens; outputs of a
+    few units are then sums of such terms that cancel, and the relative metric
+    measures fp32 cancellation in the readout (7.8e-5 with the guarded input weight,
+    1.1e-4 with the bracket form, with dt up to 30 on the mixed-launch shape below),
+    not the input weight."""
+    inp = W.generate(2, L, D, N, "f32", seed=seed)
+    g = np.random.default_rng(seed)
+    dt_target = np.exp(g.uniform(np.log(1e-7), np.log(3.0), D))
+    inp.delta_bias = (np.log(np.expm1(dt_target)) + 3.0).astype(np.float32)  # delta ~ U(-4, -2)
+    A = -np.exp(g.uniform(np.log(0.1), np.log(1e3), (D, N)))
+    slow = dt_target < 0.1  # states that do not decay only where dt is small, so they stay O(1)
+    A[slow, 0] = 0.0
+    A[slow, 1] = -1e-6
+    A[dt_target < 1e-3, 2] = 0.5   # positive A_n where dt A_n stays below 5e-4 (growth e^0.15 over 300 tokens)
+    A[dt_target < 1e-4, 3] = 20.0  # and below 2e-3
+    inp.A = A.astype(np.float32)
+    return inp
+
+
+IW_CASES = [((300, 128, 16), e) for e in ("default", "wg", "lane", "wp")] + [
+    ((300, 128, 8), "default"), ((300, 128, 8), "wp"), ((200, 96, 4), "default"),
+    ((300, 8704, 16), "default"),  # 272 channel blocks: the mixed launch (two- and one-state waves)
+]
+
+
+@pytest.mark.parametrize("shape,engine", IW_CASES, ids=[f"L{c[0][0]}_D{c[0][1]}_N{c[0][2]}_{c[1]}" for c in IW_CASES])
+def test_input_weight_over_the_whole_range(shape, engine, request):
+    """dt * A_n from 0 and 1e-13 up to 3e3 in magnitude, A_n = 0, A_n > 0: the bracket form of the
+    input weight (softplus on) against the oracle at the fp32 bound, on every engine
+    and layout that computes it."""
+    _need_gpu()
+    _engine(request, engine)
+    L, D, N = shape
+    _announce(f"input weight over the whole range {shape} engine={engine}")
+    inp = _input_weight_stress(L, D, N, seed=4242 + N)
+    check(inp, label=f"input weight {shape} {engine}")
+
+
 def test_empty_sequence_returns_initial_state():
     _need_gpu()
     from selective_state_space_22_amd import mamba_scan_fwd
