@@ -613,9 +613,15 @@ __global__ __launch_bounds__(64 * W, (wg_waves_per_simd<W, T>())) void scan_wg_k
   }
 }
 
+// Clears the work ticket and the chained-mode flags of a call.  The words are
+// cleared with agent-scope atomic stores, like every later access to them (the
+// ticket's atomic adds, the flags' release stores and acquire polls), so that no
+// XCD can read a value of the previous call that a plain store left in another
+// XCD's L2; this does not depend on the cache write-back between the two kernels,
+// which a replayed graph may arrange differently from a stream.
 __global__ void zero_words_kernel(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  if (i < n) __hip_atomic_store(p + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // T: tokens per tile of the chained mode and of the split mode's first pass;
