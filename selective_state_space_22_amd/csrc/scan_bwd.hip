@@ -528,8 +528,9 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
   }
   float dsk = 0.0f, dbs = 0.0f;  // this wave's share of the dDskip and bias sums
 
-  typename K::Raw r;
-  auto front = [&](int kt, int slot) {
+  // raw global data of two tiles: loads run two tiles ahead of the front end
+  typename K::Raw ra, rb;
+  auto front = [&](const typename K::Raw& r, int kt, int slot) {
     const int nv = k.tile_valid(kt);
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
@@ -541,13 +542,17 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
     k.stage_bc(r, sm.bc[slot]);
   };
   // tile-start data (relative state and cumulative dt) of tile kt into registers
-  float srel[S], cdt;
-  auto load_start = [&](int kt) {
+  // tile-start data of two tiles (loaded two tiles ahead, like the raw data)
+  struct Start {
+    float srel[S], cdt;
+  };
+  Start sa, sb;
+  auto load_start = [&](Start& st, int kt) {
     const uint32_t toff = (uint32_t)(kt < 0 ? 0 : kt) * (uint32_t)(N * a.D * 4);
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      srel[s] = ldf(r_srel, dv && kt >= 0 ? toff + (uint32_t)((w * S + s) * a.D * 4) + dbytes : kOutOfRange);
-    cdt = ldf(r_cdt, dv && kt >= 0 ? (uint32_t)kt * (uint32_t)(a.D * 4) + dbytes : kOutOfRange);
+      st.srel[s] = ldf(r_srel, dv && kt >= 0 ? toff + (uint32_t)((w * S + s) * a.D * 4) + dbytes : kOutOfRange);
+    st.cdt = ldf(r_cdt, dv && kt >= 0 ? (uint32_t)kt * (uint32_t)(a.D * 4) + dbytes : kOutOfRange);
   };
 
   // epilogue of tile kt: sums over the W waves, skip and gate terms, stores
@@ -579,12 +584,12 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
   };
 
   // one tile: rebuild the start state, recompute the tile's states, reverse
-  auto scan = [&](int kt, int slot, int eslot) {
+  auto scan = [&](int kt, int slot, int eslot, Start& st) {
     float hh[T][S], ab[T][S], be[T][S], xx[T][S], bx[T][S];  // per element: h, Abar, beta, dt A log2(e), B x
     float hst[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) hst[s] = __builtin_fmaf(ex2(k.a2[s] * cdt), hs0[s], srel[s]);
-    load_start(kt - 1);
+    for (int s = 0; s < S; ++s) hst[s] = __builtin_fmaf(ex2(k.a2[s] * st.cdt), hs0[s], st.srel[s]);
+    load_start(st, kt - 2);
     // forward recompute (eq. (2), (3a)) and partial readouts (eq. (3b))
 #pragma unroll
     for (int j = 0; j < T; ++j) {
@@ -640,24 +645,36 @@ __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
     stf(tot, r_pbc, owner ? (uint32_t)(((kt * T + j) * 2 + qv) * N + w * S + s) * 4u : kOutOfRange);
   };
 
-  // reverse tile pipeline: iteration for tile kt runs front(kt-1), load(kt-2),
+  // reverse tile pipeline: iteration for tile kt runs front(kt-1), load(kt-3),
   // epilogue(kt+1), scan(kt), then the one barrier.  fr/fe/bc rotate over 3
   // slots and ex over 2 (slot = tile index mod 3 / mod 2).
+  // The raw data of tile kt - 1 and the start data of tile kt are in ra, sa at even
+  // steps from the last tile and in rb, sb at odd ones (the loop is unrolled by two
+  // so that the choice is static); each buffer is refilled with the tile two below
+  // the one just consumed.
+  auto step = [&](int kt, typename K::Raw& cur, Start& st) __attribute__((always_inline)) {
+    const int slot = kt % 3;
+    if (kt > 0) front(cur, kt - 1, (kt - 1) % 3);
+    k.load(cur, kt - 3);
+    if (kt < nt - 1) epilogue(kt + 1, (kt + 1) % 3, (kt + 1) & 1);
+    scan(kt, slot, kt & 1, st);
+    __syncthreads();
+  };
   if (nt > 0) {
     const int last = nt - 1;
-    k.load(r, last);
-    front(last, last % 3);
-    k.load(r, last - 1);
-    load_start(last);
+    k.load(ra, last);
+    front(ra, last, last % 3);
+    k.load(ra, last - 1);
+    k.load(rb, last - 2);
+    load_start(sa, last);
+    load_start(sb, last - 1);
     __syncthreads();
-    for (int kt = last; kt >= 0; --kt) {
-      const int slot = kt % 3;
-      if (kt > 0) front(kt - 1, (kt - 1) % 3);
-      k.load(r, kt - 2);
-      if (kt < last) epilogue(kt + 1, (kt + 1) % 3, (kt + 1) & 1);
-      scan(kt, slot, kt & 1);
-      __syncthreads();
+    int kt = last;
+    for (; kt >= 1; kt -= 2) {
+      step(kt, ra, sa);
+      step(kt - 1, rb, sb);
     }
+    if (kt == 0) step(0, ra, sa);
     epilogue(0, 0, 0);
   }
 
