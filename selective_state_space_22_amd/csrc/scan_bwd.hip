@@ -485,9 +485,9 @@ struct MainLds {
   float ex[2][3][T][W][64];                  // per-wave partial sums over states: readout, du, ddt
 };
 
-// The recompute keeps the guarded input weight: the bracket form's dt / 2 would
-// need a fifth per-token value in LDS, which measured slower than the compare and
-// select it saves.
+// The recompute keeps the guarded input weight: the bracket form, with dt / 2
+// either a fifth per-token value in LDS or formed per token from dt, issued fewer
+// instructions and measured slower both ways.
 template <typename IO, int N, int W, int T>
 __global__ __launch_bounds__(64 * W, 1) void bwd_main_kernel(BwdArgs a) {
   using K = BwdTile<IO, N, W, T>;
