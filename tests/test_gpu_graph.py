@@ -17,14 +17,21 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("shape", [(5, 1100, 4096, 16, "bf16"), (1, 4096, 64, 16, "f32"), (1, 300, 64, 4, "f32")],
-                         ids=["chained", "split", "lane"])
-def test_scan_graph_replays_match_eager(shape):
+SCAN_GRAPH_CASES = [((5, 1100, 4096, 16, "bf16"), "default"),  # the wave-private mixed launch
+                    ((5, 1100, 4096, 16, "bf16"), "wg"),       # chained chunks: ticket, flags, carries
+                    ((1, 4096, 64, 16, "f32"), "default"),     # two passes over chunks
+                    ((1, 300, 64, 4, "f32"), "default")]       # lane engine
+
+
+@pytest.mark.parametrize("shape,engine", SCAN_GRAPH_CASES, ids=["wave_private", "chained", "split", "lane"])
+def test_scan_graph_replays_match_eager(shape, engine, request):
     _need_gpu()
+    from gpu_util import force_engine
     from selective_state_space_22_amd import binding
 
+    force_engine(request, engine)
     batch, L, D, N, io = shape
-    print(f"\n[gpu-test] graph replay of mamba_scan_fwd {shape}", flush=True)
+    print(f"\n[gpu-test] graph replay of mamba_scan_fwd {shape} engine={engine}", flush=True)
     inp = W.generate(batch, L, D, N, io, seed=123)
     d = to_device(inp)
     out = torch.empty_like(d["u"])
